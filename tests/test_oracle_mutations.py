@@ -1,0 +1,110 @@
+"""Planted mistakes in the oracle must each fail at least one pin.
+
+Each mutation below replaces one oracle function (on the CPU, via
+monkeypatch) with a plausible wrong version: a swapped operand, a dropped
+term, a wrong sign, an off-by-one, an unstable order.  The test runs every pin
+of the codec, align and FFN pin sets and requires that one of them fails.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import test_oracle_align as A
+import test_oracle_codec as C
+import test_oracle_ffn as FF
+
+ALL_PINS = C.PINS + A.PINS + FF.PINS
+
+_orig = {n: getattr(oracle, n) for n in ("split_gate_up", "silu", "expert_ffn", "align_permute",
+                                         "mx_scale_exponent", "e4m3fn_encode",
+                                         "topk_reduce_contiguous", "moe_contiguous")}
+
+
+def m_swap_gate_up(w1, order):
+    g, u = _orig["split_gate_up"](w1, order)
+    return u, g
+
+
+def m_interleave_up_first(w1, order):
+    if order != "interleave16":
+        return _orig["split_gate_up"](w1, order)
+    g, u = _orig["split_gate_up"](w1, order)
+    return u, g
+
+
+def m_silu_sign(v):
+    return v / (1.0 + np.exp(v))
+
+
+def m_ffn_no_act(x, w1, w2, order="halves"):
+    g, u = oracle.split_gate_up(np.asarray(w1, np.float64), order)
+    return ((x @ g.T) * (x @ u.T)) @ np.asarray(w2, np.float64).T
+
+
+def m_ffn_w2_transposed(x, w1, w2, order="halves"):
+    g, u = oracle.split_gate_up(np.asarray(w1, np.float64), order)
+    z = oracle.silu(x @ g.T) * (x @ u.T)
+    w2 = np.asarray(w2, np.float64)
+    if w2.shape[0] == w2.shape[1]:
+        return z @ w2
+    # a transposed read of a non-square W2: same element count, wrong layout
+    return z @ w2.reshape(w2.shape[1], w2.shape[0])
+
+
+def m_align_descending(ids, E, B):
+    got = _orig["align_permute"](ids, E, B)
+    s = got["sorted_ids"].copy()
+    for e in range(E):
+        lo, n = got["offsets"][e], got["counts"][e]
+        s[lo:lo + n] = s[lo:lo + n][::-1]
+    got["sorted_ids"] = s
+    return got
+
+
+def m_align_no_padding(ids, E, B):
+    return _orig["align_permute"](ids, E, 1)
+
+
+def m_scale_floor(bm):
+    return _orig["mx_scale_exponent"](bm) - 1
+
+
+def m_encode_ties_away(v):
+    v = np.asarray(v, np.float64)
+    c = _orig["e4m3fn_encode"](v)
+    tab = oracle.e4m3fn_table()
+    a = np.abs(v)
+    up = np.minimum((c & 0x7F).astype(np.int64) + 1, 126)
+    mid = (tab[c & 0x7F] + tab[up]) / 2
+    bump = (a == mid) & (up != (c & 0x7F))
+    return np.where(bump, (c & 0x80) | up.astype(np.uint8), c).astype(np.uint8)
+
+
+def m_reduce_reads_skipped(y, ids, w, E):
+    ids2 = np.where(np.asarray(ids) < 0, 0, ids)
+    return _orig["topk_reduce_contiguous"](y, ids2, w, E)
+
+
+def m_moe_ignores_weights(x_rows, tokens, ids, w, E, w1_of, w2_of, order="halves"):
+    return _orig["moe_contiguous"](x_rows, tokens, ids, np.ones_like(w), E, w1_of, w2_of, order)
+
+
+MUTATIONS = [
+    ("split_gate_up", m_swap_gate_up), ("split_gate_up", m_interleave_up_first),
+    ("silu", m_silu_sign), ("expert_ffn", m_ffn_no_act), ("expert_ffn", m_ffn_w2_transposed),
+    ("align_permute", m_align_descending), ("align_permute", m_align_no_padding),
+    ("mx_scale_exponent", m_scale_floor), ("e4m3fn_encode", m_encode_ties_away),
+    ("topk_reduce_contiguous", m_reduce_reads_skipped), ("moe_contiguous", m_moe_ignores_weights),
+]
+
+
+@pytest.mark.parametrize("name,fn", MUTATIONS, ids=[f.__name__ for _, f in MUTATIONS])
+def test_planted_mistake_is_caught(monkeypatch, name, fn):
+    monkeypatch.setattr(oracle, name, fn)
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin()
+        except Exception:
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught the planted mistake {fn.__name__}"
