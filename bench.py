@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused-MoE expert computation on one MI355X.
+
+A step is one pass of the whole expert path over one batch of synthetic
+inputs already resident in HBM: align/permute, W1 GEMM with SiLU-and-mul
+(and, for MXFP8 weights, the activation quantisation), W2 GEMM with the
+unpermute scatter, and the ordered top-k weighted reduce, launched through
+the C ABI stage by stage on one stream (the same kernels moe_apply_contiguous
+launches), with HIP events between the stages.
+
+Default workload: the decode batch (M=4, K=4096, I=8192, E=64, top-8, bf16),
+which is weight-bandwidth bound; ``--config`` picks another of the five.
+Prints one JSON line: tokens/s for the whole job, the dominant kernel's
+roofline (measured live from the events), and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused-MoE layer tokens/s; TFLOP/s vs MFMA peak (prefill), GB/s vs HBM (decode)"
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="decode",
+                    help="tiny | decode | prefill | mxfp8 | batched (or a full workload name)")
+    ap.add_argument("--cpu-sample", type=int, default=0,
+                    help="tokens (or batched rows) the CPU oracle is timed on (0: per-workload default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "mixture_experts_expert_align_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(cfg_name: str, kernel_files):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None if there is none or the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{cfg_name}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_hash") != kernel_source_hash(kernel_files):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_inputs as mi
+    import mixture_experts_expert_align_amd as moe
+
+    cfg = mi.config(args.config)
+    dev = "cuda"
+    torch.cuda.init()
+    print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
+    inp = mi.make_inputs(cfg, device=dev, weights=True)
+    w1_scale = w2_scale = None
+    if cfg.w_dtype == "mxfp8":
+        w1 = torch.empty(inp.w1.shape, dtype=torch.uint8, device=dev)
+        w2 = torch.empty(inp.w2.shape, dtype=torch.uint8, device=dev)
+        w1_scale = torch.empty((*inp.w1.shape[:-1], cfg.K // 32), dtype=torch.uint8, device=dev)
+        w2_scale = torch.empty((*inp.w2.shape[:-1], cfg.I // 32), dtype=torch.uint8, device=dev)
+        moe.moe_quantize_mxfp8(inp.w1, w1, w1_scale)
+        moe.moe_quantize_mxfp8(inp.w2, w2, w2_scale)
+        torch.cuda.synchronize()
+        w_f32 = (inp.w1, inp.w2)
+        inp.w1 = inp.w2 = None
+    else:
+        w1, w2 = inp.w1, inp.w2
+        w_f32 = None
+
+    contiguous = cfg.layout == "contiguous"
+    prob = moe.make_problem(cfg.M, cfg.K, cfg.I, cfg.E, topk=cfg.topk, max_tokens=cfg.max_tokens,
+                            layout=0 if contiguous else 1, w_dtype=0 if cfg.w_dtype == "bf16" else 1,
+                            w1_order=0 if cfg.w1_order == "halves" else 1)
+    plan = moe.moe_plan_init(prob)
+    ws13, ws2 = moe.allocate_workspaces(plan)
+    stream = torch.cuda.current_stream()
+
+    if contiguous:
+        ids = torch.from_numpy(inp.topk_ids).to(dev)
+        wts = torch.from_numpy(inp.topk_weights).to(dev)
+        out = torch.empty((cfg.M, cfg.K), dtype=torch.bfloat16, device=dev)
+        R = cfg.M * cfg.topk
+        valid = (inp.topk_ids >= 0) & (inp.topk_ids < cfg.E)
+        n_routes = int(valid.sum())
+        active = np.unique(inp.topk_ids[valid])
+        n_tok_read = int(valid.any(axis=1).sum())
+        stages = ["align", "gate_up_act", "down_unpermute", "reduce"]
+
+        def step(ev):
+            ev[0].record(stream)
+            moe.moe_align_permute(plan, ids, ws13, stream)
+            ev[1].record(stream)
+            moe.moe_gate_up_act(plan, inp.x, w1, w2, ws13, w1_scale, w2_scale, stream)
+            ev[2].record(stream)
+            moe.moe_down_unpermute(plan, w1, w2, ws13, ws2, w1_scale, w2_scale, stream)
+            ev[3].record(stream)
+            moe.moe_topk_reduce_contiguous(plan, ws2, ids, wts, out, stream)
+            ev[4].record(stream)
+    else:
+        counts = torch.from_numpy(inp.expert_num_tokens).to(dev)
+        row_token = torch.from_numpy(inp.row_token).to(dev)
+        row_weight = torch.from_numpy(inp.row_weight).to(dev)
+        y = torch.empty((cfg.E, cfg.max_tokens, cfg.K), dtype=torch.bfloat16, device=dev)
+        out = torch.empty((cfg.M, cfg.K), dtype=torch.bfloat16, device=dev)
+        wsr = torch.empty(moe.moe_naive_batched_ws_bytes(plan, cfg.M), dtype=torch.uint8, device=dev)
+        n_routes = int(inp.expert_num_tokens.sum())
+        active = np.flatnonzero(inp.expert_num_tokens > 0)
+        stages = ["apply_batched", "reduce_naive_batched"]
+
+        def step(ev):
+            ev[0].record(stream)
+            moe.moe_apply_batched(plan, inp.a, counts, w1, w2, y, ws13, stream)
+            ev[1].record(stream)
+            moe.moe_topk_reduce_naive_batched(plan, y, counts, row_token, row_weight, cfg.M, out,
+                                              wsr, stream)
+            ev[2].record(stream)
+
+    nev = len(stages) + 1
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+    for _ in range(args.warmup):
+        step(mk())
+    torch.cuda.synchronize()
+    events = [mk() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stage_ms = {s: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in events]))
+                for i, s in enumerate(stages)}
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens = cfg.M
+    value = tokens * args.steps / elapsed
+
+    # ---- roofline of the dominant kernel (algorithmic work per launch)
+    n_act = len(active)
+    K, I = cfg.K, cfg.I
+    if cfg.w_dtype == "mxfp8":
+        wbytes = 1.0 + 1.0 / 32
+        dtype_name = "bf16 activations, MXFP8 weights"
+    else:
+        wbytes = 2.0
+        dtype_name = "bf16"
+    if contiguous:
+        dom = "gate_up_act"
+        t_dom = stage_ms[dom] * 1e-3
+        w1_bytes = n_act * 2 * I * K * wbytes
+        alg_bytes = w1_bytes + n_tok_read * K * 2 + n_routes * I * (2 if cfg.w_dtype == "bf16" else 1 + 1 / 32)
+        alg_flops = 4.0 * n_routes * K * I
+        kernel_files = ["gemm_stream.hip"] if plan.variant == moe.VARIANT_STREAM else ["gemm_tile.hip"]
+        if cfg.w_dtype == "mxfp8":
+            kernel_files = ["gemm_stream.hip", "reduce_codec.hip"]
+    else:
+        dom = "apply_batched"
+        t_dom = stage_ms[dom] * 1e-3
+        alg_bytes = n_act * 3 * I * K * wbytes + 2 * n_routes * K * 2
+        alg_flops = 6.0 * n_routes * K * I
+        kernel_files = ["gemm_tile.hip"]
+    flops_per_byte = alg_flops / alg_bytes
+    mfma_bound = flops_per_byte > (PEAK_TFLOPS["bf16"] * 1e12) / (PEAK_HBM_GBS * 1e9)
+    if mfma_bound:
+        achieved = alg_flops / t_dom / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4)}
+    else:
+        achieved = alg_bytes / t_dom / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["kernel"] = dom
+    roof["kernel_ms"] = round(stage_ms[dom], 4)
+    roof["algorithmic_per_launch"] = {"bytes": int(alg_bytes), "flops": int(alg_flops)}
+    roof["traffic"] = traffic_record(cfg.name.split("_")[0], kernel_files)
+
+    # ---- CPU oracle on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, inp, w1, w2, w_f32, args.cpu_sample)
+
+    step_gbs = (n_act * 3 * I * K * wbytes) / (ms_per_step * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded counter-based generator; random-init expert weights)",
+        "config": {"workload": cfg.name, "M": cfg.M, "K": K, "I": I, "E": cfg.E, "topk": cfg.topk,
+                   "max_tokens": cfg.max_tokens, "weights": dtype_name, "routes": n_routes,
+                   "active_experts": n_act, "variant": plan.reason.decode()},
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "step_weight_GBps": round(step_gbs, 1),
+        "step_TFLOPs": round(6.0 * n_routes * K * I / (ms_per_step * 1e-3) / 1e12, 3),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(cfg, inp, w1, w2, w_f32, sample):
+    """The oracle, as it stands, on a bounded sample: its wall time turned
+    into the same unit (tokens/s)."""
+    import numpy as np
+    import torch
+
+    import moe_inputs as mi
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    if cfg.layout == "contiguous":
+        n = sample or {"tiny": 64, "decode": 1, "prefill": 2, "mxfp8": 4}.get(cfg.name.split("_")[0], 1)
+        ids = inp.topk_ids
+        valid = (ids >= 0) & (ids < cfg.E)
+        cand = np.flatnonzero(valid.any(axis=1))
+        tokens = cand[:n]
+        experts = sorted({int(e) for e in ids[tokens][valid[tokens]]})
+        # stage host copies of the inputs (not timed): raw bf16 bits or float32
+        if w_f32 is not None:
+            host = {e: (w_f32[0][e].cpu().numpy(), w_f32[1][e].cpu().numpy()) for e in experts}
+            dec = lambda a: oracle.mxfp8_dequantize(*oracle.mxfp8_quantize(a))
+        else:
+            host = {e: (mi.bf16_bits(inp.w1[e]), mi.bf16_bits(inp.w2[e])) for e in experts}
+            dec = oracle.bf16_to_f64
+        x = mi.bf16_bits(inp.x[torch.from_numpy(tokens).cuda()])
+        t0 = time.perf_counter()
+        xr = oracle.bf16_to_f64(x)
+        oracle.moe_contiguous(xr, tokens, ids, inp.topk_weights, cfg.E, lambda e: dec(host[e][0]),
+                              lambda e: dec(host[e][1]), cfg.w1_order)
+        dt = time.perf_counter() - t0
+        what = f"{len(tokens)} tokens ({int(valid[tokens].sum())} routes over {len(experts)} experts)"
+        units = len(tokens)
+    else:
+        counts = inp.expert_num_tokens
+        n = sample or 2
+        es = [int(e) for e in np.argsort(counts)[:n] if counts[e] > 0]   # the lightest experts
+        host = {e: (mi.bf16_bits(inp.w1[e]), mi.bf16_bits(inp.w2[e]),
+                    mi.bf16_bits(inp.a[e][: counts[e]])) for e in es}
+        t0 = time.perf_counter()
+        rows = 0
+        for e in es:
+            oracle.expert_ffn(oracle.bf16_to_f64(host[e][2]), oracle.bf16_to_f64(host[e][0]),
+                              oracle.bf16_to_f64(host[e][1]))
+            rows += int(counts[e])
+        dt = time.perf_counter() - t0
+        what = f"{rows} batched rows of experts {es} (out tokens/s scaled by 512 tokens / V rows)"
+        units = rows * cfg.M / max(1, int(counts.sum()))
+    return {"value": round(units / dt, 4), "unit": "tokens/s", "cores": int(blas_threads),
+            "kind": "oracle", "sample": what, "seconds": round(dt, 2),
+            "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,259 @@
+/*
+ * moe_mi355x.h — C ABI of the fused-MoE expert computation for one AMD
+ * MI355X (gfx950).
+ *
+ * What it computes is the expert side of the vLLM modular kernel: the steps
+ * of FusedMoEExpertsModular::apply() listed on the page "Fused MoE Modular
+ * Kernel" (section "FusedMoEExpertsModular / apply()"): permute the routes by
+ * expert, multiply by W1 (gate and up projections), SiLU-and-mul, optionally
+ * quantise the intermediate, multiply by W2, unpermute, and apply the top-k
+ * weights with a reduction.  Inputs follow that page's two activation formats
+ * (introduction): contiguous (M,K) activations with (M,topk) ids and weights,
+ * id -1 meaning a skipped slot; and batched (E,max_tokens,K) activations with
+ * expert_num_tokens[E].
+ *
+ * Conventions shared by every call:
+ *  - Pointers marked "device" are HIP device (or managed) memory; "host"
+ *    pointers are ordinary host memory.  Every buffer is owned by the caller;
+ *    the library never allocates, frees, or keeps a pointer after returning.
+ *  - Dense tensors are row-major with the last index contiguous; element
+ *    types are named per argument.  bf16 is the upper half of an IEEE
+ *    binary32; E4M3 is the OCP FP8 E4M3FN format; UE8M0 is a biased power-of
+ *    two exponent byte (value 2^(code-127)).
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Every
+ *    call only enqueues kernels on it: no host synchronisation, no device
+ *    allocation.  Grid sizes depend only on the plan, so calls can be
+ *    captured in a HIP graph.
+ *  - Return value: MOE_OK (0) or an error code.  On an error nothing has been
+ *    enqueued, except MOE_EHIP (a launch failed; earlier kernels of the same
+ *    call may have been enqueued).  No C++ exception crosses this boundary.
+ *  - Device buffers must be 16-byte aligned.
+ *  - Calls are reentrant; a plan is immutable after moe_plan_init.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* Status codes. */
+enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,        /* null/misaligned pointer, bad size or enum value   */
+  MOE_EUNSUPPORTED = 2,  /* valid but not built; the plan's reason says why   */
+  MOE_EHIP = 3           /* a kernel launch failed                            */
+};
+
+/* Activation format (page "Fused MoE Modular Kernel", introduction and
+ * FusedMoEActivationFormat in "activation_formats()"). */
+enum { MOE_LAYOUT_CONTIGUOUS = 0, MOE_LAYOUT_BATCHED = 1 };
+
+/* Expert weight element type. */
+enum {
+  MOE_W_BF16 = 0,
+  /* E4M3 codes plus one UE8M0 scale per 32 consecutive elements along the
+   * contraction dimension (K for W1, I for W2), scale exponent
+   * ceil(log2(blockmax/448)) + 127 clamped to [0,254], 0 for an all-zero block
+   * (page "Cake MegaMoE EP16 backend for BF16 activations and MXFP8 weights",
+   * section 2, the new scale rule). */
+  MOE_W_MXFP8 = 1
+};
+
+/* Row order of W1 [E, 2I, K]. */
+enum {
+  MOE_W1_HALVES = 0,        /* rows [0,I) gate, rows [I,2I) up                 */
+  MOE_W1_INTERLEAVE16 = 1   /* blocks of 32 rows: 16 gate rows, then the 16
+                               matching up rows (same page, section 2)          */
+};
+
+/* Kernel family (chosen by moe_plan_init unless forced). */
+enum {
+  MOE_VARIANT_AUTO = -1,
+  MOE_VARIANT_TILE = 0,     /* LDS-tiled grouped GEMM: both operands staged     */
+  MOE_VARIANT_STREAM = 1    /* few rows per expert: weight rows streamed from
+                               HBM straight into the MFMA row operand, the few
+                               token rows in the other operand                  */
+};
+
+/* Which TopKWeightAndReduce the caller's finalize must apply (page "Fused MoE
+ * Modular Kernel", section "TopKWeightAndReduce"). */
+enum {
+  MOE_REDUCE_NOOP = 0,          /* apply() already reduced (contiguous)         */
+  MOE_REDUCE_CONTIGUOUS = 1,
+  MOE_REDUCE_NAIVE_BATCHED = 2  /* batched: call moe_topk_reduce_naive_batched */
+};
+
+typedef struct moe_problem {
+  int64_t M;           /* contiguous: tokens; batched: output tokens          */
+  int64_t K;           /* hidden size                                         */
+  int64_t I;           /* intermediate size (W1 has 2I rows)                  */
+  int64_t E;           /* experts held by this GPU                            */
+  int64_t topk;        /* contiguous: slots per token; batched: ignored       */
+  int64_t max_tokens;  /* batched: rows per expert slab; contiguous: ignored  */
+  int32_t layout;      /* MOE_LAYOUT_*                                        */
+  int32_t w_dtype;     /* MOE_W_*                                             */
+  int32_t w1_order;    /* MOE_W1_*                                            */
+  int32_t variant;     /* MOE_VARIANT_* (AUTO lets the plan choose)           */
+} moe_problem;
+
+typedef struct moe_weights {
+  const void* w1;          /* device. bf16 or E4M3 [E, 2I, K]                  */
+  const uint8_t* w1_scale; /* device. UE8M0 [E, 2I, K/32] (MXFP8 only)         */
+  const void* w2;          /* device. bf16 or E4M3 [E, K, I]                   */
+  const uint8_t* w2_scale; /* device. UE8M0 [E, K, I/32] (MXFP8 only)          */
+} moe_weights;
+
+/* A plan: validated sizes, the chosen kernels and the workspace layout.  The
+ * offsets are byte offsets inside ws13 and are documented so that tests can
+ * inspect the intermediate results; callers otherwise treat ws13/ws2 as
+ * opaque.  (Workspaces as in "workspace_shapes()": the plan states their
+ * sizes, the caller allocates them once at the largest size it needs.) */
+typedef struct moe_plan {
+  moe_problem prob;
+  int32_t abi_version;
+  int32_t variant;         /* MOE_VARIANT_TILE or MOE_VARIANT_STREAM          */
+  int32_t block_m;         /* align tile size B: expert runs padded to it     */
+  int32_t reduce_kind;     /* MOE_REDUCE_*                                    */
+  int64_t routes;          /* R: M*topk (contiguous) or E*max_tokens (batched)*/
+  int64_t sorted_capacity; /* positions in sorted_ids (worst case over routings)*/
+  int64_t max_tiles;       /* sorted_capacity / block_m                       */
+  int64_t max_active;      /* min(E, R): experts that can hold a route        */
+  int64_t align_blocks;    /* blocks of the multi-block align path (0: single)*/
+  int64_t ws13_bytes;      /* size of workspace 13                            */
+  int64_t ws2_bytes;       /* size of workspace 2                             */
+  int64_t out_rows, out_cols;
+  /* ws13 sub-buffers (int32 unless noted) */
+  int64_t off_counts;      /* [E]    routes per expert                         */
+  int64_t off_offsets;     /* [E+1]  padded exclusive scan of counts            */
+  int64_t off_sorted_ids;  /* [sorted_capacity] flat slot t*topk+j, or R       */
+  int64_t off_block_expert;/* [max_tiles] owner expert of each tile, or -1     */
+  int64_t off_num_post_padded; /* [1] offsets[E]                              */
+  int64_t off_active;      /* [max_active+1] experts with routes, ascending;
+                              element max_active holds their number            */
+  int64_t off_status;      /* [4] [0]: ids outside {-1} U [0,E) seen          */
+  int64_t off_align_scratch; /* per-block histograms of the multi-block path  */
+  int64_t off_z;           /* intermediate silu(gate)*up rows, in sorted
+                              order: bf16 [sorted_capacity, I], or E4M3
+                              [sorted_capacity, I] for MXFP8 (batched: rows
+                              e*max_tokens + r)                                */
+  int64_t off_z_scale;     /* MXFP8: UE8M0 [rows of z, I/32]                   */
+  int64_t off_xq;          /* MXFP8: E4M3 activations gathered in sorted order
+                              [sorted_capacity, K]                              */
+  int64_t off_xq_scale;    /* MXFP8: UE8M0 [sorted_capacity, K/32]             */
+  char reason[192];        /* why this variant / why unsupported              */
+} moe_plan;
+
+/* ABI version of the loaded library; compare with MOE_ABI_VERSION to catch a
+ * stale shared object (page "Cake deterministic MoE grouped GEMM", review
+ * follow-up: a prebuilt library whose argument list no longer matches). */
+int moe_abi_version(void);
+
+/* Static string for a status code. */
+const char* moe_status_string(int status);
+
+/* sizeof(moe_problem), sizeof(moe_plan) and sizeof(moe_weights) as compiled
+ * into the library, for bindings that lay the structs out themselves.
+ * Each pointer may be NULL. */
+void moe_struct_sizes(int64_t* problem, int64_t* plan, int64_t* weights);
+
+/* Validate `prob` (host) and fill `plan` (host).  Chooses the kernel variant
+ * (STREAM when at most 64 rows can reach one expert, else TILE), the align
+ * tile size, the workspace sizes and the reduce kind (NOOP for contiguous,
+ * NAIVE_BATCHED for batched).  Errors: MOE_EINVAL for null pointers,
+ * non-positive sizes, topk > E, bad enum values or index ranges past 2^31;
+ * MOE_EUNSUPPORTED (with plan->reason set) for K % 128, I % 64 != 0 and
+ * similar shapes no kernel is built for. */
+int moe_plan_init(moe_plan* plan, const moe_problem* prob);
+
+/* plan->reason. */
+const char* moe_plan_reason(const moe_plan* plan);
+
+/* Permute (page "Fused MoE Modular Kernel", apply() step 1): group the flat
+ * routes t*topk+j of `topk_ids` (device, int32 [M, topk]) by expert.  Writes
+ * into ws13 (device, plan->ws13_bytes): counts, offsets (each expert's run
+ * padded to block_m), sorted_ids (ascending flat order within an expert;
+ * padding holds R = M*topk), block_expert (-1 past the last run),
+ * num_post_padded, the active-expert list and the status word.  Ids outside
+ * {-1} U [0,E) are skipped and counted in status[0].  Contiguous plans only. */
+int moe_align_permute(const moe_plan* plan, const int32_t* topk_ids, void* ws13, void* stream);
+
+/* The whole expert computation on the contiguous format (page "Fused MoE
+ * Modular Kernel", apply(); reduce kind NOOP: the top-k weighted sum is done
+ * here).  a: device bf16 [M, K]; topk_ids: device int32 [M, topk];
+ * topk_weights: device float32 [M, topk]; w: host struct of device pointers;
+ * out: device bf16 [M, K] — out[t] = bf16(sum_j w[t,j] * y[t,j]) summed in
+ * ascending j in float32, +0.0 for a token with no valid slot; ws13, ws2:
+ * device, plan->ws13_bytes and plan->ws2_bytes.  ws2 receives the per-(token,
+ * slot) W2 outputs y (bf16 [M*topk, K]; rows of skipped slots untouched). */
+int moe_apply_contiguous(const moe_plan* plan, const void* a, const int32_t* topk_ids,
+                         const float* topk_weights, const moe_weights* w, void* out,
+                         void* ws13, void* ws2, void* stream);
+
+/* The two matmul stages of moe_apply_contiguous on their own, for callers
+ * that time or overlap them (contiguous plans; moe_align_permute must have
+ * filled ws13 first, on the same stream).
+ * moe_gate_up_act: matmul with W1, SiLU-and-mul, and for MXFP8 weights the
+ * quantisation of the gathered activations and of the intermediate ("Fused
+ * MoE Modular Kernel", apply() steps 2-4).  Writes z into ws13.
+ * moe_down_unpermute: matmul with W2 and unpermute (steps 5-6): writes each
+ * route's row to its (token, slot) row of ws2 (bf16 [M*topk, K]).
+ * Arguments as for moe_apply_contiguous. */
+int moe_gate_up_act(const moe_plan* plan, const void* a, const moe_weights* w, void* ws13,
+                    void* stream);
+int moe_down_unpermute(const moe_plan* plan, const moe_weights* w, void* ws13, void* ws2,
+                       void* stream);
+
+/* The expert computation on the batched format (page "Fused MoE Modular
+ * Kernel", introduction: batched activations with expert_num_tokens; reduce
+ * kind NAIVE_BATCHED).  a: device bf16 [E, max_tokens, K];
+ * expert_num_tokens: device int32 [E] (each in [0, max_tokens]); y: device
+ * bf16 [E, max_tokens, K] — y[e, r] = W2_e(silu(W1g_e a[e,r]) * W1u_e
+ * a[e,r]) for r < expert_num_tokens[e]; rows past the count are neither read
+ * nor written.  ws13: device, plan->ws13_bytes. */
+int moe_apply_batched(const moe_plan* plan, const void* a, const int32_t* expert_num_tokens,
+                      const moe_weights* w, void* y, void* ws13, void* stream);
+
+/* TopKWeightAndReduceContiguous on its own.  y: device bf16 [M*topk, K], row
+ * t*topk+j is slot (t, j); out: device bf16 [M, K]; same arithmetic as the
+ * reduce inside moe_apply_contiguous. */
+int moe_topk_reduce_contiguous(const moe_plan* plan, const void* y, const int32_t* topk_ids,
+                               const float* topk_weights, void* out, void* stream);
+
+/* Bytes of workspace moe_topk_reduce_naive_batched needs for n_out tokens. */
+int64_t moe_naive_batched_ws_bytes(const moe_plan* plan, int64_t n_out);
+
+/* TopKWeightAndReduceNaiveBatched (page "Fused MoE Modular Kernel", section
+ * "TopKWeightAndReduce"): out[tok] = bf16(sum of row_weight[e,r] * y[e,r]
+ * over valid rows (r < expert_num_tokens[e]) with row_token[e,r] == tok),
+ * summed in float32 in ascending (e, r) order; tokens no row maps to get
+ * +0.0.  y: device bf16 [E, max_tokens, K]; expert_num_tokens: device int32
+ * [E]; row_token: device int32 [E, max_tokens] (valid rows in [0, n_out));
+ * row_weight: device float32 [E, max_tokens]; out: device bf16 [n_out, K];
+ * ws: device, moe_naive_batched_ws_bytes(plan, n_out).  Invalid rows' map
+ * entries are never read; valid rows mapping outside [0, n_out) are skipped
+ * and counted in the first int32 of ws (written by every call). */
+int moe_topk_reduce_naive_batched(const moe_plan* plan, const void* y,
+                                  const int32_t* expert_num_tokens, const int32_t* row_token,
+                                  const float* row_weight, int64_t n_out, void* out, void* ws,
+                                  void* stream);
+
+/* MXFP8 codec on its own (page "Cake MegaMoE EP16 backend for BF16
+ * activations and MXFP8 weights", section 2): each row of x (device, [rows,
+ * cols], float32 if x_dtype == 0, bf16 if x_dtype == 1) is cut into blocks of
+ * 32 columns; codes (device, uint8 [rows, cols]) get the E4M3 encoding
+ * (round to nearest even) of x / 2^(s-127) and scales (device, uint8 [rows,
+ * cols/32]) the scale code s of the rule above.  cols % 32 must be 0.  This is
+ * how MXFP8 weights are produced for moe_apply_*. */
+int moe_quantize_mxfp8(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* codes,
+                       uint8_t* scales, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,245 @@
+// Permute step of the expert computation ("Fused MoE Modular Kernel",
+// apply(), step 1): a stable counting sort of the flat routes t*topk+j by
+// expert, each expert's run padded to the GEMM tile size.
+//
+// histogram -> exclusive scan of the padded counts -> stable scatter.  The
+// scatter is stable (ascending flat index inside an expert) because routes
+// are taken in index order: in the multi-block path each workgroup owns a
+// contiguous chunk and starts at the scanned count of the chunks before it;
+// inside a workgroup the waves take their 64 routes in turn, and inside a
+// wave a lane's rank among the lanes with the same key comes from ballots.
+// Integer-only, so the result is the same on every run.
+//
+// Small problems (R <= kAlignSmallMaxR) run as one workgroup in one launch
+// (decode batches are launch-latency bound); larger ones as three launches.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+struct KeyRead {
+  int key;
+  bool valid;    // a route of a bucket
+  bool invalid;  // read, not -1, out of range
+};
+
+__device__ __forceinline__ KeyRead read_key(const AlignArgs& a, int64_t i) {
+  KeyRead r{-1, false, false};
+  if (a.group_count) {
+    const int64_t g = i / a.rows_per_group;
+    const int64_t row = i - g * a.rows_per_group;
+    if (row >= a.group_count[g]) return r;  // masked row: never read
+  }
+  const int k = a.keys[i];
+  r.key = k;
+  r.valid = k >= 0 && k < a.nb;
+  r.invalid = !r.valid && k != -1;
+  return r;
+}
+
+// Exclusive scan over the workgroup (blockDim.x a multiple of 64, <= 1024).
+// s_tmp needs 17 ints.  Returns the exclusive prefix; *total gets the sum.
+__device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
+  const int lane = __lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int nwaves = blockDim.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == kWave - 1) s_tmp[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < nwaves; ++w) {
+      const int t = s_tmp[w];
+      s_tmp[w] = run;
+      run += t;
+    }
+    s_tmp[16] = run;
+  }
+  __syncthreads();
+  const int res = x - v + s_tmp[wave];
+  *total = s_tmp[16];
+  __syncthreads();
+  return res;
+}
+
+// Largest e with s_off[e] <= pos (s_off non-decreasing, s_off[0] = 0).
+__device__ __forceinline__ int find_bucket(const int* s_off, int nb, int pos) {
+  int lo = 0, hi = nb - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_off[mid] <= pos) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// From per-bucket counts in s_cnt: offsets, counts, active list, tile owners
+// and padding sentinels.  Run by one workgroup.  s_off needs nb+1 ints.
+__device__ void finish_layout(const AlignArgs& a, int* s_cnt, int* s_off, int* s_tmp) {
+  const int nb = a.nb;
+  const int nt = blockDim.x;
+  const int per = (nb + nt - 1) / nt;
+  const int e0 = min(nb, (int)threadIdx.x * per);
+  const int e1 = min(nb, e0 + per);
+  int psum = 0, asum = 0;
+  for (int e = e0; e < e1; ++e) {
+    const int c = s_cnt[e];
+    psum += (c + a.B - 1) / a.B * a.B;
+    asum += c > 0;
+  }
+  int total, n_active;
+  int pbase = block_exclusive_scan(psum, s_tmp, &total);
+  int abase = block_exclusive_scan(asum, s_tmp, &n_active);
+  for (int e = e0; e < e1; ++e) {
+    const int c = s_cnt[e];
+    s_off[e] = pbase;
+    a.offsets[e] = pbase;
+    a.counts[e] = c;
+    pbase += (c + a.B - 1) / a.B * a.B;
+    if (c > 0) a.active[abase++] = e;
+  }
+  if (threadIdx.x == 0) {
+    s_off[nb] = total;
+    a.offsets[nb] = total;
+    a.num_post[0] = total;
+    a.active[a.max_active] = n_active;
+  }
+  for (int64_t i = n_active + threadIdx.x; i < a.max_active; i += nt) a.active[i] = -1;
+  __syncthreads();
+  for (int64_t b = threadIdx.x; b < a.max_tiles; b += nt) {
+    const int64_t pos = b * a.B;
+    a.block_bucket[b] = pos >= total ? -1 : find_bucket(s_off, nb, (int)pos);
+  }
+  for (int64_t p = threadIdx.x; p < a.capacity; p += nt) {
+    bool pad = p >= total;
+    if (!pad) {
+      const int e = find_bucket(s_off, nb, (int)p);
+      pad = p >= s_off[e] + s_cnt[e];
+    }
+    if (pad) a.sorted[p] = a.sentinel;
+  }
+}
+
+// Place routes [begin, end) in index order; s_cur[e] is the next free
+// position of bucket e and is advanced.  Waves take turns.
+__device__ void scatter_range(const AlignArgs& a, int64_t begin, int64_t end, int* s_cur) {
+  const int nt = blockDim.x;
+  const int wave = threadIdx.x / kWave;
+  const int nwaves = nt / kWave;
+  for (int64_t base = begin; base < end; base += nt) {
+    const int64_t i = base + threadIdx.x;
+    KeyRead kr{-1, false, false};
+    if (i < end) kr = read_key(a, i);
+    int rank, gsize;
+    bool last;
+    wave_match_rank(kr.key, kr.valid, rank, gsize, last);
+    for (int w = 0; w < nwaves; ++w) {
+      if (w == wave && kr.valid) {
+        const int b0 = s_cur[kr.key];
+        a.sorted[b0 + rank] = (int32_t)i;
+        if (last) s_cur[kr.key] = b0 + gsize;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__global__ void __launch_bounds__(1024) align_small_kernel(AlignArgs a) {
+  __shared__ int s_cnt[kAlignMaxBuckets];
+  __shared__ int s_off[kAlignMaxBuckets + 1];
+  __shared__ int s_tmp[17];
+  __shared__ int s_invalid;
+  for (int e = threadIdx.x; e < a.nb; e += blockDim.x) s_cnt[e] = 0;
+  if (threadIdx.x == 0) s_invalid = 0;
+  __syncthreads();
+  int inv = 0;
+  for (int64_t i = threadIdx.x; i < a.R; i += blockDim.x) {
+    const KeyRead kr = read_key(a, i);
+    if (kr.valid) atomicAdd(&s_cnt[kr.key], 1);
+    inv += kr.invalid;
+  }
+  if (inv) atomicAdd(&s_invalid, inv);
+  __syncthreads();
+  if (threadIdx.x == 0) a.status[0] = s_invalid;
+  finish_layout(a, s_cnt, s_off, s_tmp);
+  __syncthreads();
+  for (int e = threadIdx.x; e < a.nb; e += blockDim.x) s_cnt[e] = s_off[e];
+  __syncthreads();
+  scatter_range(a, 0, a.R, s_cnt);
+}
+
+// Multi-block path, launch 1: per-chunk histograms (column nb: invalid ids).
+__global__ void __launch_bounds__(256) align_hist_kernel(AlignArgs a) {
+  __shared__ int s_cnt[kAlignMaxBuckets + 1];
+  for (int e = threadIdx.x; e <= a.nb; e += blockDim.x) s_cnt[e] = 0;
+  __syncthreads();
+  const int64_t begin = (int64_t)blockIdx.x * kAlignChunk;
+  const int64_t end = min(a.R, begin + kAlignChunk);
+  int inv = 0;
+  for (int64_t i = begin + threadIdx.x; i < end; i += blockDim.x) {
+    const KeyRead kr = read_key(a, i);
+    if (kr.valid) atomicAdd(&s_cnt[kr.key], 1);
+    inv += kr.invalid;
+  }
+  if (inv) atomicAdd(&s_cnt[a.nb], inv);
+  __syncthreads();
+  int32_t* h = a.block_hist + (int64_t)blockIdx.x * (a.nb + 1);
+  for (int e = threadIdx.x; e <= a.nb; e += blockDim.x) h[e] = s_cnt[e];
+}
+
+// Launch 2: scan the chunk histograms per bucket (in place: each chunk's
+// starting rank), then the layout.
+__global__ void __launch_bounds__(1024) align_scan_kernel(AlignArgs a) {
+  __shared__ int s_cnt[kAlignMaxBuckets + 1];
+  __shared__ int s_off[kAlignMaxBuckets + 1];
+  __shared__ int s_tmp[17];
+  const int stride = a.nb + 1;
+  for (int e = threadIdx.x; e <= a.nb; e += blockDim.x) {
+    int run = 0;
+    for (int b = 0; b < a.nblocks; ++b) {
+      int32_t* p = a.block_hist + (int64_t)b * stride + e;
+      const int v = *p;
+      *p = run;
+      run += v;
+    }
+    s_cnt[e] = run;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) a.status[0] = s_cnt[a.nb];
+  finish_layout(a, s_cnt, s_off, s_tmp);
+}
+
+// Launch 3: each chunk scatters its routes from its starting ranks.
+__global__ void __launch_bounds__(256) align_scatter_kernel(AlignArgs a) {
+  __shared__ int s_cur[kAlignMaxBuckets];
+  const int32_t* h = a.block_hist + (int64_t)blockIdx.x * (a.nb + 1);
+  for (int e = threadIdx.x; e < a.nb; e += blockDim.x) s_cur[e] = a.offsets[e] + h[e];
+  __syncthreads();
+  const int64_t begin = (int64_t)blockIdx.x * kAlignChunk;
+  const int64_t end = min(a.R, begin + kAlignChunk);
+  scatter_range(a, begin, end, s_cur);
+}
+
+}  // namespace
+
+hipError_t launch_align(const AlignArgs& a, hipStream_t s) {
+  if (a.nblocks == 0) {
+    hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(1024), 0, s, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(align_hist_kernel, dim3(a.nblocks), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(1024), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(align_scatter_kernel, dim3(a.nblocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,107 @@
+// Device-side helpers shared by the gfx950 kernels: vector types for the
+// MFMA builtins, bf16 rounding, wave-level match, and the MXFP8 encoder.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(i32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// float -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + expf(-v)); }
+
+// Rank of this lane among the active lanes of its wave holding the same key
+// (lower lanes first), the size of that group, and whether this lane is the
+// group's last.  The loop runs once per distinct key in the wave.
+__device__ __forceinline__ void wave_match_rank(int key, bool valid, int& rank, int& gsize,
+                                                bool& is_last) {
+  const int lane = __lane_id();
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint64_t pending = __ballot(valid);
+  rank = 0;
+  gsize = 0;
+  is_last = false;
+  while (pending) {
+    const int leader = __ffsll((unsigned long long)pending) - 1;
+    const int lk = __shfl(key, leader);
+    const bool mine = valid && key == lk;
+    const uint64_t m = __ballot(mine);
+    if (mine) {
+      rank = __popcll(m & below);
+      gsize = __popcll(m);
+      is_last = rank == gsize - 1;
+    }
+    pending &= ~m;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8 (E4M3FN elements, UE8M0 block scales)
+// ---------------------------------------------------------------------------
+
+// Scale code of a block whose largest magnitude is bm (a float32 >= 0):
+// e = smallest integer with 448 * 2^e >= bm, code = clamp(e + 127, 0, 254),
+// and 0 for an all-zero block.  With bm = f * 2^q, f in [1, 2):
+// 448 * 2^e = 1.75 * 2^(e+8), so e = q - 8 + (f > 1.75).  A subnormal bm
+// (< 2^-126) always clamps to 0.
+__device__ __forceinline__ uint32_t mx_scale_code(float bm) {
+  const uint32_t u = __float_as_uint(bm) & 0x7fffffffu;
+  const uint32_t ef = u >> 23;
+  if (ef == 0) return 0u;
+  const uint32_t mant = u & 0x7fffffu;
+  int e = (int)ef - 127 - 8 + (mant > 0x600000u ? 1 : 0);
+  int code = e + 127;
+  code = code < 0 ? 0 : (code > 254 ? 254 : code);
+  return (uint32_t)code;
+}
+
+// 2^(127 - code) as a float, i.e. the reciprocal of the decoded scale.  code
+// is in [0, 254], so the exponent 127 - code lies in [-127, 127]; 2^-127 is a
+// float32 subnormal and is built from its bit pattern.
+__device__ __forceinline__ float mx_inv_scale(uint32_t code) {
+  const int ex = 127 - (int)code;
+  if (ex >= -126) return __uint_as_float((uint32_t)(ex + 127) << 23);
+  return __uint_as_float(0x00400000u);  // 2^-127 = 2^22 * 2^-149
+}
+
+// E4M3FN code of v, |v| <= 448, round to nearest even, sign kept.
+// Normal results (|v| >= 2^-6) round the 23-bit float32 mantissa to 3 bits;
+// a carry out of the mantissa moves to the next binade by itself.  Below
+// 2^-6 the grid is uniform with step 2^-9, so the code is rint(|v| * 2^9).
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  uint32_t code;
+  if (a < 0x3c800000u) {  // |v| < 2^-6
+    code = (uint32_t)rintf(__uint_as_float(a) * 512.0f);
+  } else {
+    const uint32_t ex = (a >> 23) - 127u + 7u;  // biased E4M3 exponent, >= 1
+    const uint32_t keep = (a >> 20) & 7u;
+    const uint32_t rem = a & 0xfffffu;
+    code = (ex << 3) | keep;
+    if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) code += 1u;
+  }
+  return code | sign;
+}
+
+}  // namespace moe

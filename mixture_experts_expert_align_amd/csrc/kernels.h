@@ -1,0 +1,112 @@
+// Host-side launchers of the gfx950 kernels, used by the C ABI layer
+// (moe_api.hip).  Each returns hipSuccess or the launch error; none
+// allocates or synchronises.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- align ----
+// Stable counting sort of R flat keys into nb buckets.  Key i is valid when
+// 0 <= key < nb and, if group_count is given, (i % rows_per_group) <
+// group_count[i / rows_per_group] (the batched format's valid rows).  Keys
+// other than -1 that are out of range count in status[0] (keys of rows
+// masked out by group_count are never read).
+struct AlignArgs {
+  const int32_t* keys;
+  int64_t R;
+  int32_t nb;
+  int32_t B;                   // each bucket's run is padded to a multiple of B
+  const int32_t* group_count;  // optional
+  int32_t rows_per_group;
+  int32_t* counts;             // [nb]
+  int32_t* offsets;            // [nb+1]
+  int32_t* sorted;             // [capacity]  values: flat index i, or sentinel
+  int32_t* block_bucket;       // [max_tiles]
+  int32_t* num_post;           // [1]
+  int32_t* active;             // [max_active+1]
+  int32_t* status;             // [>=1]
+  int32_t* block_hist;         // [nblocks * nb]  (multi-block path)
+  int64_t capacity;
+  int64_t max_tiles;
+  int64_t max_active;
+  int32_t sentinel;
+  int32_t nblocks;             // 0: single-block path
+};
+
+constexpr int kAlignSmallMaxR = 8192;    // single-workgroup path up to this R
+constexpr int kAlignChunk = 4096;        // keys per workgroup in the multi-block path
+constexpr int kAlignMaxBuckets = 8192;   // LDS-resident bucket counters
+
+hipError_t launch_align(const AlignArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- gemms ----
+enum Epilogue { kEpiGateUp = 0, kEpiDown = 1 };
+
+// Rows a GEMM works on: the routes of each expert in sorted (align) order for
+// the contiguous format, or rows r < count[e] of each expert's slab for the
+// batched format.
+struct RowMap {
+  int32_t layout;              // 0 contiguous, 1 batched
+  const int32_t* sorted_ids;   // contiguous
+  const int32_t* block_expert; // contiguous (tile path)
+  const int32_t* num_post;     // contiguous
+  const int32_t* offsets;      // contiguous (stream path)
+  const int32_t* counts;       // contiguous: routes per expert; batched: valid rows
+  const int32_t* active;       // contiguous (stream path)
+  int32_t topk;
+  int32_t sentinel;
+  int32_t max_tokens;          // batched
+};
+
+struct GemmArgs {
+  int32_t epi;
+  RowMap rows;
+  // activations: W1 reads x (contiguous, gathered by token) or the batched
+  // slab; W2 reads z in position order
+  const void* act;
+  const uint8_t* act_scale;    // MXFP8 only
+  int64_t act_ld;              // elements per activation row
+  // weights
+  const void* w;
+  const uint8_t* w_scale;      // MXFP8 only
+  int64_t w_expert_stride;     // elements per expert
+  int32_t kdim;                // contraction length
+  int32_t nfeat;               // W1: I; W2: K
+  int32_t I;
+  int32_t w1_order;            // 0 halves, 1 interleave16
+  int32_t E;
+  int64_t max_tiles;           // contiguous tile grid
+  int64_t max_active;          // stream grid
+  // outputs
+  void* out;                   // W1: z; W2: y rows
+  uint8_t* out_scale;          // W1 MXFP8: z scales
+  int64_t out_ld;
+};
+
+hipError_t launch_gemm_tile_bf16(const GemmArgs& g, hipStream_t s);
+hipError_t launch_gemm_stream_bf16(const GemmArgs& g, hipStream_t s);
+hipError_t launch_gemm_stream_mxfp8(const GemmArgs& g, hipStream_t s);
+
+// --------------------------------------------------------------- reduce ----
+hipError_t launch_reduce_contiguous(const uint16_t* y, const int32_t* ids, const float* w,
+                                    uint16_t* out, int64_t M, int32_t topk, int64_t K, int32_t E,
+                                    hipStream_t s);
+// out[t] = sum over CSR list of t (ascending) of w[row] * y[row]
+hipError_t launch_reduce_csr(const uint16_t* y, const float* w, const int32_t* offsets,
+                             const int32_t* rows, uint16_t* out, int64_t n_out, int64_t K,
+                             hipStream_t s);
+
+// ---------------------------------------------------------------- codec ----
+hipError_t launch_quantize_mxfp8(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                                 uint8_t* codes, uint8_t* scales, hipStream_t s);
+// MXFP8 rows of x gathered in sorted order: row p <- x[sorted_ids[p] / topk]
+// (sentinel rows are zero-filled), for p < capacity.
+hipError_t launch_quantize_gather_mxfp8(const uint16_t* x, const int32_t* sorted_ids,
+                                        const int32_t* num_post, int32_t topk, int32_t sentinel,
+                                        int64_t capacity, int64_t K, uint8_t* codes,
+                                        uint8_t* scales, hipStream_t s);
+
+}  // namespace moe

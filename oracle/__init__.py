@@ -86,24 +86,31 @@ def e4m3fn_table() -> np.ndarray:
 
 
 _E4M3 = e4m3fn_table()
-_E4M3_POS = _E4M3[:127]          # codes 0x00..0x7E: 0 .. 448, strictly increasing
 
 
 def e4m3fn_encode(v: np.ndarray) -> np.ndarray:
     """Round float64 values with |v| <= 448 to the nearest E4M3FN code, ties to
     the even code (even mantissa), keeping the sign bit of v (so -0.0 and
-    negative values that round to zero give 0x80)."""
+    negative values that round to zero give 0x80).
+
+    The finite E4M3FN magnitudes are a uniform grid: step 2^-9 on [0, 2^-6]
+    (subnormals, then the first normal binade has the same step) and step
+    2^(E-3) on each binade [2^E, 2^(E+1)), E = -6..8.  |v|'s neighbours on its
+    grid are k*step and (k+1)*step with k = floor(|v|/step); the nearer one
+    wins, a tie goes to even k.  Code = 8*(E+7) + k - 8 (k = 16 is the first
+    value of the next binade, which the same formula encodes)."""
     v = np.asarray(v, dtype=np.float64)
     a = np.abs(v)
     if np.any(~np.isfinite(a)) or np.any(a > E4M3_MAX):
         raise ValueError("e4m3fn_encode: value outside the finite E4M3FN range")
-    hi = np.searchsorted(_E4M3_POS, a, side="left")          # first code with value >= a
-    hi = np.minimum(hi, 126)
-    lo = np.maximum(hi - 1, 0)
-    d_lo = a - _E4M3_POS[lo]
-    d_hi = _E4M3_POS[hi] - a
-    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
-    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    _, p = np.frexp(a)                                   # a = f * 2^p, f in [0.5, 1)
+    E = np.where(a < 2.0 ** -6, -6, p - 1).astype(np.int32)
+    q = a / np.ldexp(1.0, E - 3)                         # |v| in grid steps; exact
+    k = np.floor(q)
+    r = q - k                                            # distance past the lower neighbour
+    ki = k.astype(np.int64)
+    ki += (r > 0.5) | ((r == 0.5) & ((ki & 1) == 1))
+    code = (8 * (E.astype(np.int64) + 7) + ki - 8).astype(np.uint8)
     neg = np.signbit(v)
     return np.where(neg, code | np.uint8(0x80), code).astype(np.uint8)
 
@@ -136,17 +143,24 @@ def mxfp8_quantize(x: np.ndarray):
 
     x: float array [..., n] with n % 32 == 0 (float32 or bf16-decoded values).
     Returns (codes uint8 [..., n], scales uint8 [..., n/32]) with
-    decoded value = E4M3(code) * 2^(scale - 127)."""
-    x = np.asarray(x, dtype=np.float64)
+    decoded value = E4M3(code) * 2^(scale - 127).  Blocks are independent;
+    rows are taken a slab at a time only to keep temporaries small."""
+    x = np.asarray(x)
     n = x.shape[-1]
     if n % 32:
         raise ValueError("mxfp8_quantize: last dimension must be a multiple of 32")
-    blocks = x.reshape(*x.shape[:-1], n // 32, 32)
-    bm = np.abs(blocks).max(axis=-1)
-    sc = mx_scale_code(bm)
-    s = np.ldexp(1.0, sc.astype(np.int64) - 127)
-    q = e4m3fn_encode(blocks / s[..., None])      # exact: s is a power of two
-    return q.reshape(x.shape), sc
+    flat = x.reshape(-1, n)
+    codes = np.empty(flat.shape, dtype=np.uint8)
+    scales = np.empty((flat.shape[0], n // 32), dtype=np.uint8)
+    step = max(1, (1 << 19) // n)
+    for r0 in range(0, flat.shape[0], step):
+        blocks = flat[r0:r0 + step].astype(np.float64).reshape(-1, n // 32, 32)
+        bm = np.abs(blocks).max(axis=-1)
+        sc = mx_scale_code(bm)
+        s = np.ldexp(1.0, sc.astype(np.int32) - 127)
+        codes[r0:r0 + step] = e4m3fn_encode(blocks / s[..., None]).reshape(-1, n)  # exact division
+        scales[r0:r0 + step] = sc
+    return codes.reshape(x.shape), scales.reshape(*x.shape[:-1], n // 32)
 
 
 def mxfp8_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:

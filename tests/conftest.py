@@ -27,3 +27,19 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def _keep_freed_memory_in_heap():
+    """Large numpy temporaries are otherwise mmap'ed and unmapped on every
+    allocation; on hosts where first-touch page faults are slow that dominates
+    the oracle's run time.  Keep freed memory in the heap for reuse."""
+    try:
+        import ctypes
+        libc = ctypes.CDLL("libc.so.6")
+        libc.mallopt(-3, 1 << 30)                  # M_MMAP_THRESHOLD
+        libc.mallopt(-1, ctypes.c_int(2 ** 31 - 1))  # M_TRIM_THRESHOLD
+    except Exception:  # pragma: no cover
+        pass
+
+
+_keep_freed_memory_in_heap()

@@ -1,0 +1,114 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every
+function include/moe_mi355x.h declares, agrees with the binding on struct
+layouts, and validates problems / lays out workspaces as documented."""
+import os
+import re
+
+import pytest
+
+import moe_inputs as mi
+import mixture_experts_expert_align_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    names = set()
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", f)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(moe_\w+)\s*\(", src))
+    return names
+
+
+def test_library_exports_every_declared_function():
+    lib = moe.load_library()
+    names = header_functions()
+    assert {"moe_plan_init", "moe_apply_contiguous", "moe_apply_batched", "moe_align_permute",
+            "moe_topk_reduce_contiguous", "moe_topk_reduce_naive_batched",
+            "moe_quantize_mxfp8"} <= names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_strings():
+    assert moe.moe_abi_version() == moe.ABI_VERSION
+    assert moe.moe_status_string(0) == "ok"
+    assert moe.moe_status_string(2) == "unsupported problem"
+
+
+def plan_for(cfg, **kw):
+    prob = moe.make_problem(cfg.M, cfg.K, cfg.I, cfg.E, topk=cfg.topk, max_tokens=cfg.max_tokens,
+                            layout=0 if cfg.layout == "contiguous" else 1,
+                            w_dtype=0 if cfg.w_dtype == "bf16" else 1,
+                            w1_order=0 if cfg.w1_order == "halves" else 1, **kw)
+    return moe.moe_plan_init(prob)
+
+
+@pytest.mark.parametrize("idx", range(5))
+def test_plans_of_the_five_workloads(idx):
+    cfg = mi.config(idx)
+    p = plan_for(cfg)
+    if cfg.layout == "contiguous":
+        R = cfg.M * cfg.topk
+        assert p.routes == R and p.reduce_kind == moe.REDUCE_NOOP
+        B = p.block_m
+        assert p.max_active == min(cfg.E, R)
+        assert p.max_tiles == (R + p.max_active * (B - 1)) // B
+        assert p.sorted_capacity == p.max_tiles * B
+        assert p.ws2_bytes >= R * cfg.K * 2
+        assert p.out_rows == cfg.M and p.out_cols == cfg.K
+    else:
+        assert p.reduce_kind == moe.REDUCE_NAIVE_BATCHED and p.variant == moe.VARIANT_TILE
+    expected_variant = {0: moe.VARIANT_TILE, 1: moe.VARIANT_STREAM, 2: moe.VARIANT_TILE,
+                        3: moe.VARIANT_STREAM, 4: moe.VARIANT_TILE}[idx]
+    assert p.variant == expected_variant, p.reason
+    # sub-buffers are in order, 256-byte aligned, and inside ws13
+    offs = [p.off_counts, p.off_offsets, p.off_sorted_ids, p.off_block_expert,
+            p.off_num_post_padded, p.off_active, p.off_status, p.off_align_scratch, p.off_z]
+    if cfg.w_dtype == "mxfp8":
+        offs += [p.off_z_scale, p.off_xq, p.off_xq_scale]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert offs[-1] < p.ws13_bytes
+    if idx == 2:
+        assert p.sorted_capacity == 81792            # 65536 + 128 * 127
+    if idx == 4:
+        assert moe.moe_naive_batched_ws_bytes(p, 512) > 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=0), moe.MOE_EINVAL), (dict(K=-1), moe.MOE_EINVAL), (dict(topk=9), moe.MOE_EINVAL),
+    (dict(layout=7), moe.MOE_EINVAL), (dict(w_dtype=3), moe.MOE_EINVAL),
+    (dict(variant=5), moe.MOE_EINVAL), (dict(K=4000), moe.MOE_EUNSUPPORTED),
+    (dict(I=100), moe.MOE_EUNSUPPORTED), (dict(M=1 << 30), moe.MOE_EINVAL), (dict(M=1 << 28), moe.MOE_EUNSUPPORTED),
+    (dict(layout=1, max_tokens=0), moe.MOE_EINVAL),
+    (dict(layout=1, max_tokens=64, variant=moe.VARIANT_STREAM), moe.MOE_EUNSUPPORTED),
+    (dict(layout=1, max_tokens=64, w_dtype=moe.W_MXFP8), moe.MOE_EUNSUPPORTED),
+    (dict(w_dtype=moe.W_MXFP8, variant=moe.VARIANT_TILE), moe.MOE_EUNSUPPORTED),
+    (dict(w1_order=moe.W1_INTERLEAVE16, I=72), moe.MOE_EINVAL),
+])
+def test_plan_validation(kw, code):
+    base = dict(M=64, K=256, I=512, E=8, topk=2)
+    base.update(kw)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_plan_init(moe.make_problem(**base))
+    assert ei.value.status == code
+    assert str(ei.value)
+
+
+def test_variant_choice_and_override():
+    p = moe.moe_plan_init(moe.make_problem(16, 256, 512, 8, topk=2))
+    assert p.variant == moe.VARIANT_STREAM
+    p = moe.moe_plan_init(moe.make_problem(17, 256, 512, 8, topk=2))
+    assert p.variant == moe.VARIANT_TILE and p.block_m == 128
+    p = moe.moe_plan_init(moe.make_problem(17, 256, 512, 8, topk=2, variant=moe.VARIANT_STREAM))
+    assert p.variant == moe.VARIANT_STREAM and p.block_m == 16
+    assert "stream" in moe.moe_plan_reason(p)
+
+
+def test_align_path_choice():
+    small = moe.moe_plan_init(moe.make_problem(1024, 256, 512, 8, topk=8))     # R = 8192
+    big = moe.moe_plan_init(moe.make_problem(1025, 256, 512, 8, topk=8))       # R = 8200
+    assert small.align_blocks == 0
+    assert big.align_blocks == 3

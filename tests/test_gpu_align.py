@@ -1,0 +1,108 @@
+"""moe_align_permute on the GPU against the oracle's align, bit for bit:
+counts, padded offsets, sorted route ids (stable), tile owners, padded
+total, the active-expert list and the invalid-id count.  Both the
+one-workgroup path (R <= 8192) and the three-launch path are covered, at
+both tile sizes the plans use (128 tiled, 16 streaming)."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import mixture_experts_expert_align_amd as moe
+import oracle
+from moe_cases import say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_align(ids: np.ndarray, E: int, variant: int):
+    M, topk = ids.shape
+    plan = moe.moe_plan_init(moe.make_problem(M, 256, 512, E, topk=topk, variant=variant))
+    ws13 = torch.full((plan.ws13_bytes,), 0xAB, dtype=torch.uint8, device="cuda")   # poison
+    dev = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
+    moe.moe_align_permute(plan, dev, ws13)
+    torch.cuda.synchronize()
+    v = lambda off, n: moe.ws_view(ws13, off, n).cpu().numpy()
+    got = {
+        "counts": v(plan.off_counts, E),
+        "offsets": v(plan.off_offsets, E + 1),
+        "sorted_ids": v(plan.off_sorted_ids, plan.sorted_capacity),
+        "block_expert": v(plan.off_block_expert, plan.max_tiles),
+        "num_post_padded": int(v(plan.off_num_post_padded, 1)[0]),
+        "active": v(plan.off_active, plan.max_active + 1),
+        "status": int(v(plan.off_status, 1)[0]),
+    }
+    return plan, got
+
+
+def check(ids, E, variant, label):
+    plan, got = run_align(ids, E, variant)
+    ref = oracle.align_permute(ids, E, plan.block_m)
+    say(f"[align] {label}: R={ids.size} E={E} B={plan.block_m} path="
+        f"{'multi' if plan.align_blocks else 'single'} post={ref['num_post_padded']}")
+    assert plan.sorted_capacity == ref["capacity"] and plan.max_tiles == ref["max_tiles"]
+    assert np.array_equal(got["counts"], ref["counts"])
+    assert np.array_equal(got["offsets"], ref["offsets"])
+    assert got["num_post_padded"] == ref["num_post_padded"]
+    assert np.array_equal(got["sorted_ids"], ref["sorted_ids"])
+    assert np.array_equal(got["block_expert"], ref["block_expert"])
+    assert got["status"] == ref["n_invalid"]
+    act = [e for e in range(E) if ref["counts"][e] > 0]
+    want = np.array(act + [-1] * (plan.max_active - len(act)) + [len(act)], dtype=np.int32)
+    assert np.array_equal(got["active"], want)
+
+
+def random_ids(seed, M, topk, E, p_skip=0.0, p_bad=0.0, distinct=True):
+    rng = np.random.default_rng(seed)
+    if distinct and topk <= E:
+        ids = np.stack([rng.permutation(E)[:topk] for _ in range(M)])
+    else:
+        ids = rng.integers(0, E, (M, topk))
+    ids = ids.astype(np.int32)
+    ids[rng.random((M, topk)) < p_skip] = -1
+    bad = rng.random((M, topk)) < p_bad
+    ids[bad] = rng.choice([E, E + 7, -2, -1000], size=int(bad.sum()))
+    return ids
+
+
+@pytest.mark.parametrize("variant", [moe.VARIANT_TILE, moe.VARIANT_STREAM])
+@pytest.mark.parametrize("idx", [0, 1, 2, 3])
+def test_align_workload_routings(idx, variant):
+    cfg = mi.config(idx)
+    ids = mi.make_routing(cfg)[0]
+    check(ids, cfg.E, variant, cfg.name)
+
+
+CASES = [
+    ("one_route", 1, 1, 1, 0.0, 0.0),
+    ("tiny_skips_bad", 37, 3, 5, 0.2, 0.1),
+    ("small_path_limit", 1024, 8, 64, 0.05, 0.0),      # R = 8192: one workgroup
+    ("multi_path_ragged", 1025, 8, 64, 0.05, 0.01),    # R = 8200: three launches, ragged chunk
+    ("many_experts", 16, 8, 2048, 0.0, 0.0),
+    ("wide_multi", 3001, 6, 300, 0.3, 0.0),
+    ("dup_ids", 200, 3, 3, 0.0, 0.0),
+]
+
+
+@pytest.mark.parametrize("variant", [moe.VARIANT_TILE, moe.VARIANT_STREAM])
+@pytest.mark.parametrize("name,M,topk,E,p_skip,p_bad", CASES, ids=[c[0] for c in CASES])
+def test_align_random(name, M, topk, E, p_skip, p_bad, variant):
+    ids = random_ids(zlib.crc32(name.encode()) % 1000, M, topk, E, p_skip, p_bad,
+                     distinct=name != "dup_ids")
+    check(ids, E, variant, name)
+
+
+@pytest.mark.parametrize("M", [5, 2000])
+def test_align_all_skipped(M):
+    ids = np.full((M, 4), -1, dtype=np.int32)
+    check(ids, 8, moe.VARIANT_TILE, f"all_skipped_M{M}")
+
+
+def test_align_deterministic():
+    ids = random_ids(3, 8192, 8, 128, 0.01, 0.0)
+    _, a = run_align(ids, 128, moe.VARIANT_TILE)
+    _, b = run_align(ids, 128, moe.VARIANT_TILE)
+    for k in a:
+        assert np.array_equal(np.asarray(a[k]), np.asarray(b[k])), k

@@ -1,0 +1,194 @@
+"""The whole expert computation on the GPU (through the C ABI) against the
+oracle.
+
+Scaled cases (every output element checked) keep each workload's recipe at
+sizes the oracle finishes in seconds while still spanning several tiles, a
+ragged tail and, for MXFP8, more than one 64-token pass per expert.  The
+full-size cases run the five workloads in the launch configuration bench.py
+times and check sampled tokens one by one.  Tolerances: bf16 weights
+|gpu - ref| <= 2e-2 * max|ref| + 1e-3 per element, MXFP8 weights
+<= 6e-2 * max|ref|, max|ref| over the checked outputs.  Also: bitwise run-to-run
+equality, +0.0 for tokens with no valid slot, nullity of weight-0 / id -1
+slots, token-shuffle equivariance."""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import mixture_experts_expert_align_amd as moe
+import oracle
+from moe_cases import (BF16_ABS, BF16_REL, MX_REL, check_close, make_case, oracle_contiguous,
+                       oracle_weights, run_batched, run_contiguous, sample_tokens, say, _host_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+def tol(cfg):
+    return (MX_REL, 0.0) if cfg.w_dtype == "mxfp8" else (BF16_REL, BF16_ABS)
+
+
+def free():
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+SCALED = [
+    ("tiny", mi.config(0), moe.VARIANT_AUTO),
+    ("tiny_stream", mi.config(0), moe.VARIANT_STREAM),
+    ("decode_m4", mi.config(1).scaled(K=512, I=1024), moe.VARIANT_AUTO),
+    ("decode_m13", mi.config(1).scaled(M=13, K=512, I=1024), moe.VARIANT_AUTO),
+    ("decode_m4_tile", mi.config(1).scaled(K=512, I=1024), moe.VARIANT_TILE),
+    ("prefill_m1000", mi.config(2).scaled(M=1000, K=256, I=192, E=16), moe.VARIANT_AUTO),
+    ("prefill_m100_stream", mi.config(2).scaled(M=100, K=256, I=256, E=16), moe.VARIANT_STREAM),
+    ("mxfp8_m512", mi.config(3).scaled(M=512, K=512, I=256), moe.VARIANT_AUTO),
+    ("mxfp8_m4160", mi.config(3).scaled(M=4160, K=512, I=256), moe.VARIANT_AUTO),
+]
+
+
+@pytest.mark.parametrize("name,cfg,variant", SCALED, ids=[s[0] for s in SCALED])
+def test_contiguous_scaled(name, cfg, variant):
+    c = make_case(cfg)
+    out, plan, ws13, ws2 = run_contiguous(c, variant)
+    say(f"[moe] {name}: variant {plan.variant} ({plan.reason.decode()})")
+    tokens = np.arange(cfg.M)
+    ref = oracle_contiguous(c, tokens)
+    check_close(out, ref, *tol(cfg), name)
+    empty = np.flatnonzero(((c.inp.topk_ids < 0) | (c.inp.topk_ids >= cfg.E)).all(axis=1))
+    if empty.size:
+        assert np.all(out[torch.from_numpy(empty).cuda()].view(torch.int16).cpu().numpy() == 0)
+    out2, *_ = run_contiguous(c, variant)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), "run-to-run bits differ"
+    assert int(moe.ws_view(ws13, plan.off_status, 1).cpu()[0]) == 0
+
+
+def test_tiny_intermediate_z():
+    """z = silu(x W1g^T) * (x W1u^T) at each sorted position (tile path)."""
+    cfg = mi.config(0)
+    c = make_case(cfg)
+    out, plan, ws13, _ = run_contiguous(c)
+    sorted_ids = moe.ws_view(ws13, plan.off_sorted_ids, plan.sorted_capacity).cpu().numpy()
+    npost = int(moe.ws_view(ws13, plan.off_num_post_padded, 1).cpu()[0])
+    z = moe.ws_view(ws13, plan.off_z, plan.sorted_capacity * cfg.I, torch.bfloat16).view(-1, cfg.I)
+    z = z[:npost].float().cpu().numpy()
+    w1_of, _ = oracle_weights(c)
+    x = _host_f64(c.inp.x)
+    for p in range(npost):
+        sid = sorted_ids[p]
+        if sid == cfg.M * cfg.topk:
+            assert np.all(z[p] == 0)
+            continue
+        t, j = divmod(int(sid), cfg.topk)
+        g, u = oracle.split_gate_up(w1_of(int(c.inp.topk_ids[t, j])), cfg.w1_order)
+        ref = oracle.silu(x[t] @ g.T) * (x[t] @ u.T)
+        assert np.abs(z[p] - ref).max() <= 2e-2 * np.abs(ref).max() + 1e-3, p
+
+
+def test_nullity_and_equivariance():
+    cfg = mi.config(2).scaled(M=300, K=256, I=192, E=16)
+    c = make_case(cfg)
+    base, *_ = run_contiguous(c)
+    ids, w = c.inp.topk_ids.copy(), c.inp.topk_weights.copy()
+    w0 = w.copy(); w0[7, 3] = 0.0
+    ids_m = ids.copy(); ids_m[7, 3] = -1
+    a, *_ = run_contiguous(c, ids=torch.from_numpy(ids).cuda(), wts=torch.from_numpy(w0).cuda())
+    b, *_ = run_contiguous(c, ids=torch.from_numpy(ids_m).cuda(), wts=torch.from_numpy(w).cuda())
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))          # weight 0 == skipped
+    keep = torch.from_numpy(np.delete(np.arange(cfg.M), 7)).cuda()
+    assert torch.equal(a[keep].view(torch.int16), base[keep].view(torch.int16))
+    perm = np.random.default_rng(3).permutation(cfg.M)
+    pt = torch.from_numpy(perm).cuda()
+    s, *_ = run_contiguous(c, ids=torch.from_numpy(ids[perm]).cuda(),
+                           wts=torch.from_numpy(w[perm]).cuda(), x=c.inp.x[pt].contiguous())
+    ref = oracle_contiguous(c, np.arange(cfg.M))
+    check_close(s, ref[perm], BF16_REL, BF16_ABS, "shuffled")
+    say(f"[moe] shuffle bitwise equal: {torch.equal(s.view(torch.int16), base[pt].view(torch.int16))}")
+
+
+def test_all_slots_skipped():
+    cfg = mi.config(0)
+    c = make_case(cfg)
+    ids = torch.full((cfg.M, cfg.topk), -1, dtype=torch.int32, device="cuda")
+    out, *_ = run_contiguous(c, ids=ids)
+    assert np.all(out.view(torch.int16).cpu().numpy() == 0)
+
+
+def test_batched_scaled():
+    cfg = mi.config(4).scaled(E=8, max_tokens=100, K=256, I=128, M=64, slot_pool=400)
+    c = make_case(cfg)
+    junk = torch.arange(cfg.max_tokens, device="cuda")[None, :] >= c.counts[:, None]
+    c.inp.a[junk] = float("nan")                   # rows past the counts are never read
+    y, out, plan = run_batched(c)
+    w1_of, w2_of = oracle_weights(c)
+    counts = c.inp.expert_num_tokens
+    a_host = c.inp.a.cpu()
+    ys = oracle.moe_batched_rows(lambda e, r: _host_f64(a_host[e][torch.from_numpy(r)]), counts,
+                                 w1_of, w2_of)
+    for e, (rows, ye) in ys.items():
+        check_close(y[e][torch.from_numpy(rows).cuda()], ye, BF16_REL, BF16_ABS, f"batched y e={e}")
+    ref = oracle.naive_batched_reduce(lambda e, r: ys[e][1][r], counts, c.inp.row_token,
+                                      c.inp.row_weight, cfg.M, cfg.K)
+    check_close(out, ref, BF16_REL, BF16_ABS, "batched out")
+    y2, out2, _ = run_batched(c)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+# ------------------------------------------------------------- full size --
+
+def test_full_decode():
+    cfg = mi.config(1)
+    c = make_case(cfg)
+    out, plan, *_ = run_contiguous(c)
+    assert plan.variant == moe.VARIANT_STREAM
+    ref = oracle_contiguous(c, np.arange(cfg.M))
+    check_close(out, ref, BF16_REL, BF16_ABS, cfg.name)
+    del c; free()
+
+
+def test_full_prefill():
+    cfg = mi.config(2)
+    c = make_case(cfg)
+    out, plan, *_ = run_contiguous(c)
+    out2, *_ = run_contiguous(c)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), "run-to-run bits differ"
+    tokens = sample_tokens(cfg.M, 6, seed=2)
+    ref = oracle_contiguous(c, tokens)
+    check_close(out[torch.from_numpy(tokens).cuda()], ref, BF16_REL, BF16_ABS, cfg.name)
+    del c; free()
+
+
+def test_full_mxfp8_share():
+    cfg = mi.config(3)
+    c = make_case(cfg)
+    out, plan, ws13, _ = run_contiguous(c)
+    ids = c.inp.topk_ids
+    nloc = (ids >= 0).sum(axis=1)
+    # tokens whose local routes touch only experts 0 and 1, plus tokens with none
+    on01 = np.flatnonzero((nloc > 0) & np.all((ids < 0) | (ids <= 1), axis=1))
+    tokens = np.sort(np.concatenate([on01[:10], np.flatnonzero(nloc == 0)[:6]]))
+    ref = oracle_contiguous(c, tokens)
+    check_close(out[torch.from_numpy(tokens).cuda()], ref, MX_REL, 0.0, cfg.name)
+    none = torch.from_numpy(np.flatnonzero(nloc == 0)).cuda()
+    assert np.all(out[none].view(torch.int16).cpu().numpy() == 0)       # 2304 tokens, exactly +0.0
+    counts = moe.ws_view(ws13, plan.off_counts, cfg.E).cpu().numpy()
+    assert np.all(counts == 64)
+    del c; free()
+
+
+def test_full_batched():
+    cfg = mi.config(4)
+    c = make_case(cfg)
+    y, out, plan = run_batched(c)
+    y2, out2, _ = run_batched(c)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    counts = c.inp.expert_num_tokens
+    w1_of, w2_of = oracle_weights(c)
+    # sampled rows of three experts (hottest, middle, coldest)
+    for e in (0, 15, 31):
+        rows = np.unique(np.concatenate([[0, counts[e] - 1], np.arange(0, counts[e], max(1, counts[e] // 5))]))
+        rows = rows[(rows >= 0) & (rows < counts[e])]
+        a = _host_f64(c.inp.a[e][torch.from_numpy(rows).cuda()])
+        ref = oracle.expert_ffn(a, w1_of(e), w2_of(e))
+        check_close(y[e][torch.from_numpy(rows).cuda()], ref, BF16_REL, BF16_ABS, f"{cfg.name} y e={e}")
+    del c; free()
