@@ -13,10 +13,10 @@
 // so what carries over is only that the weight rows occupy the row slot and
 // stream without staging.
 //
-// The contraction is split among the four 16-lane groups of a wave and among
-// the MFMA's own k slots in any fixed way, provided both operands use the
-// same split: lane group q reads elements [base + 32q, base + 32q + 32) of
-// each step (a contiguous 64-byte bf16 run or a 32-byte E4M3 MX block).
+// Which k each lane feeds the MFMA may follow any fixed assignment as long
+// as both operands use the same one, so the loads are laid out for memory:
+// the lanes of one load instruction cover a contiguous run of each of 16
+// weight rows.
 //
 // Grid: (feature strips, active experts).  The active-expert list comes from
 // the align step, so the grid depends only on the plan; workgroups whose
@@ -28,6 +28,7 @@ namespace moe {
 namespace {
 
 constexpr int NT = 256;
+constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data format (CDNA3/4 word 3)
 
 __device__ __forceinline__ i32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const i32x4*>(p); }
 __device__ __forceinline__ i32x4 ld16nt(const void* p) {
@@ -40,10 +41,23 @@ __device__ __forceinline__ int w1_row(int f, bool up, int I, int order) {
 }
 
 // ------------------------------------------------------------------ bf16 --
-// Each wave: two 16-row weight tiles t0/t1.  kGateUp: 16 features (gate
-// rows, then up rows).  kDown: 32 features (two tiles of 16).
-template <int EPI>
-__global__ void __launch_bounds__(NT) gemm_stream_bf16_kernel(GemmArgs g) {
+// A workgroup owns 16 output features of one expert and KS waves split the
+// contraction into KS equal runs; each wave streams its run of the weight
+// rows with a three-deep register pipeline, the partial sums meet in LDS and
+// wave 0 adds them in wave order (a fixed order, so every run gives the same
+// bits) before the epilogue.  Splitting the contraction keeps each
+// workgroup's task short, so the last wave of workgroups on the chip is short
+// too; with a whole contraction per workgroup the tail of the grid left much
+// of the chip idle.
+//   kGateUp: two 16-row tiles: the gate rows and the matching up rows of the
+//            16 features; epilogue z = silu(gate) * up, bf16, row = position.
+//   kDown:   one 16-row tile of W2; epilogue writes y rows per (token, slot).
+// Per lane and 128-wide step, lane group q takes the four 16-byte pieces at
+// k + 8q + 32j (j = 0..3) of its row: the four groups of one load
+// instruction read 64 contiguous bytes of each of 16 rows.
+template <int EPI, int KS>
+__global__ void __launch_bounds__(64 * KS) gemm_stream_bf16_kernel(GemmArgs g) {
+  constexpr int NTL = EPI == kEpiGateUp ? 2 : 1;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const RowMap& rm = g.rows;
@@ -53,87 +67,101 @@ __global__ void __launch_bounds__(NT) gemm_stream_bf16_kernel(GemmArgs g) {
   const int cnt = rm.counts[e];
   const int pos0 = rm.offsets[e];
   const int K = g.kdim;
-  const int q = lane >> 4;   // k lane group
+  const int KW = K / KS;                      // contraction run of this wave
+  const int q = lane >> 4;
   const int l16 = lane & 15;
+  const int kbase = wave * KW + 8 * q;
+  const int f0 = blockIdx.x * 16;
 
+  // Buffer loads: the expert's weights and the activations as two buffer
+  // resources, per-lane 32-bit byte offsets, the step's k in the scalar
+  // offset.  A lane without a token gets an offset past the buffer's size,
+  // which the hardware's range check turns into zeros.
   const uint16_t* wexp = static_cast<const uint16_t*>(g.w) + (int64_t)e * g.w_expert_stride;
-  int f0, r0, r1;
+  const __amdgpu_buffer_rsrc_t wr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)wexp, 0, (int)min<int64_t>(g.w_expert_stride * 2, 0x7fffffff),
+                                        kBufferFlags);
+  const __amdgpu_buffer_rsrc_t ar =
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.act, 0, (int)min<int64_t>(g.act_bytes, 0x7fffffff), kBufferFlags);
+  uint32_t wo[NTL];
   if (EPI == kEpiGateUp) {
-    f0 = (blockIdx.x * 4 + wave) * 16;
-    r0 = w1_row(f0 + l16, false, g.I, g.w1_order);
-    r1 = w1_row(f0 + l16, true, g.I, g.w1_order);
+    wo[0] = (uint32_t)(w1_row(f0 + l16, false, g.I, g.w1_order) * K + kbase) * 2u;
+    wo[NTL - 1] = (uint32_t)(w1_row(f0 + l16, true, g.I, g.w1_order) * K + kbase) * 2u;
   } else {
-    f0 = (blockIdx.x * 4 + wave) * 32;
-    r0 = f0 + l16;
-    r1 = f0 + 16 + l16;
+    wo[0] = (uint32_t)((f0 + l16) * K + kbase) * 2u;
   }
-  const uint16_t* w0 = wexp + (int64_t)r0 * K + 32 * q;
-  const uint16_t* w1 = wexp + (int64_t)r1 * K + 32 * q;
-  const uint16_t* act = static_cast<const uint16_t*>(g.act);
   uint16_t* out = static_cast<uint16_t*>(g.out);
-  const i32x4 zero = {0, 0, 0, 0};
+  __shared__ f32x4 red[KS][NTL][64];
+  const int nsteps = KW / 128;
 
   for (int tg = 0; tg * 16 < cnt; ++tg) {
     const int tk = tg * 16 + l16;
     const bool tv = tk < cnt;
     const int pos = pos0 + tk;
-    const uint16_t* pa = nullptr;
+    uint32_t ao = 0x80000000u;               // past the end: loads return 0
     if (tv) {
-      if (EPI == kEpiGateUp) pa = act + (int64_t)(rm.sorted_ids[pos] / rm.topk) * g.act_ld;
-      else pa = act + (int64_t)pos * g.act_ld;
-      pa += 32 * q;
+      const int64_t row = EPI == kEpiGateUp ? rm.sorted_ids[pos] / rm.topk : pos;
+      ao = (uint32_t)((row * g.act_ld + kbase) * 2);
     }
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    i32x4 a0[2][4], a1[2][4], b[2][4];
+    f32x4 acc[NTL];
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    i32x4 a[3][NTL][4], b[3][4];
     auto load = [&](int st, int k) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        a0[st][j] = ld16nt(w0 + k + 8 * j);
-        a1[st][j] = ld16nt(w1 + k + 8 * j);
-        b[st][j] = pa ? ld16(pa + k + 8 * j) : zero;
+#pragma unroll
+        for (int t = 0; t < NTL; ++t)
+          a[st][t][j] = __builtin_amdgcn_raw_buffer_load_b128(wr, wo[t] + 64 * j, 2 * k, 0);
+        b[st][j] = __builtin_amdgcn_raw_buffer_load_b128(ar, ao + 64 * j, 2 * k, 0);
       }
     };
     auto mma = [&](int st) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0[st][j]), as_bf16x8(b[st][j]), acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1[st][j]), as_bf16x8(b[st][j]), acc1, 0, 0, 0);
-      }
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int t = 0; t < NTL; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[st][t][j]), as_bf16x8(b[st][j]),
+                                                           acc[t], 0, 0, 0);
     };
-    const int nsteps = K / 128;
     load(0, 0);
-    int k = 0;
-    for (int it = 0; it + 1 < nsteps; it += 2) {
-      load(1, k + 128);
+    if (nsteps > 1) load(1, 128);
+    for (int it = 0; it < nsteps; it += 3) {
+      if (it + 2 < nsteps) load(2, 128 * (it + 2));
       mma(0);
-      if (it + 2 < nsteps) load(0, k + 256);
-      mma(1);
-      k += 256;
+      if (it + 3 < nsteps) load(0, 128 * (it + 3));
+      if (it + 1 < nsteps) mma(1);
+      if (it + 4 < nsteps) load(1, 128 * (it + 4));
+      if (it + 2 < nsteps) mma(2);
     }
-    if (nsteps & 1) mma(0);
 
-    // acc[r]: weight row (tile row) 4*q + r, token column l16
-    if (tv) {
-      if (EPI == kEpiGateUp) {
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) red[wave][t][lane] = acc[t];
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int t = 0; t < NTL; ++t) {
+        f32x4 sum = red[0][t][lane];
+        for (int w = 1; w < KS; ++w) sum += red[w][t][lane];
+        acc[t] = sum;
+      }
+      // acc[t][r]: weight row 4*q + r of tile t, token column l16
+      if (tv) {
         uint32_t h[4];
+        int64_t o;
+        if (EPI == kEpiGateUp) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(silu_f32(acc0[r]) * acc1[r]);
-        uint2 v = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-        *reinterpret_cast<uint2*>(out + (int64_t)pos * g.out_ld + f0 + 4 * q) = v;
-      } else {
-        const int64_t orow = rm.sorted_ids[pos];
-        uint32_t h0[4], h1[4];
+          for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(silu_f32(acc[0][r]) * acc[NTL - 1][r]);
+          o = (int64_t)pos * g.out_ld;
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          h0[r] = f32_to_bf16_rne(acc0[r]);
-          h1[r] = f32_to_bf16_rne(acc1[r]);
+          for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(acc[0][r]);
+          o = (int64_t)rm.sorted_ids[pos] * g.out_ld;
         }
-        *reinterpret_cast<uint2*>(out + orow * g.out_ld + f0 + 4 * q) =
-            make_uint2(h0[0] | (h0[1] << 16), h0[2] | (h0[3] << 16));
-        *reinterpret_cast<uint2*>(out + orow * g.out_ld + f0 + 16 + 4 * q) =
-            make_uint2(h1[0] | (h1[1] << 16), h1[2] | (h1[3] << 16));
+        *reinterpret_cast<uint2*>(out + o + f0 + 4 * q) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
       }
     }
+    __syncthreads();
   }
 }
 
@@ -288,14 +316,26 @@ __global__ void __launch_bounds__(NT) gemm_stream_mxfp8_kernel(GemmArgs g) {
 
 }  // namespace
 
-hipError_t launch_gemm_stream_bf16(const GemmArgs& g, hipStream_t s) {
-  const int per_block = g.epi == kEpiGateUp ? 64 : 128;
-  dim3 grid(g.nfeat / per_block, (unsigned)g.max_active);
-  if (g.epi == kEpiGateUp)
-    hipLaunchKernelGGL(gemm_stream_bf16_kernel<kEpiGateUp>, grid, dim3(NT), 0, s, g);
-  else
-    hipLaunchKernelGGL(gemm_stream_bf16_kernel<kEpiDown>, grid, dim3(NT), 0, s, g);
+// Waves per workgroup: as many as divide the contraction into runs that are
+// whole 128-wide steps, up to 4 for W1 and 8 for W2 (the fastest shapes
+// measured for the decode workload).
+template <int EPI>
+static hipError_t launch_stream_bf16(const GemmArgs& g, hipStream_t s, int max_ks) {
+  dim3 grid(g.nfeat / 16, (unsigned)g.max_active);
+  int ks = max_ks;
+  while (ks > 1 && g.kdim % (128 * ks)) ks >>= 1;
+  switch (ks) {
+    case 8: hipLaunchKernelGGL((gemm_stream_bf16_kernel<EPI, 8>), grid, dim3(512), 0, s, g); break;
+    case 4: hipLaunchKernelGGL((gemm_stream_bf16_kernel<EPI, 4>), grid, dim3(256), 0, s, g); break;
+    case 2: hipLaunchKernelGGL((gemm_stream_bf16_kernel<EPI, 2>), grid, dim3(128), 0, s, g); break;
+    default: hipLaunchKernelGGL((gemm_stream_bf16_kernel<EPI, 1>), grid, dim3(64), 0, s, g); break;
+  }
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_stream_bf16(const GemmArgs& g, hipStream_t s) {
+  return g.epi == kEpiGateUp ? launch_stream_bf16<kEpiGateUp>(g, s, 4)
+                             : launch_stream_bf16<kEpiDown>(g, s, 8);
 }
 
 hipError_t launch_gemm_stream_mxfp8(const GemmArgs& g, hipStream_t s) {

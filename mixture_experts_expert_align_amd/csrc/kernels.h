@@ -69,6 +69,7 @@ struct GemmArgs {
   const void* act;
   const uint8_t* act_scale;    // MXFP8 only
   int64_t act_ld;              // elements per activation row
+  int64_t act_bytes;           // size of the activation buffer
   // weights
   const void* w;
   const uint8_t* w_scale;      // MXFP8 only

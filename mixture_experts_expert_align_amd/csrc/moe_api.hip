@@ -139,6 +139,9 @@ int moe_plan_init(moe_plan* plan, const moe_problem* prob) {
       if (!contiguous) return fail(plan, MOE_EUNSUPPORTED, "the streaming kernels take the contiguous format only");
       if (P.K % 128 || P.I % 128)
         return fail(plan, MOE_EUNSUPPORTED, "streaming kernels need K % 128 == 0 and I % 128 == 0");
+      // 32-bit buffer offsets: one expert's W1 and the activation buffers
+      if (4 * P.I * P.K >= (1ll << 31) || 2 * P.M * P.K >= (1ll << 31))
+        return fail(plan, MOE_EUNSUPPORTED, "streaming kernels address one expert with 32-bit offsets");
       snprintf(plan->reason, sizeof(plan->reason),
                "stream: M <= 16 rows per expert, weights streamed into the MFMA row operand");
     } else {
@@ -263,6 +266,7 @@ static int gate_up_act(const moe_plan* plan, const void* a, const moe_weights* w
   }
   g.act = a;
   g.act_ld = P.K;
+  g.act_bytes = P.M * P.K * 2;
   hipError_t e = plan->variant == MOE_VARIANT_STREAM ? launch_gemm_stream_bf16(g, s)
                                                      : launch_gemm_tile_bf16(g, s);
   return e == hipSuccess ? MOE_OK : MOE_EHIP;
@@ -280,6 +284,7 @@ static int down_unpermute(const moe_plan* plan, const moe_weights* w, void* ws13
   g.nfeat = (int32_t)P.K;
   g.act = at<void>(ws13, plan->off_z);
   g.act_ld = P.I;
+  g.act_bytes = plan->sorted_capacity * P.I * 2;
   g.out = ws2;
   g.out_ld = P.K;
   hipError_t e;
