@@ -41,6 +41,14 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=0,
                     help="tokens (or batched rows) the CPU oracle is timed on (0: per-workload default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the oracle sample until this much CPU time has been spent")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run device-to-device copies of this many MiB (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                         "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter files of this "
+                         "workload and of --copy-calibration into profiles/traffic_<workload>.json")
     return ap.parse_args()
 
 
@@ -64,13 +72,84 @@ def traffic_record(cfg_name: str, kernel_files):
     return rec.get("traffic_bytes_per_launch")
 
 
+def copy_calibration(mib: int):
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(COPY_LAUNCHES):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": COPY_LAUNCHES}))
+
+
+def counter_values(path: str, counter: str, kernel_substr: str):
+    """Per-dispatch values (KiB) of one counter for kernels whose name contains
+    kernel_substr, from a rocprofv3 counter_collection.csv."""
+    import csv
+    vals = {}
+    with open(path) as fh:
+        for row in csv.DictReader(fh):
+            if row.get("Counter_Name") != counter or kernel_substr not in row.get("Kernel_Name", ""):
+                continue
+            d = row.get("Dispatch_Id") or row.get("Correlation_Id")
+            vals[d] = vals.get(d, 0.0) + float(row["Counter_Value"])
+    return list(vals.values())
+
+
+def traffic_from(args):
+    import numpy as np
+    cfg_name = args.config.split("_")[0]
+    kern = DOMINANT_KERNEL[cfg_name]
+    fetch = counter_values(args.traffic_from[0], "FETCH_SIZE", kern)
+    write = counter_values(args.traffic_from[1], "WRITE_SIZE", kern)
+    # the calibration run makes COPY_LAUNCHES copies; the runtime may split a
+    # copy over several dispatches, so compare per-copy sums
+    cfetch = sum(counter_values(args.traffic_from[2], "FETCH_SIZE", "copy")) / COPY_LAUNCHES
+    cwrite = sum(counter_values(args.traffic_from[3], "WRITE_SIZE", "copy")) / COPY_LAUNCHES
+    copy_bytes = COPY_MIB << 20
+    f_scale = copy_bytes / (cfetch * 1024)
+    w_scale = copy_bytes / (cwrite * 1024)
+    traffic = np.median(fetch) * 1024 * f_scale + np.median(write) * 1024 * w_scale
+    rec = {"workload": cfg_name, "kernel": kern,
+           "kernel_source_hash": kernel_source_hash(KERNEL_FILES[cfg_name]),
+           "fetch_kib_per_dispatch": float(np.median(fetch)), "write_kib_per_dispatch": float(np.median(write)),
+           "copy_calibration_bytes": copy_bytes,
+           "copy_fetch_kib": float(cfetch), "copy_write_kib": float(cwrite),
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "traffic_bytes_per_launch": int(traffic)}
+    out = os.path.join(ROOT, "profiles", f"traffic_{cfg_name}.json")
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+
+
+COPY_MIB = 1024
+COPY_LAUNCHES = 3
+# The dominant kernel of each workload (name substring in the profiler's
+# kernel names) and the sources it is built from.
+DOMINANT_KERNEL = {"tiny": "gemm_tile_bf16_kernel<0>", "decode": "gemm_stream_bf16_kernel<0,",
+                   "prefill": "gemm_tile_bf16_kernel<0>", "mxfp8": "gemm_stream_mxfp8_kernel<0>",
+                   "batched": "gemm_tile_bf16_kernel<0>"}
+KERNEL_FILES = {"tiny": ["gemm_tile.hip"], "decode": ["gemm_stream.hip"], "prefill": ["gemm_tile.hip"],
+                "mxfp8": ["gemm_stream.hip"], "batched": ["gemm_tile.hip"]}
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from(args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import numpy as np
     import torch
@@ -179,15 +258,11 @@ def main():
         w1_bytes = n_act * 2 * I * K * wbytes
         alg_bytes = w1_bytes + n_tok_read * K * 2 + n_routes * I * (2 if cfg.w_dtype == "bf16" else 1 + 1 / 32)
         alg_flops = 4.0 * n_routes * K * I
-        kernel_files = ["gemm_stream.hip"] if plan.variant == moe.VARIANT_STREAM else ["gemm_tile.hip"]
-        if cfg.w_dtype == "mxfp8":
-            kernel_files = ["gemm_stream.hip", "reduce_codec.hip"]
     else:
         dom = "apply_batched"
         t_dom = stage_ms[dom] * 1e-3
         alg_bytes = n_act * 3 * I * K * wbytes + 2 * n_routes * K * 2
         alg_flops = 6.0 * n_routes * K * I
-        kernel_files = ["gemm_tile.hip"]
     flops_per_byte = alg_flops / alg_bytes
     mfma_bound = flops_per_byte > (PEAK_TFLOPS["bf16"] * 1e12) / (PEAK_HBM_GBS * 1e9)
     if mfma_bound:
@@ -201,12 +276,12 @@ def main():
     roof["kernel"] = dom
     roof["kernel_ms"] = round(stage_ms[dom], 4)
     roof["algorithmic_per_launch"] = {"bytes": int(alg_bytes), "flops": int(alg_flops)}
-    roof["traffic"] = traffic_record(cfg.name.split("_")[0], kernel_files)
+    roof["traffic"] = traffic_record(cfg.name.split("_")[0], KERNEL_FILES[cfg.name.split("_")[0]])
 
     # ---- CPU oracle on a bounded sample of the same workload
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, inp, w1, w2, w_f32, args.cpu_sample)
+        cpu = cpu_baseline(cfg, inp, w1, w2, w_f32, args.cpu_sample, args.cpu_seconds)
 
     step_gbs = (n_act * 3 * I * K * wbytes) / (ms_per_step * 1e-3) / 1e9
     rec = {
@@ -226,9 +301,9 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline(cfg, inp, w1, w2, w_f32, sample):
-    """The oracle, as it stands, on a bounded sample: its wall time turned
-    into the same unit (tokens/s)."""
+def cpu_baseline(cfg, inp, w1, w2, w_f32, sample, min_seconds):
+    """The oracle, as it stands, on a bounded sample, repeated until about
+    ``min_seconds`` of CPU time: its rate in the same unit (tokens/s)."""
     import numpy as np
     import torch
 
@@ -241,7 +316,7 @@ def cpu_baseline(cfg, inp, w1, w2, w_f32, sample):
     except Exception:  # pragma: no cover
         blas_threads = 1
     if cfg.layout == "contiguous":
-        n = sample or {"tiny": 64, "decode": 1, "prefill": 2, "mxfp8": 4}.get(cfg.name.split("_")[0], 1)
+        n = sample or {"tiny": 64, "decode": 4, "prefill": 2, "mxfp8": 4}.get(cfg.name.split("_")[0], 1)
         ids = inp.topk_ids
         valid = (ids >= 0) & (ids < cfg.E)
         cand = np.flatnonzero(valid.any(axis=1))
@@ -255,13 +330,19 @@ def cpu_baseline(cfg, inp, w1, w2, w_f32, sample):
             host = {e: (mi.bf16_bits(inp.w1[e]), mi.bf16_bits(inp.w2[e])) for e in experts}
             dec = oracle.bf16_to_f64
         x = mi.bf16_bits(inp.x[torch.from_numpy(tokens).cuda()])
+        reps = 0
         t0 = time.perf_counter()
-        xr = oracle.bf16_to_f64(x)
-        oracle.moe_contiguous(xr, tokens, ids, inp.topk_weights, cfg.E, lambda e: dec(host[e][0]),
-                              lambda e: dec(host[e][1]), cfg.w1_order)
+        while True:
+            xr = oracle.bf16_to_f64(x)
+            oracle.moe_contiguous(xr, tokens, ids, inp.topk_weights, cfg.E, lambda e: dec(host[e][0]),
+                                  lambda e: dec(host[e][1]), cfg.w1_order)
+            reps += 1
+            if time.perf_counter() - t0 >= min_seconds:
+                break
         dt = time.perf_counter() - t0
-        what = f"{len(tokens)} tokens ({int(valid[tokens].sum())} routes over {len(experts)} experts)"
-        units = len(tokens)
+        what = (f"{len(tokens)} tokens ({int(valid[tokens].sum())} routes over {len(experts)} experts), "
+                f"{reps} passes")
+        units = len(tokens) * reps
     else:
         counts = inp.expert_num_tokens
         n = sample or 2
@@ -270,10 +351,13 @@ def cpu_baseline(cfg, inp, w1, w2, w_f32, sample):
                     mi.bf16_bits(inp.a[e][: counts[e]])) for e in es}
         t0 = time.perf_counter()
         rows = 0
-        for e in es:
-            oracle.expert_ffn(oracle.bf16_to_f64(host[e][2]), oracle.bf16_to_f64(host[e][0]),
-                              oracle.bf16_to_f64(host[e][1]))
-            rows += int(counts[e])
+        while True:
+            for e in es:
+                oracle.expert_ffn(oracle.bf16_to_f64(host[e][2]), oracle.bf16_to_f64(host[e][0]),
+                                  oracle.bf16_to_f64(host[e][1]))
+                rows += int(counts[e])
+            if time.perf_counter() - t0 >= min_seconds:
+                break
         dt = time.perf_counter() - t0
         what = f"{rows} batched rows of experts {es} (out tokens/s scaled by 512 tokens / V rows)"
         units = rows * cfg.M / max(1, int(counts.sum()))
