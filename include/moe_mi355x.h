@@ -166,8 +166,10 @@ void moe_struct_sizes(int64_t* problem, int64_t* plan, int64_t* weights);
  * tile size, the workspace sizes and the reduce kind (NOOP for contiguous,
  * NAIVE_BATCHED for batched).  Errors: MOE_EINVAL for null pointers,
  * non-positive sizes, topk > E, bad enum values or index ranges past 2^31;
- * MOE_EUNSUPPORTED (with plan->reason set) for K % 128, I % 64 != 0 and
- * similar shapes no kernel is built for. */
+ * MOE_EUNSUPPORTED (with plan->reason set) for shapes no kernel is built
+ * for: the tiled kernels need K % 256 == 0 and I % 128 == 0 (contiguous
+ * format) or K % 128 == 0 and I % 64 == 0 (batched format), the streaming
+ * and MXFP8 kernels K % 128 == 0 and I % 128 == 0. */
 int moe_plan_init(moe_plan* plan, const moe_problem* prob);
 
 /* plan->reason. */

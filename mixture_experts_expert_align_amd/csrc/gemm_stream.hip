@@ -5,9 +5,9 @@
 // experts' weights from HBM once.  Each wave owns a strip of weight rows and
 // the whole contraction: the weight rows go from HBM straight into the row
 // operand of the MFMA (16 rows x the contraction slice, each lane reading a
-// contiguous run of one row, no LDS), and the expert's routed tokens (up to
-// 16 per pass for bf16, 64 for MXFP8) sit in the other operand, read from
-// L2.  The Mixture-of-Experts kernel engineering on SageMaker page ("Swap-AB
+// contiguous run of one row, no LDS), and the expert's routed tokens sit in
+// the other operand: up to 16 per pass for bf16, read from L2; 64 per pass
+// for MXFP8, staged once per workgroup in LDS and shared by its waves.  The Mixture-of-Experts kernel engineering on SageMaker page ("Swap-AB
 // for WGMMA utilization") swaps A and B so the weight's large N dimension
 // fills Hopper's fixed 64-row slot; on gfx950 both MFMA slots are 16 wide,
 // so what carries over is only that the weight rows occupy the row slot and
@@ -31,9 +31,6 @@ constexpr int NT = 256;
 constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data format (CDNA3/4 word 3)
 
 __device__ __forceinline__ i32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const i32x4*>(p); }
-__device__ __forceinline__ i32x4 ld16nt(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p));
-}
 
 // W row index of intermediate feature f (gate, or up when up = true).
 __device__ __forceinline__ int w1_row(int f, bool up, int I, int order) {
@@ -174,17 +171,31 @@ __global__ void __launch_bounds__(64 * KS) gemm_stream_bf16_kernel(GemmArgs g) {
 // order, a k step therefore needs, per lane, the 16 bytes at k0 + 16g and the
 // 16 at k0 + 64 + 16g, plus the scale of MX block k0/32 + g: each MX block
 // of the weight and activation rows lines up with exactly one scale.
-// A pass covers 64 tokens (four 16-token column tiles) so each weight
-// fragment feeds four MFMAs.  Each wave: 32 features.
-//   kGateUp: tiles (gate f0..+15, up f0..+15, gate f0+16..+31, up f0+16..+31);
-//            the epilogue quantises silu(gate)*up of the 32 features of each
-//            token as one MX block (E4M3 codes + UE8M0 scale).
-//   kDown:   tiles (f0..+15, f0+16..+31); bf16 y rows per (token, slot).
+//
+// A workgroup owns four 16-row weight tiles of one expert, one per wave; each
+// wave streams its tile over the whole contraction straight from HBM into
+// registers (three steps ahead).  The 64 routed token rows of a pass (four
+// 16-token column tiles) are staged in LDS two 128-wide steps at a time and
+// shared by the four waves, so activations cross L2 once per workgroup.
+//   kGateUp: tiles (gate f0..+15, up f0..+15, gate f0+16..+31, up f0+16..+31),
+//            32 features = one MX block of z per token: the epilogue gathers
+//            the four tiles in LDS and quantises silu(gate)*up (E4M3 codes +
+//            UE8M0 scale).
+//   kDown:   tiles f0 + 16t, 64 features; bf16 y rows per (token, slot).
+constexpr int kMxTok = 64;                 // tokens per pass
+constexpr int kMxSteps = 2;                // 128-wide steps per LDS stage
+constexpr int kMxRow = 128 * kMxSteps;     // bytes of one token row per stage
+
+// LDS byte offset of 16-byte chunk c (0..kMxRow/16-1) of token row r: the
+// chunk index is XOR-ed with bits of r so that the 16 rows a load
+// instruction's lane group reads at one chunk fall in distinct banks.
+__device__ __forceinline__ int mx_lds(int r, int c) { return r * kMxRow + ((c ^ ((r >> 1) & 7)) << 4); }
+
 template <int EPI>
-__global__ void __launch_bounds__(NT) gemm_stream_mxfp8_kernel(GemmArgs g) {
-  constexpr int NTILE = EPI == kEpiGateUp ? 4 : 2;
+__global__ void __launch_bounds__(256) gemm_stream_mxfp8_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = threadIdx.x >> 6;          // = weight tile
+  const int tid = threadIdx.x;
   const RowMap& rm = g.rows;
   const int slot = blockIdx.y;
   if (slot >= rm.active[g.max_active]) return;
@@ -195,122 +206,160 @@ __global__ void __launch_bounds__(NT) gemm_stream_mxfp8_kernel(GemmArgs g) {
   const int KB = K / 32;
   const int q = lane >> 4;
   const int l16 = lane & 15;
-  const int f0 = (blockIdx.x * 4 + wave) * 32;
+  const int f0 = blockIdx.x * (EPI == kEpiGateUp ? 32 : 64);
 
   const uint8_t* wexp = static_cast<const uint8_t*>(g.w) + (int64_t)e * g.w_expert_stride;
   const uint8_t* wsexp = g.w_scale + (int64_t)e * (g.w_expert_stride / 32);
-  const uint8_t* wp[NTILE];
-  const uint8_t* wsp[NTILE];
-#pragma unroll
-  for (int t = 0; t < NTILE; ++t) {
-    int row;
-    if (EPI == kEpiGateUp) row = w1_row(f0 + 16 * (t >> 1) + l16, (t & 1) != 0, g.I, g.w1_order);
-    else row = f0 + 16 * t + l16;
-    wp[t] = wexp + (int64_t)row * K + 16 * q;
-    wsp[t] = wsexp + (int64_t)row * KB + q;
-  }
-  const uint8_t* act = static_cast<const uint8_t*>(g.act);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)wexp, 0, (int)min<int64_t>(g.w_expert_stride, 0x7fffffff), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t wsr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)wsexp, 0, (int)min<int64_t>(g.w_expert_stride / 32, 0x7fffffff), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)g.act, 0, (int)min<int64_t>(g.act_bytes, 0x7fffffff), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t asr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)g.act_scale, 0, (int)min<int64_t>(g.act_bytes / 32, 0x7fffffff), kBufferFlags);
+  int row;
+  if (EPI == kEpiGateUp) row = w1_row(f0 + 16 * (wave >> 1) + l16, (wave & 1) != 0, g.I, g.w1_order);
+  else row = f0 + 16 * wave + l16;
+  const uint32_t wo = (uint32_t)(row * K + 16 * q);
+  const uint32_t wso = (uint32_t)(row * KB + q);
 
-  for (int tg = 0; tg * 64 < cnt; ++tg) {
-    const uint8_t* pa[4];
-    const uint8_t* psa[4];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[2][kMxTok * kMxRow];
+  __shared__ uint32_t sBs[2][kMxTok * kMxSteps];          // 4 scale bytes per token per step
+  __shared__ f32x4 sOut[4][4][64];                        // epilogue: [tile][column tile][lane]
+  const int nsteps = K / 128;
+  const int nstages = (nsteps + kMxSteps - 1) / kMxSteps;   // the last stage may be half used
+
+  // token-tile staging: a stage is 64 rows x 16 chunks of 16 bytes; thread
+  // tid moves chunk tid % 16 of rows tid / 16 + 16 i (i < 4) and, for
+  // tid < 128, one scale word (token tid / 2, step tid % 2)
+  const int srow = tid >> 4, schk = tid & 15;
+  for (int tg = 0; tg * kMxTok < cnt; ++tg) {
+    uint32_t xo[4], xso = 0x80000000u;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int tk = tg * 64 + 16 * c + l16;
-      if (tk < cnt) {
-        const int64_t pos = pos0 + tk;
-        pa[c] = act + pos * g.act_ld + 16 * q;
-        psa[c] = g.act_scale + pos * (g.act_ld / 32) + q;
-      } else {
-        pa[c] = nullptr;
-        psa[c] = nullptr;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int t = tg * kMxTok + srow + 16 * i;
+      // chunk j of a stage row holds bytes 16j .. 16j+15 of the stage's 256-byte span
+      xo[i] = t < cnt ? (uint32_t)((int64_t)(pos0 + t) * g.act_ld + 16 * schk) : 0x80000000u;
     }
-    f32x4 acc[NTILE][4];
+    if (tid < kMxTok * kMxSteps) {
+      const int tt = tg * kMxTok + tid / kMxSteps;
+      if (tt < cnt) xso = (uint32_t)((int64_t)(pos0 + tt) * (g.act_ld / 32) + 4 * (tid % kMxSteps));
+    }
+    i32x4 pb[4];
+    uint32_t pbs = 0;
+    auto bload = [&](int stage) {
+      const int kb = stage * kMxRow;
 #pragma unroll
-    for (int t = 0; t < NTILE; ++t)
+      for (int i = 0; i < 4; ++i) pb[i] = __builtin_amdgcn_raw_buffer_load_b128(ar, xo[i], kb, 0);
+      if (tid < kMxTok * kMxSteps) pbs = __builtin_amdgcn_raw_buffer_load_b32(asr, xso, kb / 32, 0);
+    };
+    auto bstore = [&](int buf) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[t][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<i32x4*>(&sB[buf][mx_lds(srow + 16 * i, schk)]) = pb[i];
+      if (tid < kMxTok * kMxSteps) sBs[buf][tid] = pbs;
+    };
 
-    for (int k = 0; k < K; k += 128) {
-      const int kb = k / 32;
-      i32x8 wa[NTILE];
-      int wsc[NTILE];
+    f32x4 acc[4];
 #pragma unroll
-      for (int t = 0; t < NTILE; ++t) {
-        const i32x4 lo = ld16nt(wp[t] + k);
-        const i32x4 hi = ld16nt(wp[t] + k + 64);
-        wa[t] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        wsc[t] = wsp[t][kb];
-      }
-      i32x8 xb[4];
-      int xsc[4];
+    for (int c = 0; c < 4; ++c) acc[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    // weight fragments: three steps in flight
+    i32x8 wa[3];
+    int wsc[3];
+    auto aload = [&](int i, int step) {
+      const int k = 128 * step;
+      const i32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(wr, wo, k, 0);
+      const i32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(wr, wo + 64, k, 0);
+      wa[i] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      wsc[i] = __builtin_amdgcn_raw_buffer_load_b8(wsr, wso, k / 32, 0);
+    };
+    auto mma = [&](int i, int buf, int sub) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        if (pa[c]) {
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(pa[c] + k);
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(pa[c] + k + 64);
-          xb[c] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          xsc[c] = psa[c][kb];
-        } else {
-          xb[c] = (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
-          xsc[c] = 0;
+        const int tr = 16 * c + l16;
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(&sB[buf][mx_lds(tr, 8 * sub + q)]);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(&sB[buf][mx_lds(tr, 8 * sub + 4 + q)]);
+        const i32x8 xb = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const int xs = (sBs[buf][tr * kMxSteps + sub] >> (8 * q)) & 0xff;
+        acc[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa[i], xb, acc[c], 0, 0, 0, wsc[i], 0, xs);
+      }
+    };
+
+    bload(0);
+    aload(0, 0);
+    if (nsteps > 1) aload(1, 1);
+    bstore(0);
+    __syncthreads();
+    for (int stg = 0; stg < nstages; ++stg) {
+      const int buf = stg & 1;
+      if (stg + 1 < nstages) bload(stg + 1);
+#pragma unroll
+      for (int sub = 0; sub < kMxSteps; ++sub) {
+        const int step = stg * kMxSteps + sub;
+        if (step < nsteps) {
+          if (step + 2 < nsteps) aload((step + 2) % 3, step + 2);
+          mma(step % 3, buf, sub);
         }
       }
-#pragma unroll
-      for (int t = 0; t < NTILE; ++t)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          acc[t][c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              wa[t], xb[c], acc[t][c], 0, 0, 0, wsc[t], 0, xsc[c]);
+      if (stg + 1 < nstages) bstore(buf ^ 1);
+      __syncthreads();
     }
 
-    // acc[t][c][r]: weight row 4*q + r of tile t, token tg*64 + 16*c + l16
+    // acc[c][r]: weight row 4*q + r of this wave's tile, token tg*64 + 16*c + l16
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int tk = tg * 64 + 16 * c + l16;
-      const bool tv = tk < cnt;   // uniform per 16-lane column group only
-      const int64_t pos = pos0 + tk;
-      if (EPI == kEpiGateUp) {
-        float z[8];
+    for (int c = 0; c < 4; ++c) sOut[wave][c][lane] = acc[c];
+    __syncthreads();
+    if (EPI == kEpiGateUp) {
+      // wave c finishes column tile c: 16 tokens x 32 features
+      const int c = wave;
+      const f32x4 g0 = sOut[0][c][lane], u0 = sOut[1][c][lane];
+      const f32x4 g1 = sOut[2][c][lane], u1 = sOut[3][c][lane];
+      float z[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          z[r] = silu_f32(acc[0][c][r]) * acc[1][c][r];
-          z[4 + r] = silu_f32(acc[2][c][r]) * acc[3][c][r];
-        }
-        float m = 0.f;
+      for (int r = 0; r < 4; ++r) {
+        z[r] = silu_f32(g0[r]) * u0[r];
+        z[4 + r] = silu_f32(g1[r]) * u1[r];
+      }
+      float m = 0.f;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) m = fmaxf(m, fabsf(z[r]));
-        // the 32 features of this token live in lanes l16, l16+16, l16+32, l16+48
-        m = fmaxf(m, __shfl_xor(m, 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
-        const uint32_t sc = mx_scale_code(m);
-        const float inv = mx_inv_scale(sc);
-        uint32_t w0 = 0, w1 = 0;
+      for (int r = 0; r < 8; ++r) m = fmaxf(m, fabsf(z[r]));
+      // the 32 features of a token live in lanes l16, l16+16, l16+32, l16+48
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      const uint32_t sc = mx_scale_code(m);
+      const float inv = mx_inv_scale(sc);
+      uint32_t w0 = 0, w1 = 0;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          w0 |= e4m3_encode(z[r] * inv) << (8 * r);
-          w1 |= e4m3_encode(z[4 + r] * inv) << (8 * r);
-        }
-        if (tv) {
-          uint8_t* o = static_cast<uint8_t*>(g.out) + pos * g.out_ld;
-          *reinterpret_cast<uint32_t*>(o + f0 + 4 * q) = w0;
-          *reinterpret_cast<uint32_t*>(o + f0 + 16 + 4 * q) = w1;
-          if (q == 0) g.out_scale[pos * (g.out_ld / 32) + f0 / 32] = (uint8_t)sc;
-        }
-      } else if (tv) {
-        const int64_t orow = rm.sorted_ids[pos];
+      for (int r = 0; r < 4; ++r) {
+        w0 |= e4m3_encode(z[r] * inv) << (8 * r);
+        w1 |= e4m3_encode(z[4 + r] * inv) << (8 * r);
+      }
+      const int tk = tg * kMxTok + 16 * c + l16;
+      if (tk < cnt) {
+        const int64_t pos = pos0 + tk;
+        uint8_t* o = static_cast<uint8_t*>(g.out) + pos * g.out_ld;
+        *reinterpret_cast<uint32_t*>(o + f0 + 4 * q) = w0;
+        *reinterpret_cast<uint32_t*>(o + f0 + 16 + 4 * q) = w1;
+        if (q == 0) g.out_scale[pos * (g.out_ld / 32) + f0 / 32] = (uint8_t)sc;
+      }
+    } else {
+      // wave c writes column tile c: 16 tokens x 64 features
+      const int c = wave;
+      const int tk = tg * kMxTok + 16 * c + l16;
+      if (tk < cnt) {
+        const int64_t orow = rm.sorted_ids[pos0 + tk];
         uint16_t* o = static_cast<uint16_t*>(g.out) + orow * g.out_ld;
 #pragma unroll
-        for (int t = 0; t < NTILE; ++t) {
+        for (int t = 0; t < 4; ++t) {
+          const f32x4 v = sOut[t][c][lane];
           uint32_t h[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(acc[t][c][r]);
-          *reinterpret_cast<uint2*>(o + f0 + 16 * t + 4 * q) =
-              make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+          for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(v[r]);
+          *reinterpret_cast<uint2*>(o + f0 + 16 * t + 4 * q) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
         }
       }
     }
+    __syncthreads();
   }
 }
 
@@ -339,11 +388,12 @@ hipError_t launch_gemm_stream_bf16(const GemmArgs& g, hipStream_t s) {
 }
 
 hipError_t launch_gemm_stream_mxfp8(const GemmArgs& g, hipStream_t s) {
-  dim3 grid(g.nfeat / 128, (unsigned)g.max_active);
   if (g.epi == kEpiGateUp)
-    hipLaunchKernelGGL(gemm_stream_mxfp8_kernel<kEpiGateUp>, grid, dim3(NT), 0, s, g);
+    hipLaunchKernelGGL(gemm_stream_mxfp8_kernel<kEpiGateUp>, dim3(g.nfeat / 32, (unsigned)g.max_active),
+                       dim3(256), 0, s, g);
   else
-    hipLaunchKernelGGL(gemm_stream_mxfp8_kernel<kEpiDown>, grid, dim3(NT), 0, s, g);
+    hipLaunchKernelGGL(gemm_stream_mxfp8_kernel<kEpiDown>, dim3(g.nfeat / 64, (unsigned)g.max_active),
+                       dim3(256), 0, s, g);
   return hipGetLastError();
 }
 

@@ -130,6 +130,8 @@ int moe_plan_init(moe_plan* plan, const moe_problem* prob) {
       return fail(plan, MOE_EUNSUPPORTED, "MXFP8 weights have only the streaming kernels");
     if (P.K % 128 || P.I % 128)
       return fail(plan, MOE_EUNSUPPORTED, "MXFP8 kernels need K % 128 == 0 and I % 128 == 0");
+    if (2 * P.I * P.K >= (1ll << 31))
+      return fail(plan, MOE_EUNSUPPORTED, "MXFP8 kernels address one expert with 32-bit offsets");
     variant = MOE_VARIANT_STREAM;
     snprintf(plan->reason, sizeof(plan->reason),
              "stream (MXFP8): weight rows streamed into scaled MFMA, 64 tokens per pass");
@@ -145,9 +147,17 @@ int moe_plan_init(moe_plan* plan, const moe_problem* prob) {
       snprintf(plan->reason, sizeof(plan->reason),
                "stream: M <= 16 rows per expert, weights streamed into the MFMA row operand");
     } else {
-      if (P.K % 128 || P.I % 64)
-        return fail(plan, MOE_EUNSUPPORTED, "tiled kernels need K % 128 == 0 and I % 64 == 0");
-      snprintf(plan->reason, sizeof(plan->reason), "tile: 128x128 LDS-staged MFMA tiles");
+      if (contiguous) {
+        if (P.K % 256 || P.I % 128)
+          return fail(plan, MOE_EUNSUPPORTED, "contiguous tiled kernels need K % 256 == 0 and I % 128 == 0");
+        snprintf(plan->reason, sizeof(plan->reason),
+                 "tile: 256 weight rows x 128 routes per workgroup, LDS-staged MFMA");
+      } else {
+        if (P.K % 128 || P.I % 64)
+          return fail(plan, MOE_EUNSUPPORTED, "batched tiled kernels need K % 128 == 0 and I % 64 == 0");
+        snprintf(plan->reason, sizeof(plan->reason),
+                 "tile: 128 weight rows x 128 rows per workgroup, route-tile-major order");
+      }
     }
   }
   plan->variant = variant;
@@ -261,6 +271,7 @@ static int gate_up_act(const moe_plan* plan, const void* a, const moe_weights* w
     g.act = xq;
     g.act_scale = xqs;
     g.act_ld = P.K;
+    g.act_bytes = plan->sorted_capacity * P.K;
     g.out_scale = at<uint8_t>(ws13, plan->off_z_scale);
     return launch_gemm_stream_mxfp8(g, s) == hipSuccess ? MOE_OK : MOE_EHIP;
   }
@@ -290,6 +301,7 @@ static int down_unpermute(const moe_plan* plan, const moe_weights* w, void* ws13
   hipError_t e;
   if (P.w_dtype == MOE_W_MXFP8) {
     g.act_scale = at<uint8_t>(ws13, plan->off_z_scale);
+    g.act_bytes = plan->sorted_capacity * P.I;
     e = launch_gemm_stream_mxfp8(g, s);
   } else {
     e = plan->variant == MOE_VARIANT_STREAM ? launch_gemm_stream_bf16(g, s)

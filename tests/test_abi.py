@@ -86,6 +86,8 @@ def test_plans_of_the_five_workloads(idx):
     (dict(layout=1, max_tokens=64, variant=moe.VARIANT_STREAM), moe.MOE_EUNSUPPORTED),
     (dict(layout=1, max_tokens=64, w_dtype=moe.W_MXFP8), moe.MOE_EUNSUPPORTED),
     (dict(w_dtype=moe.W_MXFP8, variant=moe.VARIANT_TILE), moe.MOE_EUNSUPPORTED),
+    (dict(K=128), moe.MOE_EUNSUPPORTED),                  # contiguous tiles need K % 256
+    (dict(K=128, I=96, layout=1, max_tokens=64), moe.MOE_EUNSUPPORTED),
     (dict(w1_order=moe.W1_INTERLEAVE16, I=72), moe.MOE_EINVAL),
 ])
 def test_plan_validation(kw, code):
@@ -95,6 +97,12 @@ def test_plan_validation(kw, code):
         moe.moe_plan_init(moe.make_problem(**base))
     assert ei.value.status == code
     assert str(ei.value)
+
+
+def test_batched_tile_shapes():
+    """The batched tiles (128 weight rows) need only K % 128 and I % 64."""
+    p = moe.moe_plan_init(moe.make_problem(64, 128, 64, 8, max_tokens=64, layout=moe.LAYOUT_BATCHED))
+    assert p.variant == moe.VARIANT_TILE
 
 
 def test_variant_choice_and_override():

@@ -40,10 +40,12 @@ SCALED = [
     ("decode_m4", mi.config(1).scaled(K=512, I=1024), moe.VARIANT_AUTO),
     ("decode_m13", mi.config(1).scaled(M=13, K=512, I=1024), moe.VARIANT_AUTO),
     ("decode_m4_tile", mi.config(1).scaled(K=512, I=1024), moe.VARIANT_TILE),
-    ("prefill_m1000", mi.config(2).scaled(M=1000, K=256, I=192, E=16), moe.VARIANT_AUTO),
+    ("prefill_m1000", mi.config(2).scaled(M=1000, K=256, I=256, E=16), moe.VARIANT_AUTO),
+    ("prefill_m700_k512", mi.config(2).scaled(M=700, K=512, I=384, E=24), moe.VARIANT_AUTO),
     ("prefill_m100_stream", mi.config(2).scaled(M=100, K=256, I=256, E=16), moe.VARIANT_STREAM),
     ("mxfp8_m512", mi.config(3).scaled(M=512, K=512, I=256), moe.VARIANT_AUTO),
     ("mxfp8_m4160", mi.config(3).scaled(M=4160, K=512, I=256), moe.VARIANT_AUTO),
+    ("mxfp8_m12000", mi.config(3).scaled(M=12000, K=256, I=128), moe.VARIANT_AUTO),
 ]
 
 
@@ -86,7 +88,7 @@ def test_tiny_intermediate_z():
 
 
 def test_nullity_and_equivariance():
-    cfg = mi.config(2).scaled(M=300, K=256, I=192, E=16)
+    cfg = mi.config(2).scaled(M=300, K=256, I=256, E=16)
     c = make_case(cfg)
     base, *_ = run_contiguous(c)
     ids, w = c.inp.topk_ids.copy(), c.inp.topk_weights.copy()
@@ -164,9 +166,12 @@ def test_full_mxfp8_share():
     out, plan, ws13, _ = run_contiguous(c)
     ids = c.inp.topk_ids
     nloc = (ids >= 0).sum(axis=1)
-    # tokens whose local routes touch only experts 0 and 1, plus tokens with none
+    # tokens whose local routes touch only experts 0 and 1, spread over the
+    # token range so that they sit early and late in their experts' runs,
+    # plus tokens with none
     on01 = np.flatnonzero((nloc > 0) & np.all((ids < 0) | (ids <= 1), axis=1))
-    tokens = np.sort(np.concatenate([on01[:10], np.flatnonzero(nloc == 0)[:6]]))
+    pick = on01[np.unique(np.linspace(0, on01.size - 1, 12).astype(int))]
+    tokens = np.sort(np.concatenate([pick, np.flatnonzero(nloc == 0)[:6]]))
     ref = oracle_contiguous(c, tokens)
     check_close(out[torch.from_numpy(tokens).cuda()], ref, MX_REL, 0.0, cfg.name)
     none = torch.from_numpy(np.flatnonzero(nloc == 0)).cuda()
