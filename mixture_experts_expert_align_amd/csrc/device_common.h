@@ -25,6 +25,21 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// Raw buffer resource over [p, p + bytes) (32-bit data format, no stride),
+// range check clamped to 2^31 - 1 bytes.  The size is clamped with integer
+// arithmetic: a floating-point min would put the descriptor in vector
+// registers, and every load through it would become a per-lane loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, int64_t bytes) {
+  const int n = bytes < (int64_t)0x7fffffff ? (int)bytes : 0x7fffffff;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, n, 0x00020000);
+}
+
+// Workgroup barrier that waits only for the calling wave's LDS operations:
+// its outstanding global loads stay in flight across it (__syncthreads also
+// waits for those).  The memory clobber keeps the compiler from moving LDS
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 __device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + expf(-v)); }

@@ -28,7 +28,6 @@ namespace moe {
 namespace {
 
 constexpr int NT = 256;
-constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data format (CDNA3/4 word 3)
 
 __device__ __forceinline__ i32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const i32x4*>(p); }
 
@@ -75,11 +74,8 @@ __global__ void __launch_bounds__(64 * KS) gemm_stream_bf16_kernel(GemmArgs g) {
   // offset.  A lane without a token gets an offset past the buffer's size,
   // which the hardware's range check turns into zeros.
   const uint16_t* wexp = static_cast<const uint16_t*>(g.w) + (int64_t)e * g.w_expert_stride;
-  const __amdgpu_buffer_rsrc_t wr =
-      __builtin_amdgcn_make_buffer_rsrc((void*)wexp, 0, (int)min<int64_t>(g.w_expert_stride * 2, 0x7fffffff),
-                                        kBufferFlags);
-  const __amdgpu_buffer_rsrc_t ar =
-      __builtin_amdgcn_make_buffer_rsrc((void*)g.act, 0, (int)min<int64_t>(g.act_bytes, 0x7fffffff), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(wexp, g.w_expert_stride * 2);
+  const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(g.act, g.act_bytes);
   uint32_t wo[NTL];
   if (EPI == kEpiGateUp) {
     wo[0] = (uint32_t)(w1_row(f0 + l16, false, g.I, g.w1_order) * K + kbase) * 2u;
@@ -174,25 +170,41 @@ __global__ void __launch_bounds__(64 * KS) gemm_stream_bf16_kernel(GemmArgs g) {
 //
 // A workgroup owns four 16-row weight tiles of one expert, one per wave; each
 // wave streams its tile over the whole contraction straight from HBM into
-// registers (three steps ahead).  The 64 routed token rows of a pass (four
-// 16-token column tiles) are staged in LDS two 128-wide steps at a time and
-// shared by the four waves, so activations cross L2 once per workgroup.
+// registers, one stage (four 128-wide steps) ahead.  The 64 routed token rows
+// of a pass (four 16-token column tiles) are staged in LDS a stage at a time
+// (double buffered) and shared by the four waves, so activations cross L2
+// once per workgroup.  The barriers between stages wait only for LDS
+// operations, so the weight loads stay in flight across them.
 //   kGateUp: tiles (gate f0..+15, up f0..+15, gate f0+16..+31, up f0+16..+31),
 //            32 features = one MX block of z per token: the epilogue gathers
 //            the four tiles in LDS and quantises silu(gate)*up (E4M3 codes +
 //            UE8M0 scale).
 //   kDown:   tiles f0 + 16t, 64 features; bf16 y rows per (token, slot).
 constexpr int kMxTok = 64;                 // tokens per pass
-constexpr int kMxSteps = 2;                // 128-wide steps per LDS stage
-constexpr int kMxRow = 128 * kMxSteps;     // bytes of one token row per stage
 
-// LDS byte offset of 16-byte chunk c (0..kMxRow/16-1) of token row r: the
-// chunk index is XOR-ed with bits of r so that the 16 rows a load
-// instruction's lane group reads at one chunk fall in distinct banks.
-__device__ __forceinline__ int mx_lds(int r, int c) { return r * kMxRow + ((c ^ ((r >> 1) & 7)) << 4); }
+// LDS byte offset of 16-byte chunk c of staged token row r (rows of ROW
+// bytes, ROW a multiple of 128): the chunk index is XOR-ed with a function of
+// the row that stays inside the row, chosen so the 16 rows one lane group
+// reads at a chunk cover all 16 chunk slots of a 256-byte bank window (rows
+// of 128 bytes: two rows per window, 8 XOR values; wider rows: r % 16).
+template <int ROW>
+__device__ __forceinline__ int mx_lds(int r, int c) {
+  constexpr int RPW = ROW >= 256 ? 1 : 256 / ROW;            // rows per 256-byte window
+  constexpr int XM = (ROW / 16 < 16 ? ROW / 16 : 16) - 1;   // XOR range inside a row
+  return r * ROW + ((c ^ ((r / RPW) & XM)) << 4);
+}
 
-template <int EPI>
-__global__ void __launch_bounds__(256) gemm_stream_mxfp8_kernel(GemmArgs g) {
+// STEPS: 128-wide steps per stage (2, or 1 for an odd step count), dividing
+// the contraction's step count, so every stage is full and the loop has no
+// per-step tests.  (Four steps per stage need more than the 256 registers
+// that keep two workgroups on a CU.)
+template <int EPI, int STEPS>
+__global__ void __launch_bounds__(256, 2) gemm_stream_mxfp8_kernel(GemmArgs g) {
+  constexpr int kRow = 128 * STEPS;          // bytes of one token row per stage
+  constexpr int kChunks = kRow / 16;         // 16-byte chunks per staged row
+  constexpr int kStage = kMxTok * kRow;      // bytes of one staged stage
+  constexpr int kRowsPerPass = 256 / kChunks;
+  constexpr int kLoads = kMxTok / kRowsPerPass;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;          // = weight tile
   const int tid = threadIdx.x;
@@ -210,110 +222,132 @@ __global__ void __launch_bounds__(256) gemm_stream_mxfp8_kernel(GemmArgs g) {
 
   const uint8_t* wexp = static_cast<const uint8_t*>(g.w) + (int64_t)e * g.w_expert_stride;
   const uint8_t* wsexp = g.w_scale + (int64_t)e * (g.w_expert_stride / 32);
-  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)wexp, 0, (int)min<int64_t>(g.w_expert_stride, 0x7fffffff), kBufferFlags);
-  const __amdgpu_buffer_rsrc_t wsr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)wsexp, 0, (int)min<int64_t>(g.w_expert_stride / 32, 0x7fffffff), kBufferFlags);
-  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)g.act, 0, (int)min<int64_t>(g.act_bytes, 0x7fffffff), kBufferFlags);
-  const __amdgpu_buffer_rsrc_t asr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)g.act_scale, 0, (int)min<int64_t>(g.act_bytes / 32, 0x7fffffff), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(wexp, g.w_expert_stride);
+  const __amdgpu_buffer_rsrc_t wsr = buffer_rsrc(wsexp, g.w_expert_stride / 32);
+  const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(g.act, g.act_bytes);
+  const __amdgpu_buffer_rsrc_t asr = buffer_rsrc(g.act_scale, g.act_bytes / 32);
   int row;
   if (EPI == kEpiGateUp) row = w1_row(f0 + 16 * (wave >> 1) + l16, (wave & 1) != 0, g.I, g.w1_order);
   else row = f0 + 16 * wave + l16;
   const uint32_t wo = (uint32_t)(row * K + 16 * q);
   const uint32_t wso = (uint32_t)(row * KB + q);
 
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][kMxTok * kMxRow];
-  __shared__ uint32_t sBs[2][kMxTok * kMxSteps];          // 4 scale bytes per token per step
-  __shared__ f32x4 sOut[4][4][64];                        // epilogue: [tile][column tile][lane]
-  const int nsteps = K / 128;
-  const int nstages = (nsteps + kMxSteps - 1) / kMxSteps;   // the last stage may be half used
+  // staged activations (two stages) and their scales; the epilogue reuses
+  // the first stage buffer for the four waves' accumulators
+  __shared__ __attribute__((aligned(16))) uint8_t sB[2][kStage];
+  __shared__ uint32_t sBs[2][kMxTok * STEPS];             // 4 scale bytes per token per step
+  f32x4* sOut = reinterpret_cast<f32x4*>(&sB[0][0]);      // [tile][column tile][lane]
+  static_assert(16 * 64 * sizeof(f32x4) <= 2 * kStage, "epilogue buffer");
+  const int nstages = K / kRow;
 
-  // token-tile staging: a stage is 64 rows x 16 chunks of 16 bytes; thread
-  // tid moves chunk tid % 16 of rows tid / 16 + 16 i (i < 4) and, for
-  // tid < 128, one scale word (token tid / 2, step tid % 2)
-  const int srow = tid >> 4, schk = tid & 15;
+  // staging: thread tid moves chunk tid % kChunks of rows tid / kChunks +
+  // kRowsPerPass * i (i < kLoads) and, for tid < 64 * STEPS, one scale word
+  // (token tid / STEPS, step tid % STEPS)
+  const int srow = tid / kChunks, schk = tid % kChunks;
   for (int tg = 0; tg * kMxTok < cnt; ++tg) {
-    uint32_t xo[4], xso = 0x80000000u;
+    uint32_t xo[kLoads], xso = 0x80000000u;    // past the end: loads return 0
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = tg * kMxTok + srow + 16 * i;
-      // chunk j of a stage row holds bytes 16j .. 16j+15 of the stage's 256-byte span
+    for (int i = 0; i < kLoads; ++i) {
+      const int t = tg * kMxTok + srow + kRowsPerPass * i;
       xo[i] = t < cnt ? (uint32_t)((int64_t)(pos0 + t) * g.act_ld + 16 * schk) : 0x80000000u;
     }
-    if (tid < kMxTok * kMxSteps) {
-      const int tt = tg * kMxTok + tid / kMxSteps;
-      if (tt < cnt) xso = (uint32_t)((int64_t)(pos0 + tt) * (g.act_ld / 32) + 4 * (tid % kMxSteps));
+    if (tid < kMxTok * STEPS) {
+      const int tt = tg * kMxTok + tid / STEPS;
+      if (tt < cnt) xso = (uint32_t)((int64_t)(pos0 + tt) * (g.act_ld / 32) + 4 * (tid % STEPS));
     }
-    i32x4 pb[4];
+    i32x4 pb[kLoads];
     uint32_t pbs = 0;
+    // stage numbers are uniform; readfirstlane tells the compiler so, and
+    // keeps the scalar offsets of the loads in scalar registers
     auto bload = [&](int stage) {
-      const int kb = stage * kMxRow;
+      const int kb = __builtin_amdgcn_readfirstlane(stage * kRow);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pb[i] = __builtin_amdgcn_raw_buffer_load_b128(ar, xo[i], kb, 0);
-      if (tid < kMxTok * kMxSteps) pbs = __builtin_amdgcn_raw_buffer_load_b32(asr, xso, kb / 32, 0);
+      for (int i = 0; i < kLoads; ++i) pb[i] = __builtin_amdgcn_raw_buffer_load_b128(ar, xo[i], kb, 0);
+      if (tid < kMxTok * STEPS) pbs = __builtin_amdgcn_raw_buffer_load_b32(asr, xso, kb >> 5, 0);
     };
     auto bstore = [&](int buf) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<i32x4*>(&sB[buf][mx_lds(srow + 16 * i, schk)]) = pb[i];
-      if (tid < kMxTok * kMxSteps) sBs[buf][tid] = pbs;
+      for (int i = 0; i < kLoads; ++i)
+        *reinterpret_cast<i32x4*>(&sB[buf][mx_lds<kRow>(srow + kRowsPerPass * i, schk)]) = pb[i];
+      if (tid < kMxTok * STEPS) sBs[buf][tid] = pbs;
     };
 
     f32x4 acc[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    // weight fragments: three steps in flight
-    i32x8 wa[3];
-    int wsc[3];
-    auto aload = [&](int i, int step) {
-      const int k = 128 * step;
-      const i32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(wr, wo, k, 0);
-      const i32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(wr, wo + 64, k, 0);
-      wa[i] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      wsc[i] = __builtin_amdgcn_raw_buffer_load_b8(wsr, wso, k / 32, 0);
-    };
-    auto mma = [&](int i, int buf, int sub) {
+    // weight fragments of two stages
+    i32x8 wa[2][STEPS];
+    int wsc[2][STEPS];
+    auto aload = [&](int p, int stage) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int tr = 16 * c + l16;
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(&sB[buf][mx_lds(tr, 8 * sub + q)]);
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(&sB[buf][mx_lds(tr, 8 * sub + 4 + q)]);
-        const i32x8 xb = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const int xs = (sBs[buf][tr * kMxSteps + sub] >> (8 * q)) & 0xff;
-        acc[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa[i], xb, acc[c], 0, 0, 0, wsc[i], 0, xs);
+      for (int sub = 0; sub < STEPS; ++sub) {
+        const int k = __builtin_amdgcn_readfirstlane(128 * (stage * STEPS + sub));
+        const i32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(wr, wo, k, 0);
+        const i32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(wr, wo + 64, k, 0);
+        wa[p][sub] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        wsc[p][sub] = (int)(uint32_t)__builtin_amdgcn_raw_buffer_load_b8(wsr, wso, k >> 5, 0);
       }
     };
-
-    bload(0);
-    aload(0, 0);
-    if (nsteps > 1) aload(1, 1);
-    bstore(0);
-    __syncthreads();
-    for (int stg = 0; stg < nstages; ++stg) {
-      const int buf = stg & 1;
-      if (stg + 1 < nstages) bload(stg + 1);
+    auto mma = [&](int p) {
 #pragma unroll
-      for (int sub = 0; sub < kMxSteps; ++sub) {
-        const int step = stg * kMxSteps + sub;
-        if (step < nsteps) {
-          if (step + 2 < nsteps) aload((step + 2) % 3, step + 2);
-          mma(step % 3, buf, sub);
+      for (int sub = 0; sub < STEPS; ++sub) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int tr = 16 * c + l16;
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(&sB[p][mx_lds<kRow>(tr, 8 * sub + q)]);
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(&sB[p][mx_lds<kRow>(tr, 8 * sub + 4 + q)]);
+          const i32x8 xb = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const int xs = (sBs[p][tr * STEPS + sub] >> (8 * q)) & 0xff;
+          acc[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa[p][sub], xb, acc[c], 0, 0, 0,
+                                                                   wsc[p][sub], 0, xs);
         }
       }
-      if (stg + 1 < nstages) bstore(buf ^ 1);
-      __syncthreads();
+    };
+    // One stage with stage parity p (a literal at each call).  On entry the
+    // activations of stage stg+1 are in registers (fetched a stage earlier)
+    // and the weights of stage stg are on their way.  The stage stores the
+    // activations of stg+1 to LDS, fetches the activations of stg+2 and the
+    // weights of stg+1, then multiplies stage stg.  The scheduling barriers
+    // keep this order, so each load has a whole stage to arrive.  The fetch
+    // of stage stg+2 may run past the contraction (the last two stages): it
+    // reads bytes of the next row or, past the buffer, zeros, and is never
+    // stored.
+    auto body = [&](int p, int stg) {
+      bstore(p ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+      bload(stg + 2);
+      aload(p ^ 1, stg + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(p);
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+    };
+
+    // prologue, issuing in the loop's order (activations before weights) so
+    // the waits in the loop stay partial
+    bload(0);
+    bstore(0);
+    bload(1);
+    aload(0, 0);
+    lds_barrier();
+    int stg = 0;
+    while (true) {
+      if (stg + 1 >= nstages) { mma(0); break; }
+      body(0, stg++);
+      if (stg + 1 >= nstages) { mma(1); break; }
+      body(1, stg++);
     }
+    lds_barrier();
 
     // acc[c][r]: weight row 4*q + r of this wave's tile, token tg*64 + 16*c + l16
 #pragma unroll
-    for (int c = 0; c < 4; ++c) sOut[wave][c][lane] = acc[c];
-    __syncthreads();
+    for (int c = 0; c < 4; ++c) sOut[(wave * 4 + c) * 64 + lane] = acc[c];
+    lds_barrier();
     if (EPI == kEpiGateUp) {
       // wave c finishes column tile c: 16 tokens x 32 features
       const int c = wave;
-      const f32x4 g0 = sOut[0][c][lane], u0 = sOut[1][c][lane];
-      const f32x4 g1 = sOut[2][c][lane], u1 = sOut[3][c][lane];
+      const f32x4 g0 = sOut[(0 * 4 + c) * 64 + lane], u0 = sOut[(1 * 4 + c) * 64 + lane];
+      const f32x4 g1 = sOut[(2 * 4 + c) * 64 + lane], u1 = sOut[(3 * 4 + c) * 64 + lane];
       float z[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -351,7 +385,7 @@ __global__ void __launch_bounds__(256) gemm_stream_mxfp8_kernel(GemmArgs g) {
         uint16_t* o = static_cast<uint16_t*>(g.out) + orow * g.out_ld;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const f32x4 v = sOut[t][c][lane];
+          const f32x4 v = sOut[(t * 4 + c) * 64 + lane];
           uint32_t h[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(v[r]);
@@ -359,7 +393,7 @@ __global__ void __launch_bounds__(256) gemm_stream_mxfp8_kernel(GemmArgs g) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -387,14 +421,19 @@ hipError_t launch_gemm_stream_bf16(const GemmArgs& g, hipStream_t s) {
                              : launch_stream_bf16<kEpiDown>(g, s, 8);
 }
 
-hipError_t launch_gemm_stream_mxfp8(const GemmArgs& g, hipStream_t s) {
-  if (g.epi == kEpiGateUp)
-    hipLaunchKernelGGL(gemm_stream_mxfp8_kernel<kEpiGateUp>, dim3(g.nfeat / 32, (unsigned)g.max_active),
-                       dim3(256), 0, s, g);
+template <int EPI>
+static hipError_t launch_mxfp8(const GemmArgs& g, hipStream_t s) {
+  const dim3 grid(g.nfeat / (EPI == kEpiGateUp ? 32 : 64), (unsigned)g.max_active);
+  const int nsteps = g.kdim / 128;
+  if (nsteps % 2 == 0)
+    hipLaunchKernelGGL((gemm_stream_mxfp8_kernel<EPI, 2>), grid, dim3(256), 0, s, g);
   else
-    hipLaunchKernelGGL(gemm_stream_mxfp8_kernel<kEpiDown>, dim3(g.nfeat / 64, (unsigned)g.max_active),
-                       dim3(256), 0, s, g);
+    hipLaunchKernelGGL((gemm_stream_mxfp8_kernel<EPI, 1>), grid, dim3(256), 0, s, g);
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_stream_mxfp8(const GemmArgs& g, hipStream_t s) {
+  return g.epi == kEpiGateUp ? launch_mxfp8<kEpiGateUp>(g, s) : launch_mxfp8<kEpiDown>(g, s);
 }
 
 }  // namespace moe
