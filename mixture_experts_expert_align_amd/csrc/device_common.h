@@ -36,9 +36,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, int
 
 // Workgroup barrier that waits only for the calling wave's LDS operations:
 // its outstanding global loads stay in flight across it (__syncthreads also
-// waits for those).  The memory clobber keeps the compiler from moving LDS
-// accesses across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// waits for those).  The wait is the builtin (lgkmcnt 0; vmcnt 63 and expcnt
+// 7 leave those counters alone), so the compiler's own wait insertion knows
+// about it; the empty asm statements with memory clobbers keep the compiler
+// from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 

@@ -131,14 +131,18 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmA
   const int wm = wave % WM;
   const int K = g.kdim;
 
-  // ---- global -> register staging: 16-byte chunk c = tid + NT*i -> row c/CH, chunk c%CH
+  // ---- global -> register staging: 16-byte chunk c = tid + NT*i -> row c/CH, chunk c%CH.
+  // Buffer loads with per-lane byte offsets and the slice's byte offset in
+  // the scalar operand; a padding route gets an offset past the buffer, which
+  // the range check turns into zeros.
   constexpr int WCH = BN * CH / NT;   // weight chunks per thread
   constexpr int XCH = BM * CH / NT;   // route chunks per thread
   static_assert(WCH * NT == BN * CH && XCH * NT == BM * CH, "tile / thread mismatch");
   const int kc = tid % CH;
-  const uint16_t* pw[WCH];
-  const uint16_t* px[XCH];
   const uint16_t* wexp = static_cast<const uint16_t*>(g.w) + (int64_t)tc.expert * g.w_expert_stride;
+  const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(wexp, g.w_expert_stride * 2);
+  const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(g.act, g.act_bytes);
+  uint32_t ow[WCH], ox[XCH];
 #pragma unroll
   for (int i = 0; i < WCH; ++i) {
     const int n = (tid + NT * i) / CH;
@@ -150,41 +154,44 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmA
     } else {
       wrow = tc.col0 + n;
     }
-    pw[i] = wexp + (int64_t)wrow * K + kc * 8;
+    ow[i] = (uint32_t)((wrow * K + kc * 8) * 2);
   }
-  const uint16_t* act = static_cast<const uint16_t*>(g.act);
 #pragma unroll
   for (int i = 0; i < XCH; ++i) {
     const int m = (tid + NT * i) / CH;
-    const uint16_t* p = nullptr;
+    int64_t row = -1;
     if (rm.layout == 0) {
       if (EPI == kEpiGateUp) {
         const int sid = rm.sorted_ids[tc.row0 + m];
-        if (sid != rm.sentinel) p = act + (int64_t)(sid / rm.topk) * g.act_ld;
+        if (sid != rm.sentinel) row = sid / rm.topk;
       } else {
-        p = act + (tc.row0 + m) * g.act_ld;
+        row = tc.row0 + m;
       }
     } else if (m < tc.nvalid) {
-      p = act + (tc.row0 + m) * g.act_ld;
+      row = tc.row0 + m;
     }
-    px[i] = p ? p + kc * 8 : nullptr;
+    ox[i] = row >= 0 ? (uint32_t)((row * g.act_ld + kc * 8) * 2) : 0x80000000u;
   }
 
-  i32x4 rw[WCH], rx[XCH];
-  const i32x4 zero = {0, 0, 0, 0};
-  auto gload = [&](int k0) {
+  // Two register sets: slice t lives in set t % 2 from its load to its LDS
+  // store two slices later, so each load has two slices of MFMA work to
+  // arrive.
+  i32x4 rw[2][WCH], rx[2][XCH];
+  const int nk = K / BK;
+  auto gload = [&](int set, int kt) {
+    const int kb = min(kt, nk - 1) * BK * 2;   // past the end: repeat the last slice (unused)
 #pragma unroll
-    for (int i = 0; i < WCH; ++i) rw[i] = *reinterpret_cast<const i32x4*>(pw[i] + k0);
+    for (int i = 0; i < WCH; ++i) rw[set][i] = __builtin_amdgcn_raw_buffer_load_b128(wr, ow[i], kb, 0);
 #pragma unroll
-    for (int i = 0; i < XCH; ++i) rx[i] = px[i] ? *reinterpret_cast<const i32x4*>(px[i] + k0) : zero;
+    for (int i = 0; i < XCH; ++i) rx[set][i] = __builtin_amdgcn_raw_buffer_load_b128(ar, ox[i], kb, 0);
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf, int set) {
 #pragma unroll
     for (int i = 0; i < WCH; ++i)
-      *reinterpret_cast<i32x4*>(&sW[buf][lds_off<BK>((tid + NT * i) / CH, kc)]) = rw[i];
+      *reinterpret_cast<i32x4*>(&sW[buf][lds_off<BK>((tid + NT * i) / CH, kc)]) = rw[set][i];
 #pragma unroll
     for (int i = 0; i < XCH; ++i)
-      *reinterpret_cast<i32x4*>(&sX[buf][lds_off<BK>((tid + NT * i) / CH, kc)]) = rx[i];
+      *reinterpret_cast<i32x4*>(&sX[buf][lds_off<BK>((tid + NT * i) / CH, kc)]) = rx[set][i];
   };
 
   // ---- this wave's MFMA tiles.  kGateUp: weight tiles [0, TW/2) are gate
@@ -219,14 +226,7 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmA
     for (int j = 0; j < TX; ++j)
       fx[fb][j] = as_bf16x8(*reinterpret_cast<const i32x4*>(&sX[buf][lds_off<BK>(xrow_l + 32 * j, c)]));
   };
-
-  const int nk = K / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+  auto compute = [&](int buf) {
     fload(0, buf, 0);
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
@@ -237,9 +237,31 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmA
         for (int j = 0; j < TX; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[s & 1][i], fx[s & 1][j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
+  };
+  // slice kt (LDS buffer and register set kt % 2, literals at each call):
+  // multiply it, store slice kt+1 (register set (kt+1) % 2) to the other
+  // buffer, refill that set with slice kt+3
+  auto step = [&](int p, int kt) {
+    compute(p);
+    __builtin_amdgcn_sched_barrier(0);
+    sstore(p ^ 1, p ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    gload(p ^ 1, kt + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+  };
+
+  gload(0, 0);
+  gload(1, 1);
+  sstore(0, 0);
+  gload(0, 2);
+  lds_barrier();
+  int kt = 0;
+  for (; kt + 2 <= nk; kt += 2) {
+    step(0, kt);
+    step(1, kt + 1);
   }
+  if (kt < nk) compute(0);
 
   // ---- epilogue.  acc[i][j][r]: weight row (tile i) 8*(r/4) + 4*(lane/32) + r%4,
   // route wm*(BM/WM) + 32*j + lane%32.  Registers 4h..4h+3 are 4 consecutive rows.

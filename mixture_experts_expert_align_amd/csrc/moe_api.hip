@@ -147,6 +147,11 @@ int moe_plan_init(moe_plan* plan, const moe_problem* prob) {
       snprintf(plan->reason, sizeof(plan->reason),
                "stream: M <= 16 rows per expert, weights streamed into the MFMA row operand");
     } else {
+      // 32-bit buffer offsets: one expert's W1, the activation rows and z
+      const int64_t act_rows = contiguous ? P.M : P.E * P.max_tokens;
+      if (4 * P.I * P.K >= (1ll << 31) || 2 * act_rows * P.K >= (1ll << 31) ||
+          2 * (contiguous ? R + P.E * 128 : act_rows) * P.I >= (1ll << 31))
+        return fail(plan, MOE_EUNSUPPORTED, "tiled kernels address one expert and the activations with 32-bit offsets");
       if (contiguous) {
         if (P.K % 256 || P.I % 128)
           return fail(plan, MOE_EUNSUPPORTED, "contiguous tiled kernels need K % 256 == 0 and I % 128 == 0");
@@ -357,6 +362,7 @@ int moe_apply_batched(const moe_plan* plan, const void* a, const int32_t* expert
   g1.epi = kEpiGateUp;
   g1.act = a;
   g1.act_ld = P.K;
+  g1.act_bytes = P.E * P.max_tokens * P.K * 2;
   g1.w = w->w1;
   g1.w_expert_stride = 2 * P.I * P.K;
   g1.kdim = (int32_t)P.K;
@@ -367,6 +373,7 @@ int moe_apply_batched(const moe_plan* plan, const void* a, const int32_t* expert
   g2.epi = kEpiDown;
   g2.act = at<void>(ws13, plan->off_z);
   g2.act_ld = P.I;
+  g2.act_bytes = P.E * P.max_tokens * P.I * 2;
   g2.w = w->w2;
   g2.w_expert_stride = P.K * P.I;
   g2.kdim = (int32_t)P.I;
