@@ -11,7 +11,10 @@
 // Integer-only, so the result is the same on every run.
 //
 // Small problems (R <= kAlignSmallMaxR) run as one workgroup in one launch
-// (decode batches are launch-latency bound); larger ones as three launches.
+// (decode batches are launch-latency bound); larger ones as three launches:
+// per-chunk histograms (stored bucket-major), a scan of each bucket over
+// the chunks plus the bucket layout, and the scatter, whose workgroups also
+// write the padding sentinels and the tile owners.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -78,9 +81,9 @@ __device__ __forceinline__ int find_bucket(const int* s_off, int nb, int pos) {
   return lo;
 }
 
-// From per-bucket counts in s_cnt: offsets, counts, active list, tile owners
-// and padding sentinels.  Run by one workgroup.  s_off needs nb+1 ints.
-__device__ void finish_layout(const AlignArgs& a, int* s_cnt, int* s_off, int* s_tmp) {
+// From per-bucket counts in s_cnt: offsets, counts and the active list.
+// Run by one workgroup.  s_off needs nb+1 ints.
+__device__ void bucket_layout(const AlignArgs& a, int* s_cnt, int* s_off, int* s_tmp) {
   const int nb = a.nb;
   const int nt = blockDim.x;
   const int per = (nb + nt - 1) / nt;
@@ -111,18 +114,23 @@ __device__ void finish_layout(const AlignArgs& a, int* s_cnt, int* s_off, int* s
   }
   for (int64_t i = n_active + threadIdx.x; i < a.max_active; i += nt) a.active[i] = -1;
   __syncthreads();
-  for (int64_t b = threadIdx.x; b < a.max_tiles; b += nt) {
-    const int64_t pos = b * a.B;
-    a.block_bucket[b] = pos >= total ? -1 : find_bucket(s_off, nb, (int)pos);
+}
+
+// Padding sentinels and tile owners, from offsets and counts in global
+// memory: bucket e's padding [offsets[e] + counts[e], offsets[e+1]) and
+// tiles [offsets[e] / B, offsets[e+1] / B); past the total, sentinels and
+// owner -1.  Work item w of nw: buckets w, w + nw, ... one wave each, and a
+// grid-stride share of the tail.
+__device__ void pad_and_owners(const AlignArgs& a, int64_t w, int64_t nw, int64_t gtid, int64_t gsize) {
+  const int lane = __lane_id();
+  for (int64_t e = w; e < a.nb; e += nw) {
+    const int off = a.offsets[e], c = a.counts[e], end = a.offsets[e + 1];
+    for (int64_t p = off + c + lane; p < end; p += kWave) a.sorted[p] = a.sentinel;
+    for (int64_t t = off / a.B + lane; t < end / a.B; t += kWave) a.block_bucket[t] = (int32_t)e;
   }
-  for (int64_t p = threadIdx.x; p < a.capacity; p += nt) {
-    bool pad = p >= total;
-    if (!pad) {
-      const int e = find_bucket(s_off, nb, (int)p);
-      pad = p >= s_off[e] + s_cnt[e];
-    }
-    if (pad) a.sorted[p] = a.sentinel;
-  }
+  const int64_t total = a.offsets[a.nb];
+  for (int64_t p = total + gtid; p < a.capacity; p += gsize) a.sorted[p] = a.sentinel;
+  for (int64_t t = total / a.B + gtid; t < a.max_tiles; t += gsize) a.block_bucket[t] = -1;
 }
 
 // Place routes [begin, end) in index order; s_cur[e] is the next free
@@ -137,7 +145,7 @@ __device__ void scatter_range(const AlignArgs& a, int64_t begin, int64_t end, in
     if (i < end) kr = read_key(a, i);
     int rank, gsize;
     bool last;
-    wave_match_rank(kr.key, kr.valid, rank, gsize, last);
+    wave_match_rank(kr.key, kr.valid, a.nbits, rank, gsize, last);
     for (int w = 0; w < nwaves; ++w) {
       if (w == wave && kr.valid) {
         const int b0 = s_cur[kr.key];
@@ -166,20 +174,21 @@ __global__ void __launch_bounds__(1024) align_small_kernel(AlignArgs a) {
   if (inv) atomicAdd(&s_invalid, inv);
   __syncthreads();
   if (threadIdx.x == 0) a.status[0] = s_invalid;
-  finish_layout(a, s_cnt, s_off, s_tmp);
-  __syncthreads();
+  bucket_layout(a, s_cnt, s_off, s_tmp);   // ends with a barrier: its global writes are visible
+  pad_and_owners(a, threadIdx.x / kWave, blockDim.x / kWave, threadIdx.x, blockDim.x);
   for (int e = threadIdx.x; e < a.nb; e += blockDim.x) s_cnt[e] = s_off[e];
   __syncthreads();
   scatter_range(a, 0, a.R, s_cnt);
 }
 
-// Multi-block path, launch 1: per-chunk histograms (column nb: invalid ids).
+// Multi-block path, launch 1: per-chunk histograms, bucket-major:
+// block_hist[e * nblocks + b] (row nb: invalid ids).
 __global__ void __launch_bounds__(256) align_hist_kernel(AlignArgs a) {
   __shared__ int s_cnt[kAlignMaxBuckets + 1];
   for (int e = threadIdx.x; e <= a.nb; e += blockDim.x) s_cnt[e] = 0;
   __syncthreads();
-  const int64_t begin = (int64_t)blockIdx.x * kAlignChunk;
-  const int64_t end = min(a.R, begin + kAlignChunk);
+  const int64_t begin = (int64_t)blockIdx.x * a.chunk;
+  const int64_t end = min(a.R, begin + a.chunk);
   int inv = 0;
   for (int64_t i = begin + threadIdx.x; i < end; i += blockDim.x) {
     const KeyRead kr = read_key(a, i);
@@ -188,50 +197,68 @@ __global__ void __launch_bounds__(256) align_hist_kernel(AlignArgs a) {
   }
   if (inv) atomicAdd(&s_cnt[a.nb], inv);
   __syncthreads();
-  int32_t* h = a.block_hist + (int64_t)blockIdx.x * (a.nb + 1);
-  for (int e = threadIdx.x; e <= a.nb; e += blockDim.x) h[e] = s_cnt[e];
+  for (int e = threadIdx.x; e <= a.nb; e += blockDim.x) a.block_hist[(int64_t)e * a.nblocks + blockIdx.x] = s_cnt[e];
 }
 
-// Launch 2: scan the chunk histograms per bucket (in place: each chunk's
-// starting rank), then the layout.
+// Launch 2: each bucket's histogram row scanned over the chunks (in place:
+// each chunk's starting rank), a wave per bucket, then the bucket layout.
 __global__ void __launch_bounds__(1024) align_scan_kernel(AlignArgs a) {
   __shared__ int s_cnt[kAlignMaxBuckets + 1];
   __shared__ int s_off[kAlignMaxBuckets + 1];
   __shared__ int s_tmp[17];
-  const int stride = a.nb + 1;
-  for (int e = threadIdx.x; e <= a.nb; e += blockDim.x) {
+  const int lane = __lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int nwaves = blockDim.x / kWave;
+  for (int e = wave; e <= a.nb; e += nwaves) {
+    int32_t* row = a.block_hist + (int64_t)e * a.nblocks;
     int run = 0;
-    for (int b = 0; b < a.nblocks; ++b) {
-      int32_t* p = a.block_hist + (int64_t)b * stride + e;
-      const int v = *p;
-      *p = run;
-      run += v;
+    for (int b0 = 0; b0 < a.nblocks; b0 += kWave) {
+      const int b = b0 + lane;
+      const int v = b < a.nblocks ? row[b] : 0;
+      int x = v;
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const int y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+      }
+      if (b < a.nblocks) row[b] = run + x - v;
+      run += __shfl(x, kWave - 1);
     }
-    s_cnt[e] = run;
+    if (lane == 0) s_cnt[e] = run;
   }
   __syncthreads();
   if (threadIdx.x == 0) a.status[0] = s_cnt[a.nb];
-  finish_layout(a, s_cnt, s_off, s_tmp);
+  bucket_layout(a, s_cnt, s_off, s_tmp);
 }
 
-// Launch 3: each chunk scatters its routes from its starting ranks.
+// Launch 3: each chunk scatters its routes from its starting ranks; the
+// workgroups also write the padding and the tile owners.
 __global__ void __launch_bounds__(256) align_scatter_kernel(AlignArgs a) {
   __shared__ int s_cur[kAlignMaxBuckets];
-  const int32_t* h = a.block_hist + (int64_t)blockIdx.x * (a.nb + 1);
-  for (int e = threadIdx.x; e < a.nb; e += blockDim.x) s_cur[e] = a.offsets[e] + h[e];
+  for (int e = threadIdx.x; e < a.nb; e += blockDim.x)
+    s_cur[e] = a.offsets[e] + a.block_hist[(int64_t)e * a.nblocks + blockIdx.x];
   __syncthreads();
-  const int64_t begin = (int64_t)blockIdx.x * kAlignChunk;
-  const int64_t end = min(a.R, begin + kAlignChunk);
+  const int64_t begin = (int64_t)blockIdx.x * a.chunk;
+  const int64_t end = min(a.R, begin + a.chunk);
   scatter_range(a, begin, end, s_cur);
+  const int nwaves = blockDim.x / kWave;
+  pad_and_owners(a, (int64_t)blockIdx.x * nwaves + threadIdx.x / kWave, (int64_t)gridDim.x * nwaves,
+                 (int64_t)blockIdx.x * blockDim.x + threadIdx.x, (int64_t)gridDim.x * blockDim.x);
 }
 
 }  // namespace
 
-hipError_t launch_align(const AlignArgs& a, hipStream_t s) {
+hipError_t launch_align(const AlignArgs& args, hipStream_t s) {
+  AlignArgs a = args;
+  a.nbits = 0;
+  while ((1 << a.nbits) < a.nb) ++a.nbits;
   if (a.nblocks == 0) {
     hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(1024), 0, s, a);
     return hipGetLastError();
   }
+  // chunks of a multiple of 256 routes, one per workgroup
+  const int64_t per = (a.R + a.nblocks - 1) / a.nblocks;
+  a.chunk = (int32_t)((per + 255) / 256 * 256);
   hipLaunchKernelGGL(align_hist_kernel, dim3(a.nblocks), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -51,29 +51,22 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_floa
 
 __device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + expf(-v)); }
 
-// Rank of this lane among the active lanes of its wave holding the same key
+// Rank of this lane among the valid lanes of its wave holding the same key
 // (lower lanes first), the size of that group, and whether this lane is the
-// group's last.  The loop runs once per distinct key in the wave.
-__device__ __forceinline__ void wave_match_rank(int key, bool valid, int& rank, int& gsize,
+// group's last.  Keys are below 2^nbits; one ballot per key bit narrows each
+// lane's mask to the lanes that agree with it on every bit.
+__device__ __forceinline__ void wave_match_rank(int key, bool valid, int nbits, int& rank, int& gsize,
                                                 bool& is_last) {
   const int lane = __lane_id();
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  uint64_t pending = __ballot(valid);
-  rank = 0;
-  gsize = 0;
-  is_last = false;
-  while (pending) {
-    const int leader = __ffsll((unsigned long long)pending) - 1;
-    const int lk = __shfl(key, leader);
-    const bool mine = valid && key == lk;
-    const uint64_t m = __ballot(mine);
-    if (mine) {
-      rank = __popcll(m & below);
-      gsize = __popcll(m);
-      is_last = rank == gsize - 1;
-    }
-    pending &= ~m;
+  uint64_t eq = __ballot(valid);
+  for (int j = 0; j < nbits; ++j) {
+    const uint64_t b = __ballot((key >> j) & 1);
+    eq &= ((key >> j) & 1) ? b : ~b;
   }
+  rank = __popcll(eq & below);
+  gsize = __popcll(eq);
+  is_last = valid && rank == gsize - 1;
 }
 
 // ---------------------------------------------------------------------------

@@ -33,11 +33,14 @@ struct AlignArgs {
   int64_t max_tiles;
   int64_t max_active;
   int32_t sentinel;
-  int32_t nblocks;             // 0: single-block path
+  int32_t nblocks;             // 0: single-block path; else chunks (<= kAlignMaxBlocks)
+  int32_t chunk;               // set by launch_align: keys per chunk
+  int32_t nbits;               // set by launch_align: bits of a bucket index
 };
 
 constexpr int kAlignSmallMaxR = 8192;    // single-workgroup path up to this R
-constexpr int kAlignChunk = 4096;        // keys per workgroup in the multi-block path
+constexpr int kAlignChunk = 1024;        // keys per workgroup in the multi-block path (at least)
+constexpr int kAlignMaxBlocks = 1024;    // workgroups of the multi-block path (at most)
 constexpr int kAlignMaxBuckets = 8192;   // LDS-resident bucket counters
 
 hipError_t launch_align(const AlignArgs& a, hipStream_t s);

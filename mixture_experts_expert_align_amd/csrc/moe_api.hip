@@ -41,7 +41,11 @@ AlignLayout layout_align(int64_t base, int64_t nb, int64_t capacity, int64_t max
   return L;
 }
 
-int64_t align_nblocks(int64_t R) { return R <= kAlignSmallMaxR ? 0 : (R + kAlignChunk - 1) / kAlignChunk; }
+int64_t align_nblocks(int64_t R) {
+  if (R <= kAlignSmallMaxR) return 0;
+  const int64_t n = (R + kAlignChunk - 1) / kAlignChunk;
+  return n < kAlignMaxBlocks ? n : kAlignMaxBlocks;
+}
 
 template <typename T>
 T* at(void* base, int64_t off) { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }

@@ -119,4 +119,6 @@ def test_align_path_choice():
     small = moe.moe_plan_init(moe.make_problem(1024, 256, 512, 8, topk=8))     # R = 8192
     big = moe.moe_plan_init(moe.make_problem(1025, 256, 512, 8, topk=8))       # R = 8200
     assert small.align_blocks == 0
-    assert big.align_blocks == 3
+    assert big.align_blocks == 9                                                # chunks of 1024
+    huge = moe.moe_plan_init(moe.make_problem(131073, 256, 512, 8, topk=8))    # R = 1048584
+    assert huge.align_blocks == 1024                                            # at most 1024 chunks
