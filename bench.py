@@ -53,10 +53,16 @@ def parse():
 
 
 def kernel_source_hash(files):
+    """Hash of the kernels' sources with comments and whitespace removed, so
+    that only a change to the code itself invalidates recorded counters."""
+    import re
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "mixture_experts_expert_align_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "mixture_experts_expert_align_amd", "csrc", f)) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        h.update(re.sub(r"\s+", "", src).encode())
     return h.hexdigest()[:16]
 
 
@@ -101,9 +107,11 @@ def counter_values(path: str, counter: str, kernel_substr: str):
 def traffic_from(args):
     import numpy as np
     cfg_name = args.config.split("_")[0]
-    kern = DOMINANT_KERNEL[cfg_name]
-    fetch = counter_values(args.traffic_from[0], "FETCH_SIZE", kern)
-    write = counter_values(args.traffic_from[1], "WRITE_SIZE", kern)
+    kerns = DOMINANT_KERNEL[cfg_name]
+    # per kernel of the timed stage: the median over its dispatches; the
+    # stage's traffic is the sum over its kernels
+    fetch = [float(np.median(counter_values(args.traffic_from[0], "FETCH_SIZE", k))) for k in kerns]
+    write = [float(np.median(counter_values(args.traffic_from[1], "WRITE_SIZE", k))) for k in kerns]
     # the calibration run makes COPY_LAUNCHES copies; the runtime may split a
     # copy over several dispatches, so compare per-copy sums
     cfetch = sum(counter_values(args.traffic_from[2], "FETCH_SIZE", "copy")) / COPY_LAUNCHES
@@ -111,10 +119,10 @@ def traffic_from(args):
     copy_bytes = COPY_MIB << 20
     f_scale = copy_bytes / (cfetch * 1024)
     w_scale = copy_bytes / (cwrite * 1024)
-    traffic = np.median(fetch) * 1024 * f_scale + np.median(write) * 1024 * w_scale
-    rec = {"workload": cfg_name, "kernel": kern,
+    traffic = sum(fetch) * 1024 * f_scale + sum(write) * 1024 * w_scale
+    rec = {"workload": cfg_name, "kernels": list(kerns),
            "kernel_source_hash": kernel_source_hash(KERNEL_FILES[cfg_name]),
-           "fetch_kib_per_dispatch": float(np.median(fetch)), "write_kib_per_dispatch": float(np.median(write)),
+           "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
            "copy_calibration_bytes": copy_bytes,
            "copy_fetch_kib": float(cfetch), "copy_write_kib": float(cwrite),
            "fetch_scale": f_scale, "write_scale": w_scale,
@@ -127,13 +135,17 @@ def traffic_from(args):
 
 COPY_MIB = 1024
 COPY_LAUNCHES = 3
-# The dominant kernel of each workload (name substring in the profiler's
-# kernel names) and the sources it is built from.
-DOMINANT_KERNEL = {"tiny": "gemm_tile_bf16_kernel<0>", "decode": "gemm_stream_bf16_kernel<0,",
-                   "prefill": "gemm_tile_bf16_kernel<0>", "mxfp8": "gemm_stream_mxfp8_kernel<0>",
-                   "batched": "gemm_tile_bf16_kernel<0>"}
+# The kernels of each workload's timed dominant stage (name substrings in
+# the profiler's kernel names) and the sources they are built from: the W1
+# stage (gate_up_act) for the contiguous format (for MXFP8 weights it also
+# quantises the gathered activation rows), both GEMMs (apply_batched) for
+# the batched format.
+DOMINANT_KERNEL = {"tiny": ["gemm_tile_bf16_kernel<0,"], "decode": ["gemm_stream_bf16_kernel<0,"],
+                   "prefill": ["gemm_tile_bf16_kernel<0,"],
+                   "mxfp8": ["quantize_gather_kernel", "gemm_stream_mxfp8_kernel<0,"],
+                   "batched": ["gemm_tile_bf16_kernel<0,", "gemm_tile_bf16_kernel<1,"]}
 KERNEL_FILES = {"tiny": ["gemm_tile.hip"], "decode": ["gemm_stream.hip"], "prefill": ["gemm_tile.hip"],
-                "mxfp8": ["gemm_stream.hip"], "batched": ["gemm_tile.hip"]}
+                "mxfp8": ["reduce_codec.hip", "gemm_stream.hip"], "batched": ["gemm_tile.hip"]}
 
 
 def main():

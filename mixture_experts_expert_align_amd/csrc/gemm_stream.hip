@@ -170,7 +170,7 @@ __global__ void __launch_bounds__(64 * KS) gemm_stream_bf16_kernel(GemmArgs g) {
 //
 // A workgroup owns four 16-row weight tiles of one expert, one per wave; each
 // wave streams its tile over the whole contraction straight from HBM into
-// registers, one stage (four 128-wide steps) ahead.  The 64 routed token rows
+// registers, one stage (two 128-wide steps) ahead.  The 64 routed token rows
 // of a pass (four 16-token column tiles) are staged in LDS a stage at a time
 // (double buffered) and shared by the four waves, so activations cross L2
 // once per workgroup.  The barriers between stages wait only for LDS
