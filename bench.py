@@ -190,16 +190,26 @@ def main():
         w_f32 = None
 
     contiguous = cfg.layout == "contiguous"
+    # an expert-parallel share (the affine routing) is fed as an EP
+    # implementation receives it: global ids, unmasked weights, the rank's map
+    ep_share = contiguous and inp.global_ids is not None
     prob = moe.make_problem(cfg.M, cfg.K, cfg.I, cfg.E, topk=cfg.topk, max_tokens=cfg.max_tokens,
                             layout=0 if contiguous else 1, w_dtype=0 if cfg.w_dtype == "bf16" else 1,
-                            w1_order=0 if cfg.w1_order == "halves" else 1)
+                            w1_order=0 if cfg.w1_order == "halves" else 1,
+                            global_experts=cfg.global_experts if ep_share else 0)
     plan = moe.moe_plan_init(prob)
     ws13, ws2 = moe.allocate_workspaces(plan)
     stream = torch.cuda.current_stream()
 
     if contiguous:
-        ids = torch.from_numpy(inp.topk_ids).to(dev)
-        wts = torch.from_numpy(inp.topk_weights).to(dev)
+        emap = None
+        if ep_share:
+            ids = torch.from_numpy(inp.global_ids).to(dev)
+            wts = torch.from_numpy(inp.global_weights).to(dev)
+            emap = torch.from_numpy(mi.ep_expert_map(cfg.global_experts, cfg.E, rank=0)).to(dev)
+        else:
+            ids = torch.from_numpy(inp.topk_ids).to(dev)
+            wts = torch.from_numpy(inp.topk_weights).to(dev)
         out = torch.empty((cfg.M, cfg.K), dtype=torch.bfloat16, device=dev)
         R = cfg.M * cfg.topk
         valid = (inp.topk_ids >= 0) & (inp.topk_ids < cfg.E)
@@ -210,13 +220,13 @@ def main():
 
         def step(ev):
             ev[0].record(stream)
-            moe.moe_align_permute(plan, ids, ws13, stream)
+            moe.moe_align_permute(plan, ids, ws13, stream, expert_map=emap)
             ev[1].record(stream)
             moe.moe_gate_up_act(plan, inp.x, w1, w2, ws13, w1_scale, w2_scale, stream)
             ev[2].record(stream)
             moe.moe_down_unpermute(plan, w1, w2, ws13, ws2, w1_scale, w2_scale, stream)
             ev[3].record(stream)
-            moe.moe_topk_reduce_contiguous(plan, ws2, ids, wts, out, stream)
+            moe.moe_topk_reduce_contiguous(plan, ws2, ids, wts, out, stream, expert_map=emap)
             ev[4].record(stream)
     else:
         counts = torch.from_numpy(inp.expert_num_tokens).to(dev)
@@ -303,7 +313,8 @@ def main():
         "data": "synthetic (seeded counter-based generator; random-init expert weights)",
         "config": {"workload": cfg.name, "M": cfg.M, "K": K, "I": I, "E": cfg.E, "topk": cfg.topk,
                    "max_tokens": cfg.max_tokens, "weights": dtype_name, "routes": n_routes,
-                   "active_experts": n_act, "variant": plan.reason.decode()},
+                   "active_experts": n_act, "variant": plan.reason.decode(),
+                   "global_experts": int(plan.prob.global_experts)},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "step_weight_GBps": round(step_gbs, 1),
         "step_TFLOPs": round(6.0 * n_routes * K * I / (ms_per_step * 1e-3) / 1e12, 3),

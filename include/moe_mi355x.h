@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 /* Status codes. */
 enum {
@@ -95,6 +95,14 @@ typedef struct moe_problem {
   int64_t E;           /* experts held by this GPU                            */
   int64_t topk;        /* contiguous: slots per token; batched: ignored       */
   int64_t max_tokens;  /* batched: rows per expert slab; contiguous: ignored  */
+  /* contiguous: 0 when topk_ids hold local expert ids in [0,E); otherwise
+   * the number G >= E of global expert ids, and topk_ids hold global ids in
+   * [0,G) that moe_weights.expert_map maps to local ones (an expert-parallel
+   * share: page "Fused MoE Modular Kernel", "How To Add a
+   * FusedMoEExpertsModular Type", supports_expert_map(); page "DeepGEMM Mega
+   * MoE as an EP implementation", introduction: global ids, unmasked
+   * weights).  Batched: must be 0. */
+  int64_t global_experts;
   int32_t layout;      /* MOE_LAYOUT_*                                        */
   int32_t w_dtype;     /* MOE_W_*                                             */
   int32_t w1_order;    /* MOE_W1_*                                            */
@@ -106,6 +114,12 @@ typedef struct moe_weights {
   const uint8_t* w1_scale; /* device. UE8M0 [E, 2I, K/32] (MXFP8 only)         */
   const void* w2;          /* device. bf16 or E4M3 [E, K, I]                   */
   const uint8_t* w2_scale; /* device. UE8M0 [E, K, I/32] (MXFP8 only)          */
+  /* device. int32 [global_experts] when prob.global_experts > 0 (else NULL):
+   * the local id in [0,E) of each global expert, -1 for an expert this GPU
+   * does not hold.  Slots whose expert maps to -1 are skipped (whatever their
+   * weight); global ids outside {-1} U [0,G) and map entries outside
+   * {-1} U [0,E) are skipped and counted as invalid. */
+  const int32_t* expert_map;
 } moe_weights;
 
 /* A plan: validated sizes, the chosen kernels and the workspace layout.  The
@@ -165,7 +179,8 @@ void moe_struct_sizes(int64_t* problem, int64_t* plan, int64_t* weights);
  * (STREAM when at most 64 rows can reach one expert, else TILE), the align
  * tile size, the workspace sizes and the reduce kind (NOOP for contiguous,
  * NAIVE_BATCHED for batched).  Errors: MOE_EINVAL for null pointers,
- * non-positive sizes, topk > E, bad enum values or index ranges past 2^31;
+ * non-positive sizes, topk > E, global_experts neither 0 nor in [E, 2^31),
+ * bad enum values or index ranges past 2^31;
  * MOE_EUNSUPPORTED (with plan->reason set) for shapes no kernel is built
  * for: the tiled kernels need K % 256 == 0 and I % 128 == 0 (contiguous
  * format) or K % 128 == 0 and I % 64 == 0 (batched format), the streaming
@@ -181,8 +196,12 @@ const char* moe_plan_reason(const moe_plan* plan);
  * padded to block_m), sorted_ids (ascending flat order within an expert;
  * padding holds R = M*topk), block_expert (-1 past the last run),
  * num_post_padded, the active-expert list and the status word.  Ids outside
- * {-1} U [0,E) are skipped and counted in status[0].  Contiguous plans only. */
-int moe_align_permute(const moe_plan* plan, const int32_t* topk_ids, void* ws13, void* stream);
+ * {-1} U [0,E) are skipped and counted in status[0].  expert_map: device
+ * int32 [global_experts] as in moe_weights (ids are then global and mapped
+ * first), or NULL when plan->prob.global_experts == 0 (MOE_EINVAL if one is
+ * given without the other).  Contiguous plans only. */
+int moe_align_permute(const moe_plan* plan, const int32_t* topk_ids, const int32_t* expert_map,
+                      void* ws13, void* stream);
 
 /* The whole expert computation on the contiguous format (page "Fused MoE
  * Modular Kernel", apply(); reduce kind NOOP: the top-k weighted sum is done
@@ -204,7 +223,8 @@ int moe_apply_contiguous(const moe_plan* plan, const void* a, const int32_t* top
  * MoE Modular Kernel", apply() steps 2-4).  Writes z into ws13.
  * moe_down_unpermute: matmul with W2 and unpermute (steps 5-6): writes each
  * route's row to its (token, slot) row of ws2 (bf16 [M*topk, K]).
- * Arguments as for moe_apply_contiguous. */
+ * Arguments as for moe_apply_contiguous (w->expert_map is not read: the
+ * routes come from moe_align_permute). */
 int moe_gate_up_act(const moe_plan* plan, const void* a, const moe_weights* w, void* ws13,
                     void* stream);
 int moe_down_unpermute(const moe_plan* plan, const moe_weights* w, void* ws13, void* ws2,
@@ -221,10 +241,12 @@ int moe_apply_batched(const moe_plan* plan, const void* a, const int32_t* expert
                       const moe_weights* w, void* y, void* ws13, void* stream);
 
 /* TopKWeightAndReduceContiguous on its own.  y: device bf16 [M*topk, K], row
- * t*topk+j is slot (t, j); out: device bf16 [M, K]; same arithmetic as the
- * reduce inside moe_apply_contiguous. */
+ * t*topk+j is slot (t, j); out: device bf16 [M, K]; expert_map as for
+ * moe_align_permute; same arithmetic as the reduce inside
+ * moe_apply_contiguous. */
 int moe_topk_reduce_contiguous(const moe_plan* plan, const void* y, const int32_t* topk_ids,
-                               const float* topk_weights, void* out, void* stream);
+                               const float* topk_weights, const int32_t* expert_map, void* out,
+                               void* stream);
 
 /* Bytes of workspace moe_topk_reduce_naive_batched needs for n_out tokens. */
 int64_t moe_naive_batched_ws_bytes(const moe_plan* plan, int64_t n_out);

@@ -25,7 +25,7 @@ __all__ = [
     "moe_quantize_mxfp8", "make_problem", "allocate_workspaces", "ws_view",
 ]
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, 1, 2, 3
 LAYOUT_CONTIGUOUS, LAYOUT_BATCHED = 0, 1
 W_BF16, W_MXFP8 = 0, 1
@@ -38,8 +38,8 @@ _i64, _i32, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
 
 class MoeProblem(ctypes.Structure):
     _fields_ = [("M", _i64), ("K", _i64), ("I", _i64), ("E", _i64), ("topk", _i64),
-                ("max_tokens", _i64), ("layout", _i32), ("w_dtype", _i32), ("w1_order", _i32),
-                ("variant", _i32)]
+                ("max_tokens", _i64), ("global_experts", _i64), ("layout", _i32), ("w_dtype", _i32),
+                ("w1_order", _i32), ("variant", _i32)]
 
 
 class MoePlan(ctypes.Structure):
@@ -55,7 +55,7 @@ class MoePlan(ctypes.Structure):
 
 
 class MoeWeights(ctypes.Structure):
-    _fields_ = [("w1", _vp), ("w1_scale", _vp), ("w2", _vp), ("w2_scale", _vp)]
+    _fields_ = [("w1", _vp), ("w1_scale", _vp), ("w2", _vp), ("w2_scale", _vp), ("expert_map", _vp)]
 
 
 class MoeError(RuntimeError):
@@ -90,12 +90,12 @@ def load_library() -> ctypes.CDLL:
         "moe_struct_sizes": (None, [_vp, _vp, _vp]),
         "moe_plan_init": (_i32, [_vp, _vp]),
         "moe_plan_reason": (ctypes.c_char_p, [_vp]),
-        "moe_align_permute": (_i32, [_vp, _vp, _vp, _vp]),
+        "moe_align_permute": (_i32, [_vp] * 5),
         "moe_apply_contiguous": (_i32, [_vp] * 9),
         "moe_apply_batched": (_i32, [_vp] * 7),
         "moe_gate_up_act": (_i32, [_vp] * 5),
         "moe_down_unpermute": (_i32, [_vp] * 5),
-        "moe_topk_reduce_contiguous": (_i32, [_vp] * 6),
+        "moe_topk_reduce_contiguous": (_i32, [_vp] * 7),
         "moe_naive_batched_ws_bytes": (_i64, [_vp, _i64]),
         "moe_topk_reduce_naive_batched": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp]),
         "moe_quantize_mxfp8": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _vp]),
@@ -153,8 +153,8 @@ def moe_status_string(status: int) -> str:
 
 
 def make_problem(M, K, I, E, topk=0, max_tokens=0, layout=LAYOUT_CONTIGUOUS, w_dtype=W_BF16,
-                 w1_order=W1_HALVES, variant=VARIANT_AUTO) -> MoeProblem:
-    return MoeProblem(M, K, I, E, topk, max_tokens, layout, w_dtype, w1_order, variant)
+                 w1_order=W1_HALVES, variant=VARIANT_AUTO, global_experts=0) -> MoeProblem:
+    return MoeProblem(M, K, I, E, topk, max_tokens, global_experts, layout, w_dtype, w1_order, variant)
 
 
 def moe_plan_init(prob: MoeProblem) -> MoePlan:
@@ -181,19 +181,20 @@ def ws_view(ws: torch.Tensor, offset: int, count: int, dtype=torch.int32) -> tor
     return ws[offset: offset + nbytes].view(dtype)
 
 
-def moe_align_permute(plan: MoePlan, topk_ids: torch.Tensor, ws13: torch.Tensor, stream=None):
-    st = load_library().moe_align_permute(ctypes.byref(plan), _ptr(topk_ids), _ptr(ws13),
-                                          _stream(stream))
+def moe_align_permute(plan: MoePlan, topk_ids: torch.Tensor, ws13: torch.Tensor, stream=None,
+                      expert_map: Optional[torch.Tensor] = None):
+    st = load_library().moe_align_permute(ctypes.byref(plan), _ptr(topk_ids), _ptr(expert_map),
+                                          _ptr(ws13), _stream(stream))
     _check("moe_align_permute", st)
 
 
-def _weights(w1, w2, w1_scale=None, w2_scale=None) -> MoeWeights:
-    return MoeWeights(_ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale))
+def _weights(w1, w2, w1_scale=None, w2_scale=None, expert_map=None) -> MoeWeights:
+    return MoeWeights(_ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale), _ptr(expert_map))
 
 
 def moe_apply_contiguous(plan: MoePlan, a, topk_ids, topk_weights, w1, w2, out, ws13, ws2,
-                         w1_scale=None, w2_scale=None, stream=None):
-    w = _weights(w1, w2, w1_scale, w2_scale)
+                         w1_scale=None, w2_scale=None, stream=None, expert_map=None):
+    w = _weights(w1, w2, w1_scale, w2_scale, expert_map)
     st = load_library().moe_apply_contiguous(
         ctypes.byref(plan), _ptr(a), _ptr(topk_ids), _ptr(topk_weights), ctypes.byref(w), _ptr(out),
         _ptr(ws13), _ptr(ws2), _stream(stream))
@@ -221,9 +222,11 @@ def moe_apply_batched(plan: MoePlan, a, expert_num_tokens, w1, w2, y, ws13, stre
     _check("moe_apply_batched", st)
 
 
-def moe_topk_reduce_contiguous(plan: MoePlan, y, topk_ids, topk_weights, out, stream=None):
+def moe_topk_reduce_contiguous(plan: MoePlan, y, topk_ids, topk_weights, out, stream=None,
+                               expert_map: Optional[torch.Tensor] = None):
     st = load_library().moe_topk_reduce_contiguous(ctypes.byref(plan), _ptr(y), _ptr(topk_ids),
-                                                   _ptr(topk_weights), _ptr(out), _stream(stream))
+                                                   _ptr(topk_weights), _ptr(expert_map), _ptr(out),
+                                                   _stream(stream))
     _check("moe_topk_reduce_contiguous", st)
 
 

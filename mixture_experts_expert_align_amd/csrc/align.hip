@@ -34,7 +34,15 @@ __device__ __forceinline__ KeyRead read_key(const AlignArgs& a, int64_t i) {
     const int64_t row = i - g * a.rows_per_group;
     if (row >= a.group_count[g]) return r;  // masked row: never read
   }
-  const int k = a.keys[i];
+  int k = a.keys[i];
+  if (a.key_map) {
+    if (k >= 0 && k < a.key_range) {
+      k = a.key_map[k];
+    } else if (k != -1) {
+      r.invalid = true;    // outside {-1} U [0, key_range)
+      return r;
+    }
+  }
   r.key = k;
   r.valid = k >= 0 && k < a.nb;
   r.invalid = !r.valid && k != -1;

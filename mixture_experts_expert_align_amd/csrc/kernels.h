@@ -9,13 +9,17 @@
 namespace moe {
 
 // ---------------------------------------------------------------- align ----
-// Stable counting sort of R flat keys into nb buckets.  Key i is valid when
-// 0 <= key < nb and, if group_count is given, (i % rows_per_group) <
-// group_count[i / rows_per_group] (the batched format's valid rows).  Keys
-// other than -1 that are out of range count in status[0] (keys of rows
-// masked out by group_count are never read).
+// Stable counting sort of R flat keys into nb buckets.  With key_map, a key
+// k in [0, key_range) is first replaced by key_map[k] (-1: skipped, not an
+// error) and a key outside {-1} U [0, key_range) is invalid.  Key i is valid
+// when the (mapped) key is in [0, nb) and, if group_count is given,
+// (i % rows_per_group) < group_count[i / rows_per_group] (the batched
+// format's valid rows).  Keys other than -1 that are out of range count in
+// status[0] (keys of rows masked out by group_count are never read).
 struct AlignArgs {
   const int32_t* keys;
+  const int32_t* key_map;      // optional: keys in [0, key_range) are replaced by key_map[key]
+  int32_t key_range;
   int64_t R;
   int32_t nb;
   int32_t B;                   // each bucket's run is padded to a multiple of B
@@ -95,9 +99,11 @@ hipError_t launch_gemm_stream_bf16(const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_stream_mxfp8(const GemmArgs& g, hipStream_t s);
 
 // --------------------------------------------------------------- reduce ----
+// out[t] = sum over slots j (ascending) whose id (mapped through expert_map
+// when given: ids in [0, G)) is a local expert in [0, E) of w[t,j] * y[t*topk+j]
 hipError_t launch_reduce_contiguous(const uint16_t* y, const int32_t* ids, const float* w,
-                                    uint16_t* out, int64_t M, int32_t topk, int64_t K, int32_t E,
-                                    hipStream_t s);
+                                    const int32_t* expert_map, int32_t G, uint16_t* out, int64_t M,
+                                    int32_t topk, int64_t K, int32_t E, hipStream_t s);
 // out[t] = sum over CSR list of t (ascending) of w[row] * y[row]
 hipError_t launch_reduce_csr(const uint16_t* y, const float* w, const int32_t* offsets,
                              const int32_t* rows, uint16_t* out, int64_t n_out, int64_t K,

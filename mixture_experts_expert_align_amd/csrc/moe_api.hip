@@ -50,9 +50,11 @@ int64_t align_nblocks(int64_t R) {
 template <typename T>
 T* at(void* base, int64_t off) { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
 
-AlignArgs align_args(const moe_plan* p, const int32_t* keys, void* ws13) {
+AlignArgs align_args(const moe_plan* p, const int32_t* keys, const int32_t* expert_map, void* ws13) {
   AlignArgs a{};
   a.keys = keys;
+  a.key_map = expert_map;
+  a.key_range = (int32_t)p->prob.global_experts;
   a.R = p->routes;
   a.nb = (int32_t)p->prob.E;
   a.B = p->block_m;
@@ -114,9 +116,14 @@ int moe_plan_init(moe_plan* plan, const moe_problem* prob) {
     return fail(plan, MOE_EINVAL, "unknown variant");
   const bool contiguous = P.layout == MOE_LAYOUT_CONTIGUOUS;
   if (contiguous) {
-    if (P.topk <= 0 || P.topk > P.E) return fail(plan, MOE_EINVAL, "topk must be in [1, E]");
-  } else if (P.max_tokens <= 0) {
-    return fail(plan, MOE_EINVAL, "max_tokens must be positive");
+    if (P.global_experts != 0 && (P.global_experts < P.E || P.global_experts >= (1ll << 31)))
+      return fail(plan, MOE_EINVAL, "global_experts must be 0 or in [E, 2^31)");
+    const int64_t id_space = P.global_experts ? P.global_experts : P.E;
+    if (P.topk <= 0 || P.topk > id_space)
+      return fail(plan, MOE_EINVAL, "topk must be in [1, E] (or [1, global_experts])");
+  } else {
+    if (P.max_tokens <= 0) return fail(plan, MOE_EINVAL, "max_tokens must be positive");
+    if (P.global_experts != 0) return fail(plan, MOE_EINVAL, "the batched format takes local experts only");
   }
   const int64_t R = contiguous ? P.M * P.topk : P.E * P.max_tokens;
   // flat slot ids, positions and the sentinel are int32; rows are addressed
@@ -220,11 +227,17 @@ int moe_plan_init(moe_plan* plan, const moe_problem* prob) {
   return MOE_OK;
 }
 
-int moe_align_permute(const moe_plan* plan, const int32_t* topk_ids, void* ws13, void* stream) {
+// An expert map is given exactly when the plan's ids are global.
+static bool map_ok(const moe_plan* plan, const int32_t* expert_map) {
+  return plan->prob.global_experts ? aligned4(expert_map) : expert_map == nullptr;
+}
+
+int moe_align_permute(const moe_plan* plan, const int32_t* topk_ids, const int32_t* expert_map,
+                      void* ws13, void* stream) {
   if (!plan || plan->abi_version != MOE_ABI_VERSION) return MOE_EINVAL;
   if (plan->prob.layout != MOE_LAYOUT_CONTIGUOUS) return MOE_EINVAL;
-  if (!aligned4(topk_ids) || !aligned16(ws13)) return MOE_EINVAL;
-  AlignArgs a = align_args(plan, topk_ids, ws13);
+  if (!aligned4(topk_ids) || !aligned16(ws13) || !map_ok(plan, expert_map)) return MOE_EINVAL;
+  AlignArgs a = align_args(plan, topk_ids, expert_map, ws13);
   return launch_align(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
@@ -334,19 +347,20 @@ int moe_down_unpermute(const moe_plan* plan, const moe_weights* w, void* ws13, v
 int moe_apply_contiguous(const moe_plan* plan, const void* a, const int32_t* topk_ids,
                          const float* topk_weights, const moe_weights* w, void* out, void* ws13,
                          void* ws2, void* stream) {
-  if (!contiguous_args_ok(plan, w)) return MOE_EINVAL;
+  if (!contiguous_args_ok(plan, w) || !map_ok(plan, w->expert_map)) return MOE_EINVAL;
   const moe_problem& P = plan->prob;
   if (!aligned16(a) || !aligned4(topk_ids) || !aligned4(topk_weights) || !aligned16(out) ||
       !aligned16(ws13) || !aligned16(ws2))
     return MOE_EINVAL;
   hipStream_t s = (hipStream_t)stream;
-  AlignArgs al = align_args(plan, topk_ids, ws13);
+  AlignArgs al = align_args(plan, topk_ids, w->expert_map, ws13);
   if (launch_align(al, s) != hipSuccess) return MOE_EHIP;
   int st = gate_up_act(plan, a, w, ws13, s);
   if (st != MOE_OK) return st;
   st = down_unpermute(plan, w, ws13, ws2, s);
   if (st != MOE_OK) return st;
   hipError_t e = launch_reduce_contiguous(static_cast<const uint16_t*>(ws2), topk_ids, topk_weights,
+                                          w->expert_map, (int32_t)P.global_experts,
                                           static_cast<uint16_t*>(out), P.M, (int32_t)P.topk, P.K,
                                           (int32_t)P.E, s);
   return e == hipSuccess ? MOE_OK : MOE_EHIP;
@@ -390,13 +404,16 @@ int moe_apply_batched(const moe_plan* plan, const void* a, const int32_t* expert
 }
 
 int moe_topk_reduce_contiguous(const moe_plan* plan, const void* y, const int32_t* topk_ids,
-                               const float* topk_weights, void* out, void* stream) {
+                               const float* topk_weights, const int32_t* expert_map, void* out,
+                               void* stream) {
   if (!plan || plan->abi_version != MOE_ABI_VERSION) return MOE_EINVAL;
   const moe_problem& P = plan->prob;
   if (P.layout != MOE_LAYOUT_CONTIGUOUS) return MOE_EINVAL;
-  if (!aligned16(y) || !aligned4(topk_ids) || !aligned4(topk_weights) || !aligned16(out))
+  if (!aligned16(y) || !aligned4(topk_ids) || !aligned4(topk_weights) || !aligned16(out) ||
+      !map_ok(plan, expert_map))
     return MOE_EINVAL;
   hipError_t e = launch_reduce_contiguous(static_cast<const uint16_t*>(y), topk_ids, topk_weights,
+                                          expert_map, (int32_t)P.global_experts,
                                           static_cast<uint16_t*>(out), P.M, (int32_t)P.topk, P.K,
                                           (int32_t)P.E, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : MOE_EHIP;

@@ -40,6 +40,7 @@ __device__ __forceinline__ i32x4 pack8(const float* acc) {
 __global__ void __launch_bounds__(NT) reduce_contiguous_kernel(const uint16_t* __restrict__ y,
                                                                const int32_t* __restrict__ ids,
                                                                const float* __restrict__ w,
+                                                               const int32_t* __restrict__ emap, int G,
                                                                uint16_t* __restrict__ out, int64_t M,
                                                                int topk, int64_t K, int E) {
   const int64_t K8 = K / 8;
@@ -50,7 +51,8 @@ __global__ void __launch_bounds__(NT) reduce_contiguous_kernel(const uint16_t* _
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < topk; ++j) {
     const int64_t s = t * topk + j;
-    const int id = ids[s];
+    int id = ids[s];
+    if (emap) id = (id >= 0 && id < G) ? emap[id] : -1;   // global -> local (-1: held elsewhere)
     if (id < 0 || id >= E) continue;
     const i32x4 v = *reinterpret_cast<const i32x4*>(y + s * K + c);
     fma8(acc, w[s], v);
@@ -164,10 +166,10 @@ inline unsigned nblocks(int64_t n) { return (unsigned)((n + NT - 1) / NT); }
 }  // namespace
 
 hipError_t launch_reduce_contiguous(const uint16_t* y, const int32_t* ids, const float* w,
-                                    uint16_t* out, int64_t M, int32_t topk, int64_t K, int32_t E,
-                                    hipStream_t s) {
+                                    const int32_t* expert_map, int32_t G, uint16_t* out, int64_t M,
+                                    int32_t topk, int64_t K, int32_t E, hipStream_t s) {
   hipLaunchKernelGGL(reduce_contiguous_kernel, dim3(nblocks(M * (K / 8))), dim3(NT), 0, s, y, ids, w,
-                     out, M, topk, K, E);
+                     expert_map, G, out, M, topk, K, E);
   return hipGetLastError();
 }
 

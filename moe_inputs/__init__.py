@@ -181,16 +181,27 @@ def routing_softmax_topk(logits: np.ndarray, topk: int, bias: Optional[np.ndarra
 
 def routing_affine_ep_share(M: int, topk: int, global_experts: int, local_experts: int):
     """The affine route map of the MegaMoE EP16 example: global id of slot
-    (t, j) is ((t*topk + j)*73 + 19) mod global_experts.  This GPU holds the
-    experts [0, local_experts); other ids become -1 with weight 0, and the
-    local ones get weight 1/topk."""
+    (t, j) is ((t*topk + j)*73 + 19) mod global_experts, every slot weighted
+    1/topk.  This GPU holds the experts [0, local_experts).  Returns the
+    host-masked local form (other ids -1 with weight 0) and the global form
+    (global ids, unmasked weights) that goes with ``ep_expert_map``."""
     t = np.arange(M, dtype=np.int64)[:, None]
     j = np.arange(topk, dtype=np.int64)[None, :]
     gid = ((t * topk + j) * 73 + 19) % global_experts
     local = gid < local_experts
     ids = np.where(local, gid, -1).astype(np.int32)
     w = np.where(local, np.float32(1.0 / topk), np.float32(0.0)).astype(np.float32)
-    return ids, w, gid.astype(np.int32)
+    gw = np.full(gid.shape, np.float32(1.0 / topk), dtype=np.float32)
+    return ids, w, gid.astype(np.int32), gw
+
+
+def ep_expert_map(global_experts: int, local_experts: int, rank: int = 0) -> np.ndarray:
+    """int32 [global_experts]: rank ``rank`` of an expert-parallel group holds
+    the global experts [rank*local_experts, (rank+1)*local_experts) as local
+    ids 0.., every other entry is -1."""
+    g = np.arange(global_experts, dtype=np.int64)
+    lo = rank * local_experts
+    return np.where((g >= lo) & (g < lo + local_experts), g - lo, -1).astype(np.int32)
 
 
 def batched_zipf_rows(E: int, max_tokens: int, n_out: int, slot_pool: int, seed: int,
@@ -224,6 +235,7 @@ class Inputs:
     topk_ids: Optional[np.ndarray] = None       # int32 [M,topk]
     topk_weights: Optional[np.ndarray] = None   # float32 [M,topk]
     global_ids: Optional[np.ndarray] = None     # int32 [M,topk] (affine routing only)
+    global_weights: Optional[np.ndarray] = None # float32 [M,topk], unmasked (affine routing only)
     # batched
     a: Optional[torch.Tensor] = None            # bf16 [E,max_tokens,K]
     expert_num_tokens: Optional[np.ndarray] = None  # int32 [E]
@@ -287,7 +299,7 @@ def make_inputs(cfg: MoEConfig, device="cpu", weights: bool = True) -> Inputs:
         r = make_routing(cfg)
         inp.topk_ids, inp.topk_weights = r[0], r[1]
         if len(r) > 2:
-            inp.global_ids = r[2]
+            inp.global_ids, inp.global_weights = r[2], r[3]
         inp.x = activations(cfg, device)
     else:
         inp.expert_num_tokens, inp.row_token, inp.row_weight = make_routing(cfg)

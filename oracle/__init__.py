@@ -34,6 +34,9 @@ Readings where the pages are silent (each also listed in the design notes):
 * The align step pads each expert's run of routes to a multiple of the tile
   size B with the sentinel M*topk; routes keep ascending flat (t*topk + j) order
   within an expert; ids outside {-1} U [0, E) are skipped and counted.
+* With global expert ids, the map is applied first (``map_expert_ids``) and the
+  steps then run on local ids; a slot whose expert another GPU holds is
+  skipped without being counted as invalid.
 
 parity pins: every function here is pinned by ``tests/test_oracle_*.py``
 (closed forms, library special cases, brute force, invariants); none is
@@ -211,6 +214,30 @@ def expert_ffn(x: np.ndarray, w1: np.ndarray, w2: np.ndarray, order: str = "halv
     u = x @ up.T
     z = silu(g) * u
     return z @ np.asarray(w2, dtype=np.float64).T
+
+
+# --------------------------------------------------------------------------
+# Global expert ids (expert parallelism)
+# --------------------------------------------------------------------------
+
+def map_expert_ids(topk_ids: np.ndarray, expert_map: np.ndarray) -> np.ndarray:
+    """Global expert ids -> this GPU's local ids through an expert map.
+
+    [MK] "How To Add a FusedMoEExpertsModular Type", supports_expert_map():
+    an implementation may take global ids with a map; [MEGA] introduction:
+    the expert kernel receives global (not rank-remapped) ids and unmasked
+    weights.  expert_map[g] is the local id of global expert g, or -1 when
+    another GPU holds it.  Result: -1 stays -1 (skipped slot); g in [0, G)
+    becomes expert_map[g] (-1: held elsewhere, skipped); any other id becomes
+    -2 (skipped and counted as invalid by the steps below, like a local id
+    outside [0, E); so is a map entry outside {-1} U [0, E))."""
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    emap = np.asarray(expert_map, dtype=np.int64)
+    out = np.full(ids.shape, -2, dtype=np.int64)
+    out[ids == -1] = -1
+    inside = (ids >= 0) & (ids < emap.size)
+    out[inside] = emap[ids[inside]]
+    return out.astype(np.int32)
 
 
 # --------------------------------------------------------------------------

@@ -45,12 +45,12 @@ class DeviceCase:
     cache: dict = field(default_factory=dict)
 
 
-def problem(cfg: mi.MoEConfig, variant=moe.VARIANT_AUTO):
+def problem(cfg: mi.MoEConfig, variant=moe.VARIANT_AUTO, global_experts=0):
     return moe.make_problem(cfg.M, cfg.K, cfg.I, cfg.E, topk=cfg.topk, max_tokens=cfg.max_tokens,
                             layout=moe.LAYOUT_CONTIGUOUS if cfg.layout == "contiguous" else moe.LAYOUT_BATCHED,
                             w_dtype=moe.W_BF16 if cfg.w_dtype == "bf16" else moe.W_MXFP8,
                             w1_order=moe.W1_HALVES if cfg.w1_order == "halves" else moe.W1_INTERLEAVE16,
-                            variant=variant)
+                            variant=variant, global_experts=global_experts)
 
 
 def quantize_on_device(w: torch.Tensor):
@@ -82,13 +82,18 @@ def make_case(cfg: mi.MoEConfig, device="cuda") -> DeviceCase:
     return c
 
 
-def run_contiguous(c: DeviceCase, variant=moe.VARIANT_AUTO, ids=None, wts=None, x=None):
-    plan = moe.moe_plan_init(problem(c.cfg, variant))
+def run_contiguous(c: DeviceCase, variant=moe.VARIANT_AUTO, ids=None, wts=None, x=None,
+                   expert_map: Optional[np.ndarray] = None):
+    """One moe_apply_contiguous call; with ``expert_map`` (host int32 [G]) the
+    ids are global and the plan's global_experts is G."""
+    G = 0 if expert_map is None else len(expert_map)
+    plan = moe.moe_plan_init(problem(c.cfg, variant, global_experts=G))
     ws13, ws2 = moe.allocate_workspaces(plan)
     out = torch.empty((c.cfg.M, c.cfg.K), dtype=torch.bfloat16, device="cuda")
+    emap = None if expert_map is None else torch.from_numpy(np.asarray(expert_map, np.int32)).cuda()
     moe.moe_apply_contiguous(plan, c.inp.x if x is None else x, c.ids if ids is None else ids,
                              c.wts if wts is None else wts, c.w1, c.w2, out, ws13, ws2,
-                             c.w1_scale, c.w2_scale)
+                             c.w1_scale, c.w2_scale, expert_map=emap)
     torch.cuda.synchronize()
     return out, plan, ws13, ws2
 

@@ -87,6 +87,9 @@ def test_plans_of_the_five_workloads(idx):
     (dict(layout=1, max_tokens=64, w_dtype=moe.W_MXFP8), moe.MOE_EUNSUPPORTED),
     (dict(w_dtype=moe.W_MXFP8, variant=moe.VARIANT_TILE), moe.MOE_EUNSUPPORTED),
     (dict(K=128), moe.MOE_EUNSUPPORTED),                  # contiguous tiles need K % 256
+    (dict(global_experts=4), moe.MOE_EINVAL),             # fewer global than local experts
+    (dict(global_experts=1 << 31), moe.MOE_EINVAL),
+    (dict(layout=1, max_tokens=64, global_experts=16), moe.MOE_EINVAL),
     (dict(K=128, I=96, layout=1, max_tokens=64), moe.MOE_EUNSUPPORTED),
     (dict(w1_order=moe.W1_INTERLEAVE16, I=72), moe.MOE_EINVAL),
 ])
@@ -97,6 +100,14 @@ def test_plan_validation(kw, code):
         moe.moe_plan_init(moe.make_problem(**base))
     assert ei.value.status == code
     assert str(ei.value)
+
+
+def test_global_experts_topk_range():
+    """With global ids, topk is bounded by the global id space, not by E."""
+    p = moe.moe_plan_init(moe.make_problem(64, 256, 512, 2, topk=8, global_experts=512))
+    assert p.prob.global_experts == 512
+    with pytest.raises(moe.MoeError):
+        moe.moe_plan_init(moe.make_problem(64, 256, 512, 2, topk=8))
 
 
 def test_batched_tile_shapes():

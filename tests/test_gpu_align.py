@@ -17,12 +17,15 @@ from moe_cases import say
 pytestmark = pytest.mark.gpu
 
 
-def run_align(ids: np.ndarray, E: int, variant: int):
+def run_align(ids: np.ndarray, E: int, variant: int, expert_map=None):
     M, topk = ids.shape
-    plan = moe.moe_plan_init(moe.make_problem(M, 256, 512, E, topk=topk, variant=variant))
+    G = 0 if expert_map is None else len(expert_map)
+    plan = moe.moe_plan_init(moe.make_problem(M, 256, 512, E, topk=topk, variant=variant,
+                                              global_experts=G))
     ws13 = torch.full((plan.ws13_bytes,), 0xAB, dtype=torch.uint8, device="cuda")   # poison
     dev = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
-    moe.moe_align_permute(plan, dev, ws13)
+    emap = None if expert_map is None else torch.from_numpy(np.asarray(expert_map, np.int32)).cuda()
+    moe.moe_align_permute(plan, dev, ws13, expert_map=emap)
     torch.cuda.synchronize()
     v = lambda off, n: moe.ws_view(ws13, off, n).cpu().numpy()
     got = {
@@ -37,9 +40,10 @@ def run_align(ids: np.ndarray, E: int, variant: int):
     return plan, got
 
 
-def check(ids, E, variant, label):
-    plan, got = run_align(ids, E, variant)
-    ref = oracle.align_permute(ids, E, plan.block_m)
+def check(ids, E, variant, label, expert_map=None):
+    plan, got = run_align(ids, E, variant, expert_map)
+    local = ids if expert_map is None else oracle.map_expert_ids(ids, expert_map)
+    ref = oracle.align_permute(local, E, plan.block_m)
     say(f"[align] {label}: R={ids.size} E={E} B={plan.block_m} path="
         f"{'multi' if plan.align_blocks else 'single'} post={ref['num_post_padded']}")
     assert plan.sorted_capacity == ref["capacity"] and plan.max_tiles == ref["max_tiles"]
@@ -110,3 +114,18 @@ def test_align_deterministic():
     _, b = run_align(ids, 128, moe.VARIANT_TILE)
     for k in a:
         assert np.array_equal(np.asarray(a[k]), np.asarray(b[k])), k
+
+
+@pytest.mark.parametrize("variant", [moe.VARIANT_TILE, moe.VARIANT_STREAM])
+@pytest.mark.parametrize("M", [300, 3000])
+def test_align_expert_map(M, variant):
+    """Global ids in [0, G) (plus -1 and out-of-range ids) through a map that
+    holds a scrambled subset of the experts, some entries out of range."""
+    rng = np.random.default_rng(M)
+    G, E, topk = 200, 24, 6
+    ids = random_ids(M, M, topk, G, p_skip=0.1, p_bad=0.02)
+    emap = np.full(G, -1, np.int32)
+    held = rng.choice(G, E, replace=False)
+    emap[held] = rng.permutation(E)
+    emap[rng.choice(np.flatnonzero(emap < 0), 3, replace=False)] = [E, E + 5, -7]   # invalid entries
+    check(ids, E, variant, f"expert_map_M{M}", expert_map=emap)

@@ -108,6 +108,51 @@ def test_nullity_and_equivariance():
     say(f"[moe] shuffle bitwise equal: {torch.equal(s.view(torch.int16), base[pt].view(torch.int16))}")
 
 
+def test_expert_map_bf16():
+    """Global ids through an expert map: this GPU is rank 1 of 3 and holds
+    global experts 16..31 as local 0..15; other slots are held elsewhere (or
+    -1 / invalid) and are skipped."""
+    cfg = mi.config(2).scaled(M=600, K=256, I=256, E=16)
+    c = make_case(cfg)
+    rng = np.random.default_rng(21)
+    ids = c.inp.topk_ids
+    gid = (ids + 16 * rng.integers(0, 3, ids.shape)).astype(np.int32)
+    gid[ids < 0] = -1
+    gid[5, 0] = 48                               # outside [0, G): invalid
+    emap = mi.ep_expert_map(48, 16, rank=1)
+    out, plan, ws13, _ = run_contiguous(c, ids=torch.from_numpy(gid).cuda(), expert_map=emap)
+    local = oracle.map_expert_ids(gid, emap)
+    ref = oracle_contiguous(c, np.arange(cfg.M), ids=local)
+    check_close(out, ref, BF16_REL, BF16_ABS, "expert_map bf16")
+    assert int(moe.ws_view(ws13, plan.off_status, 1).cpu()[0]) == 1
+    none = np.flatnonzero((local < 0).all(axis=1))
+    assert none.size and np.all(out[torch.from_numpy(none).cuda()].view(torch.int16).cpu().numpy() == 0)
+
+
+@pytest.mark.parametrize("M", [4160, 4096])
+def test_expert_map_mxfp8_share(M):
+    """The EP16 rank share fed the way an EP implementation receives it:
+    global ids in [0, 512), unmasked weights 1/8, and the rank-0 map."""
+    cfg = mi.config(3).scaled(M=M, K=512, I=256) if M != 4096 else mi.config(3)
+    c = make_case(cfg)
+    emap = mi.ep_expert_map(cfg.global_experts, cfg.E, rank=0)
+    gid = torch.from_numpy(c.inp.global_ids).cuda()
+    gw = torch.from_numpy(c.inp.global_weights).cuda()
+    out, plan, ws13, _ = run_contiguous(c, ids=gid, wts=gw, expert_map=emap)
+    local = oracle.map_expert_ids(c.inp.global_ids, emap)
+    assert np.array_equal(local, c.inp.topk_ids)            # the host-masked form of the recipe
+    if M == 4096:
+        masked, *_ = run_contiguous(c)                       # the host-masked call, same bits
+        assert torch.equal(out.view(torch.int16), masked.view(torch.int16))
+        tokens = sample_tokens(M, 12, seed=5)
+    else:
+        tokens = np.arange(M)
+    ref = oracle_contiguous(c, tokens, ids=local, wts=c.inp.global_weights)
+    check_close(out[torch.from_numpy(tokens).cuda()], ref, MX_REL, 0.0, f"expert_map {cfg.name}")
+    assert int(moe.ws_view(ws13, plan.off_status, 1).cpu()[0]) == 0
+    del c; free()
+
+
 def test_all_slots_skipped():
     cfg = mi.config(0)
     c = make_case(cfg)

@@ -51,6 +51,31 @@ def test_reduce_contiguous():
     assert np.all(out[5].view(torch.int16).cpu().numpy() == 0)          # +0.0
 
 
+def test_reduce_contiguous_expert_map():
+    """Global ids mapped through an expert map: slots of experts held
+    elsewhere (map -1) are skipped like id -1; their y rows are never read."""
+    rng = np.random.default_rng(6)
+    M, topk, K, E, G = 300, 4, 256, 6, 20
+    gid = rng.integers(0, G, (M, topk)).astype(np.int32)
+    gid[rng.random((M, topk)) < 0.1] = -1
+    emap = np.full(G, -1, np.int32)
+    emap[rng.choice(G, E, replace=False)] = rng.permutation(E)
+    local = oracle.map_expert_ids(gid, emap)
+    w = rng.random((M, topk)).astype(np.float32)
+    y = mi.ih4_normal(M * topk * K, 1.0, 98, 9, 2, device="cuda").view(M * topk, K)
+    y[torch.from_numpy((local.reshape(-1) < 0)).cuda()] = float("nan")     # never read
+    plan = moe.moe_plan_init(moe.make_problem(M, K, 512, E, topk=topk, global_experts=G))
+    out = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    moe.moe_topk_reduce_contiguous(plan, y, torch.from_numpy(gid).cuda(), torch.from_numpy(w).cuda(),
+                                   out, expert_map=torch.from_numpy(emap).cuda())
+    torch.cuda.synchronize()
+    yh = np.nan_to_num(oracle.bf16_to_f64(mi.bf16_bits(y)))
+    ref = oracle.topk_reduce_contiguous(yh, local, w, E)
+    absum = oracle.topk_reduce_contiguous(np.abs(yh), local, np.abs(w), E)
+    g = out.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(g - ref) <= bf16_bound(ref, absum))
+
+
 def run_naive_batched(E, T, K, n_out, counts, tok, w, seed):
     y = mi.ih4_normal(E * T * K, 1.0, seed, 9, 1, device="cuda").view(E, T, K)
     invalid = torch.arange(T, device="cuda")[None, :] >= torch.from_numpy(counts).cuda()[:, None]

@@ -101,14 +101,14 @@ def pin_affine_equal_load():
     rows = [l.split() for l in open(os.path.join(GOLDEN, "cake_affine_route_map.txt"))
             if l.strip() and not l.startswith("#")]
     for tokens, topk, n_exp, load in [tuple(int(v) for v in r) for r in rows]:
-        _, _, gid = moe_inputs.routing_affine_ep_share(tokens, topk, n_exp, n_exp)
+        _, _, gid, _ = moe_inputs.routing_affine_ep_share(tokens, topk, n_exp, n_exp)
         got = oracle.align_permute(gid, n_exp, 1)
         assert np.all(got["counts"] == load), (tokens, load)
 
 
 def pin_mxfp8_share_closed_form():
     cfg = moe_inputs.config(3)
-    ids, w, _ = moe_inputs.routing_affine_ep_share(cfg.M, cfg.topk, cfg.global_experts, cfg.E)
+    ids, w, _, _ = moe_inputs.routing_affine_ep_share(cfg.M, cfg.topk, cfg.global_experts, cfg.E)
     got = oracle.align_permute(ids, cfg.E, 16)
     assert np.all(got["counts"] == 64) and got["counts"].sum() == 2048
     per_token = (ids >= 0).sum(axis=1)

@@ -237,9 +237,52 @@ def pin_mxfp8_weights_layer():
     assert not np.array_equal(got, ref)
 
 
+def pin_expert_map_partition():
+    # Expert parallelism with global ids: P ranks each hold a disjoint set of
+    # the G global experts (in a scrambled local order) and see the same
+    # global ids and unmasked weights; the sum of their outputs is the
+    # single-GPU result with every expert local (identity ids).
+    rng = np.random.default_rng(20)
+    G, P = 6, 3
+    x, w1, w2, ids, w = random_problem(rng, M=11, K=16, I=8, E=G, topk=3)
+    ids[2, 1] = -1
+    full = run_oracle(x, w1, w2, ids, w)
+    owner = rng.permutation(G) % P                       # rank of each global expert
+    total = np.zeros_like(full)
+    for r in range(P):
+        held = [int(g) for g in rng.permutation(np.flatnonzero(owner == r))]   # local order
+        emap = np.full(G, -1, np.int32)
+        emap[held] = np.arange(len(held))
+        local = oracle.map_expert_ids(ids, emap)
+        assert np.all((local == -1) | ((local >= 0) & (local < len(held))))
+        total += oracle.moe_contiguous(x, np.arange(11), local, w, len(held),
+                                       lambda e: w1[held[e]], lambda e: w2[held[e]])
+    assert np.allclose(total, full, rtol=1e-12, atol=1e-13)
+
+
+def pin_expert_map_worked_example():
+    # G = 8 global experts, this GPU holds global 5 (local 0) and 0 (local 1);
+    # global 7 maps to 9, outside [0, E=2).  By hand, slot by slot:
+    #   -1 -> skipped;  0 -> local 1;  5 -> local 0;  1 -> held elsewhere
+    #   (skipped, not invalid);  7 -> 9 (invalid);  8 -> outside [0, G)
+    #   (invalid);  -3 -> invalid;  5 -> local 0.
+    emap = np.array([1, -1, -1, -1, -1, 0, -1, 9], np.int32)
+    ids = np.array([[-1, 0, 5, 1], [7, 8, -3, 5]], np.int32)
+    local = oracle.map_expert_ids(ids, emap)
+    got = oracle.align_permute(local, 2, 1)
+    assert got["n_invalid"] == 3
+    assert list(got["counts"]) == [2, 1]                 # local 0: flat 2 and 7; local 1: flat 1
+    assert list(got["sorted_ids"][:3]) == [2, 7, 1]
+    y = np.arange(8, dtype=np.float64)[:, None] + 1.0     # y row of slot (t, j) = t*4 + j + 1
+    wts = np.full((2, 4), 0.5, np.float32)
+    out = oracle.topk_reduce_contiguous(y, local, wts, 2)
+    assert out[0, 0] == 0.5 * (2 + 3) and out[1, 0] == 0.5 * 8
+
+
 PINS = [pin_silu_library, pin_closed_form_selection, pin_dense_swiglu_library,
         pin_dense_mixing_bruteforce, pin_equivariance, pin_nullity_linearity, pin_reduce_contiguous,
-        pin_interleave_layout, pin_batched, pin_mxfp8_weights_layer]
+        pin_interleave_layout, pin_batched, pin_mxfp8_weights_layer, pin_expert_map_partition,
+        pin_expert_map_worked_example]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)

@@ -17,7 +17,8 @@ ALL_PINS = C.PINS + A.PINS + FF.PINS
 
 _orig = {n: getattr(oracle, n) for n in ("split_gate_up", "silu", "expert_ffn", "align_permute",
                                          "mx_scale_exponent", "e4m3fn_encode",
-                                         "topk_reduce_contiguous", "moe_contiguous")}
+                                         "topk_reduce_contiguous", "moe_contiguous",
+                                         "map_expert_ids")}
 
 
 def m_swap_gate_up(w1, order):
@@ -89,12 +90,29 @@ def m_moe_ignores_weights(x_rows, tokens, ids, w, E, w1_of, w2_of, order="halves
     return _orig["moe_contiguous"](x_rows, tokens, ids, np.ones_like(w), E, w1_of, w2_of, order)
 
 
+def m_map_ignored(ids, emap):
+    return np.asarray(ids, np.int32)                     # global ids used as local ones
+
+
+def m_map_remote_invalid(ids, emap):
+    out = _orig["map_expert_ids"](ids, emap)
+    return np.where((out == -1) & (np.asarray(ids) != -1), -2, out).astype(np.int32)
+
+
+def m_map_out_of_range_kept(ids, emap):
+    ids = np.asarray(ids, np.int64)
+    out = _orig["map_expert_ids"](np.where(ids >= len(emap), -1, ids), emap)
+    return out                                           # ids past G silently skipped
+
+
 MUTATIONS = [
     ("split_gate_up", m_swap_gate_up), ("split_gate_up", m_interleave_up_first),
     ("silu", m_silu_sign), ("expert_ffn", m_ffn_no_act), ("expert_ffn", m_ffn_w2_transposed),
     ("align_permute", m_align_descending), ("align_permute", m_align_no_padding),
     ("mx_scale_exponent", m_scale_floor), ("e4m3fn_encode", m_encode_ties_away),
     ("topk_reduce_contiguous", m_reduce_reads_skipped), ("moe_contiguous", m_moe_ignores_weights),
+    ("map_expert_ids", m_map_ignored), ("map_expert_ids", m_map_remote_invalid),
+    ("map_expert_ids", m_map_out_of_range_kept),
 ]
 
 
