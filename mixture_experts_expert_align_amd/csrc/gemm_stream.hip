@@ -174,11 +174,11 @@ __global__ void __launch_bounds__(64 * KS) gemm_stream_bf16_kernel(GemmArgs g) {
 // a chunk).  The tokens' codes and scales are staged in LDS a chunk of CS
 // steps at a time (two buffers), by buffer loads that write LDS directly, so
 // staging costs no registers and the waves meet at a barrier once per chunk.
-// The compiler does not track those loads: the wait before each chunk's
-// barrier is explicit, counted from the fixed issue order (a chunk issues a
-// scale-group load, then in each step the 2 weight loads of the step CS
-// ahead; the chunk after next
-// is staged right after the barrier; weight scales come 16 steps to a load).
+// The compiler does not track those loads, so the wait before each chunk's
+// barrier is explicit, counted from a fixed issue order: a chunk issues one
+// weight-scale load (a 16-step group), then in each step the 2 weight loads
+// of the step CS ahead, and after its barrier the CS + 1 staging loads of the
+// chunk after next.
 //   kGateUp: wave w holds the gate (w even) or up (w odd) rows of features
 //            f0 + 16 (w / 2) .. +15; z = silu(gate) * up per token, quantised
 //            per 32 features (one MX block = waves 4b .. 4b+3) in the
