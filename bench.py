@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="decode",
                     help="tiny | decode | prefill | mxfp8 | batched (or a full workload name)")
+    ap.add_argument("--variant", default="auto", choices=["auto", "tile", "stream", "fused"],
+                    help="kernel family (auto: the plan's choice); fused: one launch for align, "
+                         "W1 and W2, then the reduce, timed as one stage")
     ap.add_argument("--cpu-sample", type=int, default=0,
                     help="tokens (or batched rows) the CPU oracle is timed on (0: per-workload default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -106,7 +109,7 @@ def counter_values(path: str, counter: str, kernel_substr: str):
 
 def traffic_from(args):
     import numpy as np
-    cfg_name = args.config.split("_")[0]
+    cfg_name = args.config.split("_")[0] + ("" if args.variant == "auto" else "_" + args.variant)
     kerns = DOMINANT_KERNEL[cfg_name]
     # per kernel of the timed stage: the median over its dispatches; the
     # stage's traffic is the sum over its kernels
@@ -140,12 +143,17 @@ COPY_LAUNCHES = 3
 # stage (gate_up_act) for the contiguous format (for MXFP8 weights it also
 # quantises the gathered activation rows), both GEMMs (apply_batched) for
 # the batched format.
-DOMINANT_KERNEL = {"tiny": ["gemm_tile_bf16_kernel<0,"], "decode": ["gemm_stream_bf16_kernel<0,"],
+# traffic records: keyed by workload, or workload_variant for a forced variant
+FUSED_KERNELS = ["fused_stream_bf16_kernel", "reduce_contiguous_kernel"]
+FUSED_FILES = ["fused.hip", "stream_bf16.h", "align_device.h", "reduce_codec.hip"]
+DOMINANT_KERNEL = {"tiny": FUSED_KERNELS, "decode": ["gemm_stream_bf16_kernel<0,"],
                    "prefill": ["gemm_tile_bf16_kernel<0,"],
                    "mxfp8": ["quantize_gather_kernel", "gemm_stream_mxfp8_kernel<0,"],
-                   "batched": ["gemm_tile_bf16_kernel<0,", "gemm_tile_bf16_kernel<1,"]}
-KERNEL_FILES = {"tiny": ["gemm_tile.hip"], "decode": ["gemm_stream.hip"], "prefill": ["gemm_tile.hip"],
-                "mxfp8": ["reduce_codec.hip", "gemm_stream.hip"], "batched": ["gemm_tile.hip"]}
+                   "batched": ["gemm_tile_bf16_kernel<0,", "gemm_tile_bf16_kernel<1,"],
+                   "decode_fused": FUSED_KERNELS, "tiny_fused": FUSED_KERNELS}
+KERNEL_FILES = {"tiny": FUSED_FILES, "decode": ["gemm_stream.hip", "stream_bf16.h"],
+                "prefill": ["gemm_tile.hip"], "mxfp8": ["reduce_codec.hip", "gemm_mxfp8.hip"],
+                "batched": ["gemm_tile.hip"], "decode_fused": FUSED_FILES, "tiny_fused": FUSED_FILES}
 
 
 def main():
@@ -196,7 +204,9 @@ def main():
     prob = moe.make_problem(cfg.M, cfg.K, cfg.I, cfg.E, topk=cfg.topk, max_tokens=cfg.max_tokens,
                             layout=0 if contiguous else 1, w_dtype=0 if cfg.w_dtype == "bf16" else 1,
                             w1_order=0 if cfg.w1_order == "halves" else 1,
-                            global_experts=cfg.global_experts if ep_share else 0)
+                            global_experts=cfg.global_experts if ep_share else 0,
+                            variant={"auto": moe.VARIANT_AUTO, "tile": moe.VARIANT_TILE,
+                                     "stream": moe.VARIANT_STREAM, "fused": moe.VARIANT_FUSED}[args.variant])
     plan = moe.moe_plan_init(prob)
     ws13, ws2 = moe.allocate_workspaces(plan)
     stream = torch.cuda.current_stream()
@@ -217,8 +227,17 @@ def main():
         active = np.unique(inp.topk_ids[valid])
         n_tok_read = int(valid.any(axis=1).sum())
         stages = ["align", "gate_up_act", "down_unpermute", "reduce"]
+        fused = plan.variant == moe.VARIANT_FUSED
+        if fused:
+            stages = ["apply"]
 
         def step(ev):
+            if fused:   # the two launches of the single-launch variant, one stage
+                ev[0].record(stream)
+                moe.moe_apply_contiguous(plan, inp.x, ids, wts, w1, w2, out, ws13, ws2, w1_scale,
+                                         w2_scale, stream, expert_map=emap)
+                ev[1].record(stream)
+                return
             ev[0].record(stream)
             moe.moe_align_permute(plan, ids, ws13, stream, expert_map=emap)
             ev[1].record(stream)
@@ -262,6 +281,20 @@ def main():
     stage_ms = {s: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in events]))
                 for i, s in enumerate(stages)}
     ms_per_step = elapsed * 1e3 / args.steps
+    step_ev = [ev[0].elapsed_time(ev[-1]) for ev in events]
+
+    # the same steps with L2 and the Infinity Cache flushed before each (a
+    # 512 MiB fill between steps, outside each step's event pair): the cold
+    # figure for workloads whose weights would otherwise stay cached
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = [mk() for _ in range(args.steps)]
+    for k in range(args.steps):
+        flush.fill_(k & 0xFF)
+        step(cold[k])
+    torch.cuda.synchronize()
+    cold_ev = [ev[0].elapsed_time(ev[-1]) for ev in cold]
+    del flush
+    pct = lambda v: {f"p{q}": round(float(np.percentile(v, q)), 4) for q in (10, 50, 90)}
     tokens = cfg.M
     value = tokens * args.steps / elapsed
 
@@ -274,7 +307,14 @@ def main():
     else:
         wbytes = 2.0
         dtype_name = "bf16"
-    if contiguous:
+    if contiguous and "apply" in stage_ms:
+        # the whole layer in one stage: both weight sets, x rows read once,
+        # out written once (intermediates are the implementation's overhead)
+        dom = "apply"
+        t_dom = stage_ms[dom] * 1e-3
+        alg_bytes = n_act * 3 * I * K * wbytes + n_tok_read * K * 2 + cfg.M * K * 2
+        alg_flops = 6.0 * n_routes * K * I
+    elif contiguous:
         dom = "gate_up_act"
         t_dom = stage_ms[dom] * 1e-3
         w1_bytes = n_act * 2 * I * K * wbytes
@@ -298,7 +338,8 @@ def main():
     roof["kernel"] = dom
     roof["kernel_ms"] = round(stage_ms[dom], 4)
     roof["algorithmic_per_launch"] = {"bytes": int(alg_bytes), "flops": int(alg_flops)}
-    roof["traffic"] = traffic_record(cfg.name.split("_")[0], KERNEL_FILES[cfg.name.split("_")[0]])
+    tkey = cfg.name.split("_")[0] + ("" if args.variant == "auto" else "_" + args.variant)
+    roof["traffic"] = traffic_record(tkey, KERNEL_FILES[tkey]) if tkey in KERNEL_FILES else None
 
     # ---- CPU oracle on a bounded sample of the same workload
     cpu = None
@@ -316,6 +357,8 @@ def main():
                    "active_experts": n_act, "variant": plan.reason.decode(),
                    "global_experts": int(plan.prob.global_experts)},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "step_event_ms": pct(step_ev),
+        "step_event_ms_cache_flushed": pct(cold_ev),
         "step_weight_GBps": round(step_gbs, 1),
         "step_TFLOPs": round(6.0 * n_routes * K * I / (ms_per_step * 1e-3) / 1e12, 3),
         "roofline": roof,

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 /* Status codes. */
 enum {
@@ -75,9 +75,20 @@ enum {
 enum {
   MOE_VARIANT_AUTO = -1,
   MOE_VARIANT_TILE = 0,     /* LDS-tiled grouped GEMM: both operands staged     */
-  MOE_VARIANT_STREAM = 1    /* few rows per expert: weight rows streamed from
+  MOE_VARIANT_STREAM = 1,   /* few rows per expert: weight rows streamed from
                                HBM straight into the MFMA row operand, the few
                                token rows in the other operand                  */
+  /* the streaming path of moe_apply_contiguous in two launches: one kernel
+   * runs the permute, W1 + SiLU-and-mul and W2 + unpermute as work items
+   * taken from a device ticket counter (a W2 item waits for its expert's W1
+   * items), then the ordered reduce (page "Cake MegaMoE EP16 backend for
+   * BF16 activations and MXFP8 weights", section 4: one model kernel plus one
+   * ordered top-k reduce per run).  bf16 weights, contiguous format,
+   * M*topk <= 8192, E <= 2048; same results, bit for bit, as
+   * MOE_VARIANT_STREAM.  AUTO picks it for small layers (all weights within
+   * 1 GiB, at most 32 routes per expert).  The stage entry points run the
+   * two-launch streaming kernels on such a plan. */
+  MOE_VARIANT_FUSED = 2
 };
 
 /* Which TopKWeightAndReduce the caller's finalize must apply (page "Fused MoE
@@ -130,7 +141,7 @@ typedef struct moe_weights {
 typedef struct moe_plan {
   moe_problem prob;
   int32_t abi_version;
-  int32_t variant;         /* MOE_VARIANT_TILE or MOE_VARIANT_STREAM          */
+  int32_t variant;         /* MOE_VARIANT_TILE, _STREAM or _FUSED             */
   int32_t block_m;         /* align tile size B: expert runs padded to it     */
   int32_t reduce_kind;     /* MOE_REDUCE_*                                    */
   int64_t routes;          /* R: M*topk (contiguous) or E*max_tokens (batched)*/
@@ -149,7 +160,10 @@ typedef struct moe_plan {
   int64_t off_num_post_padded; /* [1] offsets[E]                              */
   int64_t off_active;      /* [max_active+1] experts with routes, ascending;
                               element max_active holds their number            */
-  int64_t off_status;      /* [4] [0]: ids outside {-1} U [0,E) seen          */
+  int64_t off_status;      /* [4] [0]: ids outside {-1} U [0,E) seen;
+                              [1] (MOE_VARIANT_FUSED): waits that timed out,
+                              summed over calls (non-zero: the outputs of
+                              some call are undefined)                         */
   int64_t off_align_scratch; /* per-block histograms of the multi-block path  */
   int64_t off_z;           /* intermediate silu(gate)*up rows, in sorted
                               order: bf16 [sorted_capacity, I], or E4M3
@@ -159,6 +173,15 @@ typedef struct moe_plan {
   int64_t off_xq;          /* MXFP8: E4M3 activations gathered in sorted order
                               [sorted_capacity, K]                              */
   int64_t off_xq_scale;    /* MXFP8: UE8M0 [sorted_capacity, K/32]             */
+  int64_t off_sync;        /* MOE_VARIANT_FUSED: the work queue, int32 words:
+                              counters at 32*i for i < 2 + max_active (ticket,
+                              align published, W1 strips done per slot), then
+                              int4 [max_active] slot records.  The counters
+                              must be zero before the first call on this ws13
+                              (allocate it zero-filled) and are zero again
+                              after every moe_apply_contiguous call; -1 for
+                              other variants.  Calls that share a ws13 must
+                              not overlap.                                     */
   char reason[192];        /* why this variant / why unsupported              */
 } moe_plan;
 

@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "ABI_VERSION", "LAYOUT_CONTIGUOUS", "LAYOUT_BATCHED", "W_BF16", "W_MXFP8", "W1_HALVES",
-    "W1_INTERLEAVE16", "VARIANT_AUTO", "VARIANT_TILE", "VARIANT_STREAM", "REDUCE_NOOP",
+    "W1_INTERLEAVE16", "VARIANT_AUTO", "VARIANT_TILE", "VARIANT_STREAM", "VARIANT_FUSED", "REDUCE_NOOP",
     "REDUCE_CONTIGUOUS", "REDUCE_NAIVE_BATCHED", "MoeError", "MoeProblem", "MoePlan", "MoeWeights",
     "load_library", "library_path", "moe_abi_version", "moe_status_string", "moe_plan_init",
     "moe_plan_reason", "moe_align_permute", "moe_apply_contiguous", "moe_apply_batched",
@@ -25,12 +25,12 @@ __all__ = [
     "moe_quantize_mxfp8", "make_problem", "allocate_workspaces", "ws_view",
 ]
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, 1, 2, 3
 LAYOUT_CONTIGUOUS, LAYOUT_BATCHED = 0, 1
 W_BF16, W_MXFP8 = 0, 1
 W1_HALVES, W1_INTERLEAVE16 = 0, 1
-VARIANT_AUTO, VARIANT_TILE, VARIANT_STREAM = -1, 0, 1
+VARIANT_AUTO, VARIANT_TILE, VARIANT_STREAM, VARIANT_FUSED = -1, 0, 1, 2
 REDUCE_NOOP, REDUCE_CONTIGUOUS, REDUCE_NAIVE_BATCHED = 0, 1, 2
 
 _i64, _i32, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
@@ -50,7 +50,7 @@ class MoePlan(ctypes.Structure):
                 ("off_counts", _i64), ("off_offsets", _i64), ("off_sorted_ids", _i64),
                 ("off_block_expert", _i64), ("off_num_post_padded", _i64), ("off_active", _i64),
                 ("off_status", _i64), ("off_align_scratch", _i64), ("off_z", _i64),
-                ("off_z_scale", _i64), ("off_xq", _i64), ("off_xq_scale", _i64),
+                ("off_z_scale", _i64), ("off_xq", _i64), ("off_xq_scale", _i64), ("off_sync", _i64),
                 ("reason", ctypes.c_char * 192)]
 
 
@@ -169,8 +169,9 @@ def moe_plan_reason(plan: MoePlan) -> str:
 
 
 def allocate_workspaces(plan: MoePlan, device="cuda"):
-    """ws13 and ws2 as uint8 device tensors of the sizes the plan states."""
-    ws13 = torch.empty(max(plan.ws13_bytes, 16), dtype=torch.uint8, device=device)
+    """ws13 and ws2 as uint8 device tensors of the sizes the plan states
+    (ws13 zero-filled: the single-launch variant keeps its counters there)."""
+    ws13 = torch.zeros(max(plan.ws13_bytes, 16), dtype=torch.uint8, device=device)
     ws2 = torch.empty(max(plan.ws2_bytes, 16), dtype=torch.uint8, device=device)
     return ws13, ws2
 

@@ -119,4 +119,9 @@ __device__ __forceinline__ uint32_t e4m3_encode(float v) {
   return code | sign;
 }
 
+// W row index of intermediate feature f (gate, or up when up = true).
+__device__ __forceinline__ int w1_row(int f, bool up, int I, int order) {
+  return order == 0 ? (up ? I + f : f) : (32 * (f >> 4) + (f & 15) + (up ? 16 : 0));
+}
+
 }  // namespace moe

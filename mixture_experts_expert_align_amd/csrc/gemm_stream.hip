@@ -1,13 +1,14 @@
-// Streaming grouped GEMMs for experts that hold few rows (decode batches,
-// and one rank's local-expert share of a large layer).
+// Streaming grouped GEMMs with bf16 weights for experts that hold few rows
+// (decode batches), one launch per matmul; the strip itself is in
+// stream_bf16.h, shared with the single-launch path.
 //
 // With few rows per expert the matmuls are bound by reading the active
 // experts' weights from HBM once.  Each wave owns a strip of weight rows and
 // the whole contraction: the weight rows go from HBM straight into the row
 // operand of the MFMA (16 rows x the contraction slice, each lane reading a
 // contiguous run of one row, no LDS), and the expert's routed tokens sit in
-// the other operand: up to 16 per pass for bf16, read from L2; 64 per pass
-// for MXFP8, staged once per workgroup in LDS and shared by its waves.  The Mixture-of-Experts kernel engineering on SageMaker page ("Swap-AB
+// the other operand, up to 16 per pass, read from L2.  The page
+// "Mixture-of-Experts kernel engineering on SageMaker" ("Swap-AB
 // for WGMMA utilization") swaps A and B so the weight's large N dimension
 // fills Hopper's fixed 64-row slot; on gfx950 both MFMA slots are 16 wide,
 // so what carries over is only that the weight rows occupy the row slot and
@@ -21,399 +22,20 @@
 // Grid: (feature strips, active experts).  The active-expert list comes from
 // the align step, so the grid depends only on the plan; workgroups whose
 // slot is past the number of active experts leave at once.
-#include "device_common.h"
-#include "kernels.h"
+#include "stream_bf16.h"
 
 namespace moe {
 namespace {
 
-constexpr int NT = 256;
-
-__device__ __forceinline__ i32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const i32x4*>(p); }
-
-// W row index of intermediate feature f (gate, or up when up = true).
-__device__ __forceinline__ int w1_row(int f, bool up, int I, int order) {
-  return order == 0 ? (up ? I + f : f) : (32 * (f >> 4) + (f & 15) + (up ? 16 : 0));
-}
-
 // ------------------------------------------------------------------ bf16 --
-// A workgroup owns 16 output features of one expert and KS waves split the
-// contraction into KS equal runs; each wave streams its run of the weight
-// rows with a three-deep register pipeline, the partial sums meet in LDS and
-// wave 0 adds them in wave order (a fixed order, so every run gives the same
-// bits) before the epilogue.  Splitting the contraction keeps each
-// workgroup's task short, so the last wave of workgroups on the chip is short
-// too; with a whole contraction per workgroup the tail of the grid left much
-// of the chip idle.
-//   kGateUp: two 16-row tiles: the gate rows and the matching up rows of the
-//            16 features; epilogue z = silu(gate) * up, bf16, row = position.
-//   kDown:   one 16-row tile of W2; epilogue writes y rows per (token, slot).
-// Per lane and 128-wide step, lane group q takes the four 16-byte pieces at
-// k + 8q + 32j (j = 0..3) of its row: the four groups of one load
-// instruction read 64 contiguous bytes of each of 16 rows.
+// Grid (I or K / 16 feature strips, active-expert slots); KS waves per strip.
 template <int EPI, int KS>
 __global__ void __launch_bounds__(64 * KS) gemm_stream_bf16_kernel(GemmArgs g) {
-  constexpr int NTL = EPI == kEpiGateUp ? 2 : 1;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const RowMap& rm = g.rows;
-  const int slot = blockIdx.y;
-  if (slot >= rm.active[g.max_active]) return;
-  const int e = rm.active[slot];
-  const int cnt = rm.counts[e];
-  const int pos0 = rm.offsets[e];
-  const int K = g.kdim;
-  const int KW = K / KS;                      // contraction run of this wave
-  const int q = lane >> 4;
-  const int l16 = lane & 15;
-  const int kbase = wave * KW + 8 * q;
-  const int f0 = blockIdx.x * 16;
-
-  // Buffer loads: the expert's weights and the activations as two buffer
-  // resources, per-lane 32-bit byte offsets, the step's k in the scalar
-  // offset.  A lane without a token gets an offset past the buffer's size,
-  // which the hardware's range check turns into zeros.
-  const uint16_t* wexp = static_cast<const uint16_t*>(g.w) + (int64_t)e * g.w_expert_stride;
-  const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(wexp, g.w_expert_stride * 2);
-  const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(g.act, g.act_bytes);
-  uint32_t wo[NTL];
-  if (EPI == kEpiGateUp) {
-    wo[0] = (uint32_t)(w1_row(f0 + l16, false, g.I, g.w1_order) * K + kbase) * 2u;
-    wo[NTL - 1] = (uint32_t)(w1_row(f0 + l16, true, g.I, g.w1_order) * K + kbase) * 2u;
-  } else {
-    wo[0] = (uint32_t)((f0 + l16) * K + kbase) * 2u;
-  }
-  uint16_t* out = static_cast<uint16_t*>(g.out);
-  __shared__ f32x4 red[KS][NTL][64];
-  const int nsteps = KW / 128;
-
-  for (int tg = 0; tg * 16 < cnt; ++tg) {
-    const int tk = tg * 16 + l16;
-    const bool tv = tk < cnt;
-    const int pos = pos0 + tk;
-    uint32_t ao = 0x80000000u;               // past the end: loads return 0
-    if (tv) {
-      const int64_t row = EPI == kEpiGateUp ? rm.sorted_ids[pos] / rm.topk : pos;
-      ao = (uint32_t)((row * g.act_ld + kbase) * 2);
-    }
-    f32x4 acc[NTL];
-#pragma unroll
-    for (int t = 0; t < NTL; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    i32x4 a[3][NTL][4], b[3][4];
-    auto load = [&](int st, int k) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int t = 0; t < NTL; ++t)
-          a[st][t][j] = __builtin_amdgcn_raw_buffer_load_b128(wr, wo[t] + 64 * j, 2 * k, 0);
-        b[st][j] = __builtin_amdgcn_raw_buffer_load_b128(ar, ao + 64 * j, 2 * k, 0);
-      }
-    };
-    auto mma = [&](int st) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int t = 0; t < NTL; ++t)
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[st][t][j]), as_bf16x8(b[st][j]),
-                                                           acc[t], 0, 0, 0);
-    };
-    load(0, 0);
-    if (nsteps > 1) load(1, 128);
-    for (int it = 0; it < nsteps; it += 3) {
-      if (it + 2 < nsteps) load(2, 128 * (it + 2));
-      mma(0);
-      if (it + 3 < nsteps) load(0, 128 * (it + 3));
-      if (it + 1 < nsteps) mma(1);
-      if (it + 4 < nsteps) load(1, 128 * (it + 4));
-      if (it + 2 < nsteps) mma(2);
-    }
-
-#pragma unroll
-    for (int t = 0; t < NTL; ++t) red[wave][t][lane] = acc[t];
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-      for (int t = 0; t < NTL; ++t) {
-        f32x4 sum = red[0][t][lane];
-        for (int w = 1; w < KS; ++w) sum += red[w][t][lane];
-        acc[t] = sum;
-      }
-      // acc[t][r]: weight row 4*q + r of tile t, token column l16
-      if (tv) {
-        uint32_t h[4];
-        int64_t o;
-        if (EPI == kEpiGateUp) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(silu_f32(acc[0][r]) * acc[NTL - 1][r]);
-          o = (int64_t)pos * g.out_ld;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(acc[0][r]);
-          o = (int64_t)rm.sorted_ids[pos] * g.out_ld;
-        }
-        *reinterpret_cast<uint2*>(out + o + f0 + 4 * q) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-      }
-    }
-    __syncthreads();
-  }
-}
-
-// ----------------------------------------------------------------- MXFP8 --
-// v_mfma_scale_f32_16x16x128_f8f6f4, one 128-wide contraction step per
-// instruction.  Operand layout (measured on gfx950 with an in-bounds probe of
-// the builtin): in lane l (row l % 16, group g = l / 16) bytes 0-15 hold
-// k = 16g .. 16g+15 and bytes 16-31 hold k = 64+16g .. 64+16g+15, and the
-// lane's scale byte is the scale of the 32-wide k block g.  Read in memory
-// order, a k step therefore needs, per lane, the 16 bytes at k0 + 16g and the
-// 16 at k0 + 64 + 16g, plus the scale of MX block k0/32 + g: each MX block
-// of the weight and activation rows lines up with exactly one scale.
-//
-// A workgroup of 8 waves owns 128 weight rows of one expert, 16 per wave, and
-// the expert's routed tokens, 64 per pass.  Weights stream from HBM straight
-// into registers, CS 128-wide steps ahead (CS register sets, one per step of
-// a chunk).  The tokens' codes and scales are staged in LDS a chunk of CS
-// steps at a time (two buffers), by buffer loads that write LDS directly, so
-// staging costs no registers and the waves meet at a barrier once per chunk.
-// The compiler does not track those loads, so the wait before each chunk's
-// barrier is explicit, counted from a fixed issue order: a chunk issues one
-// weight-scale load (a 16-step group), then in each step the 2 weight loads
-// of the step CS ahead, and after its barrier the CS + 1 staging loads of the
-// chunk after next.
-//   kGateUp: wave w holds the gate (w even) or up (w odd) rows of features
-//            f0 + 16 (w / 2) .. +15; z = silu(gate) * up per token, quantised
-//            per 32 features (one MX block = waves 4b .. 4b+3) in the
-//            epilogue, which gathers the tiles in LDS.
-//   kDown:   wave w holds rows f0 + 16 w .. +15 and writes them as bf16 y rows
-//            per (token, slot) straight from its accumulators.
-constexpr int kMxTok = 64;                       // tokens per pass
-constexpr int kMxWaves = 8;
-constexpr int kMxStepA = kMxTok * 128;           // token code bytes per step
-constexpr int kMxStepAS = kMxTok * 4;            // token scale bytes per step (one wave's slot)
-
-typedef __attribute__((address_space(3))) void lds_void;
-__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint8_t* dst, uint32_t vo, int so) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, vo, so, 0, 0);
-}
-__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, uint8_t* dst, uint32_t vo, int so) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, vo, so, 0, 0);
-}
-// Keeps every instruction on its side: the explicit vmcnt waits below count
-// loads in program order, so neither the compiler's IR passes (memory
-// clobber) nor its scheduler may move a load across one of these.
-__device__ __forceinline__ void issue_order() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding: vmcnt
-// in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xf00);
-  asm volatile("" ::: "memory");
-}
-
-// CS: steps per chunk (4, 2 or 1, dividing the contraction's step count);
-// the weights stream CS steps ahead.
-template <int EPI, int CS>
-__global__ void __launch_bounds__(64 * kMxWaves, 4) gemm_stream_mxfp8_kernel(GemmArgs g) {
-  constexpr int kChunk = CS * kMxStepA + kMxWaves * kMxStepAS;   // one LDS buffer
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const RowMap& rm = g.rows;
-  const int slot = blockIdx.y;
-  if (slot >= rm.active[g.max_active]) return;
-  const int e = rm.active[slot];
-  const int cnt = rm.counts[e];
-  const int pos0 = rm.offsets[e];
-  const int K = g.kdim;
-  const int KB = K / 32;
-  const int q = lane >> 4;
-  const int l16 = lane & 15;
-  const int f0 = blockIdx.x * (EPI == kEpiGateUp ? 64 : 128);
-  const int nsteps = K / 128;
-  const int nchunks = nsteps / CS;
-
-  const uint8_t* wexp = static_cast<const uint8_t*>(g.w) + (int64_t)e * g.w_expert_stride;
-  const uint8_t* wsexp = g.w_scale + (int64_t)e * (g.w_expert_stride / 32);
-  const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(wexp, g.w_expert_stride);
-  const __amdgpu_buffer_rsrc_t wsr = buffer_rsrc(wsexp, g.w_expert_stride / 32);
-  const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(g.act, g.act_bytes);
-  const __amdgpu_buffer_rsrc_t asr = buffer_rsrc(g.act_scale, g.act_bytes / 32);
-  const int row = EPI == kEpiGateUp ? w1_row(f0 + 16 * (wave >> 1) + l16, (wave & 1) != 0, g.I, g.w1_order)
-                                    : f0 + 16 * wave + l16;
-  const uint32_t wo = (uint32_t)(row * K + 16 * q);     // lane: row l16, bytes 16q of a step (+64)
-  // weight scales, 16 steps at a time: lane (row l16, group q) loads the 4
-  // words of steps 4q .. 4q+3 of a 16-step group (16 bytes), and each step
-  // takes its word from the lane that holds it (one load per chunk instead
-  // of one per step: every load instruction costs the address unit 64 lane
-  // requests, whatever its width)
-  const uint32_t wso = (uint32_t)(row * KB + 16 * q);
-  const int ngroups = (nsteps + 15) / 16;
-
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2 * kChunk];
-  // within a buffer: step sub's codes at sub * kMxStepA, laid out [token tile
-  // c][half j][lane] (1 KB blocks: lane i holds token 16c + i % 16, bytes
-  // 64j + 16 (i / 16) of the step), then one 256-byte slot per wave: wave w
-  // loads the scale words of all 64 tokens for step w % CS (waves past CS
-  // load copies, so every wave issues the same loads and none is masked)
-
-  for (int tg = 0; tg * kMxTok < cnt; ++tg) {
-    // this wave stages block (c, j) = (wave / 2, wave % 2) of every step and
-    // the scale words of step wave % CS; past the count: zeros
-    const int tk = tg * kMxTok + 16 * (wave >> 1) + l16;
-    const uint32_t xo = tk < cnt ? (uint32_t)((int64_t)(pos0 + tk) * g.act_ld + 64 * (wave & 1) + 16 * q) : 0x80000000u;
-    const int ts = tg * kMxTok + lane;
-    const uint32_t xso = ts < cnt ? (uint32_t)((int64_t)(pos0 + ts) * (g.act_ld / 32)) : 0x80000000u;
-    const int ssub = wave % CS;
-    // CS + 1 loads per wave: chunk ch into buffer buf
-    auto stage = [&](int ch, int buf) {
-      uint8_t* base = sA + buf * kChunk;
-#pragma unroll
-      for (int sub = 0; sub < CS; ++sub)
-        lds_load16(ar, base + sub * kMxStepA + wave * 1024, xo, (ch * CS + sub) * 128);
-      lds_load4(asr, base + CS * kMxStepA + wave * kMxStepAS, xso, (ch * CS + ssub) * 4);
-    };
-    // 2 loads: the weights of step st into register set i
-    i32x8 wa[CS];
-    auto wload = [&](int i, int st) {
-      const int k = st * 128;
-      const i32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(wr, wo, k, 0);
-      const i32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(wr, wo + 64, k, 0);
-      wa[i] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    };
-    // 1 load: the scale words of 16-step group gi (past the end: the last)
-    auto sload = [&](int gi) {
-      return __builtin_amdgcn_raw_buffer_load_b128(wsr, wso, 64 * min(gi, ngroups - 1), 0);
-    };
-    i32x4 scur, snext;   // the current chunk's group, the next chunk's
-    f32x4 acc[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    auto mma = [&](int i, int buf, int sub, int st) {
-      const uint8_t* base = sA + buf * kChunk;
-      // step st is word st % 4 of the lanes of group q = (st % 16) / 4
-      const int w4 = st & 3;
-      const int word = w4 == 0 ? scur[0] : w4 == 1 ? scur[1] : w4 == 2 ? scur[2] : scur[3];
-      const uint32_t wsw = (uint32_t)__shfl(word, l16 + 16 * ((st & 15) >> 2));
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const i32x4 xl = *reinterpret_cast<const i32x4*>(base + sub * kMxStepA + (2 * c) * 1024 + 16 * lane);
-        const i32x4 xh = *reinterpret_cast<const i32x4*>(base + sub * kMxStepA + (2 * c + 1) * 1024 + 16 * lane);
-        const i32x8 xb = (i32x8){xl[0], xl[1], xl[2], xl[3], xh[0], xh[1], xh[2], xh[3]};
-        const uint32_t xsw =   // wave sub's slot holds step sub
-            *reinterpret_cast<const uint32_t*>(base + CS * kMxStepA + sub * kMxStepAS + 4 * (16 * c + l16));
-        acc[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa[i], xb, acc[c], 0, 0, 0,
-                                                                 (int)(wsw >> (8 * q)), 0, (int)(xsw >> (8 * q)));
-      }
-    };
-    // the CS steps of chunk ch (LDS buffer buf): multiply step s, then load
-    // the weights of step s + CS into the freed register set (past the end:
-    // the last step again, unused)
-    auto chunk = [&](int ch, int buf) {
-      scur = snext;                                   // loaded a chunk ago
-      snext = sload(((ch + 1) * CS) / 16);
-      issue_order();
-#pragma unroll
-      for (int sub = 0; sub < CS; ++sub) {
-        mma(sub, buf, sub, ch * CS + sub);
-        wload(sub, min((ch + 1) * CS + sub, nsteps - 1));
-        // also: one step's token fragments live at a time
-        issue_order();
-      }
-    };
-
-    // prologue: chunk 0 staged, the weights of steps 0 .. CS-1 loaded, chunk 1
-    // staged (the loop's issue order: weights, then the next staging)
-    stage(0, 0);
-    issue_order();
-    snext = sload(0);
-    issue_order();
-#pragma unroll
-    for (int sub = 0; sub < CS; ++sub) {
-      wload(sub, min(sub, nsteps - 1));
-      issue_order();
-    }
-    stage(min(1, nchunks - 1), 1);
-    issue_order();
-    // chunk 0's loads are older than the scale group's (1), the weights' (2 CS)
-    // and chunk 1's (CS + 1)
-    wait_vm<3 * CS + 2>();
-    lds_barrier();
-    for (int ch = 0; ch + 1 < nchunks; ++ch) {
-      const int buf = ch & 1;
-      chunk(ch, buf);
-      // chunk ch+1's staging loads are older than the scale group and the 2 CS
-      // weight loads of this chunk; then every wave's share is in place and
-      // chunk ch is read
-      wait_vm<2 * CS + 1>();
-      lds_barrier();
-      stage(min(ch + 2, nchunks - 1), buf);   // past the end: reloads the last chunk, unused
-      issue_order();
-    }
-    chunk(nchunks - 1, (nchunks - 1) & 1);
-    // drain the remaining (unused) loads before LDS is reused
-    wait_vm<0>();
-    lds_barrier();
-
-    // acc[c][r]: weight row 4*q + r of this wave's tile, token tg*64 + 16*c + l16
-    if (EPI == kEpiGateUp) {
-      f32x4* sOut = reinterpret_cast<f32x4*>(sA);      // [wave][token tile][lane]
-#pragma unroll
-      for (int c = 0; c < 4; ++c) sOut[(wave * 4 + c) * 64 + lane] = acc[c];
-      lds_barrier();
-      // wave w finishes token tile c = w % 4 of MX block b = w / 4 (features
-      // f0 + 32 b .. +31: gate/up tiles of waves 4b .. 4b+3)
-      const int c = wave & 3, b = wave >> 2;
-      const f32x4 g0 = sOut[((4 * b + 0) * 4 + c) * 64 + lane], u0 = sOut[((4 * b + 1) * 4 + c) * 64 + lane];
-      const f32x4 g1 = sOut[((4 * b + 2) * 4 + c) * 64 + lane], u1 = sOut[((4 * b + 3) * 4 + c) * 64 + lane];
-      float z[8];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        z[r] = silu_f32(g0[r]) * u0[r];
-        z[4 + r] = silu_f32(g1[r]) * u1[r];
-      }
-      float m = 0.f;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) m = fmaxf(m, fabsf(z[r]));
-      // the 32 features of a token live in lanes l16, l16+16, l16+32, l16+48
-      m = fmaxf(m, __shfl_xor(m, 16));
-      m = fmaxf(m, __shfl_xor(m, 32));
-      const uint32_t sc = mx_scale_code(m);
-      const float inv = mx_inv_scale(sc);
-      uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        w0 |= e4m3_encode(z[r] * inv) << (8 * r);
-        w1 |= e4m3_encode(z[4 + r] * inv) << (8 * r);
-      }
-      const int t = tg * kMxTok + 16 * c + l16;
-      if (t < cnt) {
-        const int64_t pos = pos0 + t;
-        uint8_t* o = static_cast<uint8_t*>(g.out) + pos * g.out_ld;
-        const int fb = f0 + 32 * b;
-        *reinterpret_cast<uint32_t*>(o + fb + 4 * q) = w0;
-        *reinterpret_cast<uint32_t*>(o + fb + 16 + 4 * q) = w1;
-        if (q == 0) g.out_scale[pos * (g.out_ld / 32) + fb / 32] = (uint8_t)sc;
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int t = tg * kMxTok + 16 * c + l16;
-        if (t < cnt) {
-          const int64_t orow = rm.sorted_ids[pos0 + t];
-          uint16_t* o = static_cast<uint16_t*>(g.out) + orow * g.out_ld + f0 + 16 * wave + 4 * q;
-          uint32_t h[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(acc[c][r]);
-          *reinterpret_cast<uint2*>(o) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-        }
-      }
-    }
-    lds_barrier();
-  }
+  __shared__ f32x4 red[KS * (EPI == kEpiGateUp ? 2 : 1) * 64];
+  SlotRows sr;
+  if (!slot_rows<false>(g, blockIdx.y, sr)) return;
+  const int32_t* sid = g.rows.sorted_ids + sr.pos0;
+  stream_bf16_strip<EPI>(g, sr, [&](int tk) { return sid[tk]; }, blockIdx.x * 16, threadIdx.x >> 6, KS, red);
 }
 
 }  // namespace
@@ -438,25 +60,6 @@ static hipError_t launch_stream_bf16(const GemmArgs& g, hipStream_t s, int max_k
 hipError_t launch_gemm_stream_bf16(const GemmArgs& g, hipStream_t s) {
   return g.epi == kEpiGateUp ? launch_stream_bf16<kEpiGateUp>(g, s, 4)
                              : launch_stream_bf16<kEpiDown>(g, s, 8);
-}
-
-template <int EPI>
-static hipError_t launch_mxfp8(const GemmArgs& g, hipStream_t s) {
-  const dim3 grid(g.nfeat / (EPI == kEpiGateUp ? 64 : 128), (unsigned)g.max_active);
-  const int nsteps = g.kdim / 128;
-  // W2 keeps chunks of 2 steps: with 4 its epilogue's registers no longer
-  // fit the 128 that let two workgroups share a CU
-  if (EPI == kEpiGateUp && nsteps % 4 == 0)
-    hipLaunchKernelGGL((gemm_stream_mxfp8_kernel<kEpiGateUp, 4>), grid, dim3(64 * kMxWaves), 0, s, g);
-  else if (nsteps % 2 == 0)
-    hipLaunchKernelGGL((gemm_stream_mxfp8_kernel<EPI, 2>), grid, dim3(64 * kMxWaves), 0, s, g);
-  else
-    hipLaunchKernelGGL((gemm_stream_mxfp8_kernel<EPI, 1>), grid, dim3(64 * kMxWaves), 0, s, g);
-  return hipGetLastError();
-}
-
-hipError_t launch_gemm_stream_mxfp8(const GemmArgs& g, hipStream_t s) {
-  return g.epi == kEpiGateUp ? launch_mxfp8<kEpiGateUp>(g, s) : launch_mxfp8<kEpiDown>(g, s);
 }
 
 }  // namespace moe

@@ -39,8 +39,15 @@ struct AlignArgs {
   int32_t sentinel;
   int32_t nblocks;             // 0: single-block path; else chunks (<= kAlignMaxBlocks)
   int32_t chunk;               // set by launch_align: keys per chunk
-  int32_t nbits;               // set by launch_align: bits of a bucket index
+  int32_t nbits;               // set by align_key_bits: bits of a bucket index
 };
+
+// Bits a bucket index in [0, nb) needs (the scatter's per-bit ballots).
+inline int32_t align_key_bits(int32_t nb) {
+  int32_t n = 0;
+  while ((1 << n) < nb) ++n;
+  return n;
+}
 
 constexpr int kAlignSmallMaxR = 8192;    // single-workgroup path up to this R
 constexpr int kAlignChunk = 1024;        // keys per workgroup in the multi-block path (at least)
@@ -98,12 +105,47 @@ hipError_t launch_gemm_tile_bf16(const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_stream_bf16(const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_stream_mxfp8(const GemmArgs& g, hipStream_t s);
 
+// -------------------------------------------------------- single launch ----
+// Align, W1 + SiLU-and-mul and W2 + unpermute of the bf16 streaming path in
+// one launch (work items taken from a device ticket counter; see fused.hip).
+constexpr int kFusedMaxExperts = 2048;   // the align's bucket arrays live in LDS
+// The sync area, in int32 words: one 128-byte line per counter (they are
+// polled and incremented by different workgroups at once) — [0] ticket,
+// [32] align published, [64 + 32 s] W1 strips published for slot s — then
+// one record per slot, int4 {expert, rows, first position, 1}, or zeros for
+// a slot past the active experts (written by the align).  The counters are
+// zero before the first call and the reduce that follows each call zeroes
+// them again.
+constexpr int kSyncLine = 32;
+enum { kSyncTicket = 0, kSyncAligned = kSyncLine, kSyncSlots = 2 * kSyncLine };
+__host__ __device__ inline int64_t sync_counter_lines(int64_t max_active) { return 2 + max_active; }
+__host__ __device__ inline int64_t sync_words(int64_t max_active) { return kSyncLine * sync_counter_lines(max_active) + 4 * max_active; }
+
+struct FusedArgs {
+  AlignArgs align;             // single-workgroup align (nblocks 0)
+  GemmArgs w1, w2;             // as for the two streaming launches
+  int32_t* sync;               // [sync_words(max_active)]
+  int64_t max_active;
+  // set by the launcher
+  int32_t ks1, ks2;            // waves per W1 / W2 strip
+  int32_t ns1, ns2;            // strips per workgroup
+  int32_t p1, p2;              // strips per slot
+  int32_t c1, c2;              // strips per ticket
+  int64_t n1c, n2c;            // W1 / W2 tickets
+  int64_t nitems;              // workgroups of the launch
+};
+
+hipError_t launch_fused_stream_bf16(FusedArgs f, hipStream_t s);
+
 // --------------------------------------------------------------- reduce ----
 // out[t] = sum over slots j (ascending) whose id (mapped through expert_map
 // when given: ids in [0, G)) is a local expert in [0, E) of w[t,j] * y[t*topk+j]
+// sync_zero (optional): word 32 i is zeroed for i < sync_lines (the
+// single-launch path's counters, for the next call).
 hipError_t launch_reduce_contiguous(const uint16_t* y, const int32_t* ids, const float* w,
                                     const int32_t* expert_map, int32_t G, uint16_t* out, int64_t M,
-                                    int32_t topk, int64_t K, int32_t E, hipStream_t s);
+                                    int32_t topk, int64_t K, int32_t E, int32_t* sync_zero,
+                                    int64_t sync_lines, hipStream_t s);
 // out[t] = sum over CSR list of t (ascending) of w[row] * y[row]
 hipError_t launch_reduce_csr(const uint16_t* y, const float* w, const int32_t* offsets,
                              const int32_t* rows, uint16_t* out, int64_t n_out, int64_t K,

@@ -112,7 +112,7 @@ int moe_plan_init(moe_plan* plan, const moe_problem* prob) {
     return fail(plan, MOE_EINVAL, "unknown weight dtype");
   if (P.w1_order != MOE_W1_HALVES && P.w1_order != MOE_W1_INTERLEAVE16)
     return fail(plan, MOE_EINVAL, "unknown W1 row order");
-  if (P.variant < MOE_VARIANT_AUTO || P.variant > MOE_VARIANT_STREAM)
+  if (P.variant < MOE_VARIANT_AUTO || P.variant > MOE_VARIANT_FUSED)
     return fail(plan, MOE_EINVAL, "unknown variant");
   const bool contiguous = P.layout == MOE_LAYOUT_CONTIGUOUS;
   if (contiguous) {
@@ -137,8 +137,8 @@ int moe_plan_init(moe_plan* plan, const moe_problem* prob) {
   if (P.w_dtype == MOE_W_MXFP8) {
     if (!contiguous)
       return fail(plan, MOE_EUNSUPPORTED, "MXFP8 weights are built for the contiguous format only");
-    if (variant == MOE_VARIANT_TILE)
-      return fail(plan, MOE_EUNSUPPORTED, "MXFP8 weights have only the streaming kernels");
+    if (variant == MOE_VARIANT_TILE || variant == MOE_VARIANT_FUSED)
+      return fail(plan, MOE_EUNSUPPORTED, "MXFP8 weights have only the two-launch streaming kernels");
     if (P.K % 128 || P.I % 128)
       return fail(plan, MOE_EUNSUPPORTED, "MXFP8 kernels need K % 128 == 0 and I % 128 == 0");
     if (2 * P.I * P.K >= (1ll << 31))
@@ -147,16 +147,35 @@ int moe_plan_init(moe_plan* plan, const moe_problem* prob) {
     snprintf(plan->reason, sizeof(plan->reason),
              "stream (MXFP8): weight rows streamed into scaled MFMA, 64 tokens per pass");
   } else {
-    if (variant == MOE_VARIANT_AUTO) variant = (contiguous && P.M <= 16) ? MOE_VARIANT_STREAM : MOE_VARIANT_TILE;
-    if (variant == MOE_VARIANT_STREAM) {
+    if (variant == MOE_VARIANT_AUTO) {
+      // small layers (all weights within 1 GiB, at most 32 rows per expert
+      // that can hold a route, one-workgroup align): one launch plus the
+      // reduce, where launch latency is most of the time; few rows per
+      // expert: the two streaming launches; otherwise the tiles
+      const int64_t slots = P.E < R ? P.E : R;
+      const bool small = 6 * P.E * P.I * P.K <= (1ll << 30) && R <= 32 * slots && R <= kAlignSmallMaxR &&
+                         P.E <= kFusedMaxExperts && P.K % 128 == 0 && P.I % 128 == 0;
+      variant = !contiguous ? MOE_VARIANT_TILE
+                : small     ? MOE_VARIANT_FUSED
+                : P.M <= 16 ? MOE_VARIANT_STREAM
+                            : MOE_VARIANT_TILE;
+    }
+    if (variant == MOE_VARIANT_STREAM || variant == MOE_VARIANT_FUSED) {
       if (!contiguous) return fail(plan, MOE_EUNSUPPORTED, "the streaming kernels take the contiguous format only");
       if (P.K % 128 || P.I % 128)
         return fail(plan, MOE_EUNSUPPORTED, "streaming kernels need K % 128 == 0 and I % 128 == 0");
       // 32-bit buffer offsets: one expert's W1 and the activation buffers
       if (4 * P.I * P.K >= (1ll << 31) || 2 * P.M * P.K >= (1ll << 31))
         return fail(plan, MOE_EUNSUPPORTED, "streaming kernels address one expert with 32-bit offsets");
-      snprintf(plan->reason, sizeof(plan->reason),
-               "stream: M <= 16 rows per expert, weights streamed into the MFMA row operand");
+      if (variant == MOE_VARIANT_FUSED) {
+        if (R > kAlignSmallMaxR || P.E > kFusedMaxExperts)
+          return fail(plan, MOE_EUNSUPPORTED, "the single-launch kernel needs M*topk <= 8192 and E <= 2048");
+        snprintf(plan->reason, sizeof(plan->reason),
+                 "fused: align, W1 and W2 streaming strips in one launch (device work queue), then the reduce");
+      } else {
+        snprintf(plan->reason, sizeof(plan->reason),
+                 "stream: M <= 16 rows per expert, weights streamed into the MFMA row operand");
+      }
     } else {
       // 32-bit buffer offsets: one expert's W1, the activation rows and z
       const int64_t act_rows = contiguous ? P.M : P.E * P.max_tokens;
@@ -185,7 +204,7 @@ int moe_plan_init(moe_plan* plan, const moe_problem* prob) {
     plan->max_active = P.E < R ? P.E : R;
     plan->max_tiles = (R + plan->max_active * (B - 1)) / B;
     plan->sorted_capacity = plan->max_tiles * B;
-    plan->align_blocks = align_nblocks(R);
+    plan->align_blocks = variant == MOE_VARIANT_FUSED ? 0 : align_nblocks(R);
   } else {
     plan->max_active = P.E;
     plan->max_tiles = 0;
@@ -219,6 +238,12 @@ int moe_plan_init(moe_plan* plan, const moe_problem* prob) {
   } else {
     o = up(o + zrows * P.I * 2, kAlign);
     plan->off_z_scale = plan->off_xq = plan->off_xq_scale = -1;
+  }
+  if (variant == MOE_VARIANT_FUSED) {
+    plan->off_sync = o;
+    o = up(o + 4 * sync_words(plan->max_active), kAlign);
+  } else {
+    plan->off_sync = -1;
   }
   plan->ws13_bytes = o;
   plan->ws2_bytes = contiguous ? up(R * P.K * 2, kAlign) : 0;
@@ -271,8 +296,7 @@ static bool contiguous_args_ok(const moe_plan* plan, const moe_weights* w) {
   return true;
 }
 
-static int gate_up_act(const moe_plan* plan, const void* a, const moe_weights* w, void* ws13,
-                       hipStream_t s) {
+static GemmArgs w1_args(const moe_plan* plan, const moe_weights* w, void* ws13) {
   const moe_problem& P = plan->prob;
   GemmArgs g = gemm_common(plan, ws13);
   g.epi = kEpiGateUp;
@@ -283,6 +307,30 @@ static int gate_up_act(const moe_plan* plan, const void* a, const moe_weights* w
   g.nfeat = (int32_t)P.I;
   g.out = at<void>(ws13, plan->off_z);
   g.out_ld = P.I;
+  return g;
+}
+
+static GemmArgs w2_args(const moe_plan* plan, const moe_weights* w, void* ws13, void* ws2) {
+  const moe_problem& P = plan->prob;
+  GemmArgs g = gemm_common(plan, ws13);
+  g.epi = kEpiDown;
+  g.w = w->w2;
+  g.w_scale = w->w2_scale;
+  g.w_expert_stride = P.K * P.I;
+  g.kdim = (int32_t)P.I;
+  g.nfeat = (int32_t)P.K;
+  g.act = at<void>(ws13, plan->off_z);
+  g.act_ld = P.I;
+  g.act_bytes = plan->sorted_capacity * P.I * 2;
+  g.out = ws2;
+  g.out_ld = P.K;
+  return g;
+}
+
+static int gate_up_act(const moe_plan* plan, const void* a, const moe_weights* w, void* ws13,
+                       hipStream_t s) {
+  const moe_problem& P = plan->prob;
+  GemmArgs g = w1_args(plan, w, ws13);
   if (P.w_dtype == MOE_W_MXFP8) {
     uint8_t* xq = at<uint8_t>(ws13, plan->off_xq);
     uint8_t* xqs = at<uint8_t>(ws13, plan->off_xq_scale);
@@ -300,7 +348,7 @@ static int gate_up_act(const moe_plan* plan, const void* a, const moe_weights* w
   g.act = a;
   g.act_ld = P.K;
   g.act_bytes = P.M * P.K * 2;
-  hipError_t e = plan->variant == MOE_VARIANT_STREAM ? launch_gemm_stream_bf16(g, s)
+  hipError_t e = plan->variant != MOE_VARIANT_TILE ? launch_gemm_stream_bf16(g, s)
                                                      : launch_gemm_tile_bf16(g, s);
   return e == hipSuccess ? MOE_OK : MOE_EHIP;
 }
@@ -308,25 +356,14 @@ static int gate_up_act(const moe_plan* plan, const void* a, const moe_weights* w
 static int down_unpermute(const moe_plan* plan, const moe_weights* w, void* ws13, void* ws2,
                           hipStream_t s) {
   const moe_problem& P = plan->prob;
-  GemmArgs g = gemm_common(plan, ws13);
-  g.epi = kEpiDown;
-  g.w = w->w2;
-  g.w_scale = w->w2_scale;
-  g.w_expert_stride = P.K * P.I;
-  g.kdim = (int32_t)P.I;
-  g.nfeat = (int32_t)P.K;
-  g.act = at<void>(ws13, plan->off_z);
-  g.act_ld = P.I;
-  g.act_bytes = plan->sorted_capacity * P.I * 2;
-  g.out = ws2;
-  g.out_ld = P.K;
+  GemmArgs g = w2_args(plan, w, ws13, ws2);
   hipError_t e;
   if (P.w_dtype == MOE_W_MXFP8) {
     g.act_scale = at<uint8_t>(ws13, plan->off_z_scale);
     g.act_bytes = plan->sorted_capacity * P.I;
     e = launch_gemm_stream_mxfp8(g, s);
   } else {
-    e = plan->variant == MOE_VARIANT_STREAM ? launch_gemm_stream_bf16(g, s)
+    e = plan->variant != MOE_VARIANT_TILE ? launch_gemm_stream_bf16(g, s)
                                             : launch_gemm_tile_bf16(g, s);
   }
   return e == hipSuccess ? MOE_OK : MOE_EHIP;
@@ -354,15 +391,31 @@ int moe_apply_contiguous(const moe_plan* plan, const void* a, const int32_t* top
     return MOE_EINVAL;
   hipStream_t s = (hipStream_t)stream;
   AlignArgs al = align_args(plan, topk_ids, w->expert_map, ws13);
-  if (launch_align(al, s) != hipSuccess) return MOE_EHIP;
-  int st = gate_up_act(plan, a, w, ws13, s);
-  if (st != MOE_OK) return st;
-  st = down_unpermute(plan, w, ws13, ws2, s);
-  if (st != MOE_OK) return st;
+  if (plan->variant == MOE_VARIANT_FUSED) {
+    FusedArgs f{};
+    f.align = al;
+    f.w1 = w1_args(plan, w, ws13);
+    f.w1.act = a;
+    f.w1.act_ld = P.K;
+    f.w1.act_bytes = P.M * P.K * 2;
+    f.w2 = w2_args(plan, w, ws13, ws2);
+    f.sync = at<int32_t>(ws13, plan->off_sync);
+    f.max_active = plan->max_active;
+    if (launch_fused_stream_bf16(f, s) != hipSuccess) return MOE_EHIP;
+  } else {
+    if (launch_align(al, s) != hipSuccess) return MOE_EHIP;
+    int st = gate_up_act(plan, a, w, ws13, s);
+    if (st != MOE_OK) return st;
+    st = down_unpermute(plan, w, ws13, ws2, s);
+    if (st != MOE_OK) return st;
+  }
+  const bool fused = plan->variant == MOE_VARIANT_FUSED;
   hipError_t e = launch_reduce_contiguous(static_cast<const uint16_t*>(ws2), topk_ids, topk_weights,
                                           w->expert_map, (int32_t)P.global_experts,
                                           static_cast<uint16_t*>(out), P.M, (int32_t)P.topk, P.K,
-                                          (int32_t)P.E, s);
+                                          (int32_t)P.E,
+                                          fused ? at<int32_t>(ws13, plan->off_sync) : nullptr,
+                                          fused ? sync_counter_lines(plan->max_active) : 0, s);
   return e == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
@@ -415,7 +468,7 @@ int moe_topk_reduce_contiguous(const moe_plan* plan, const void* y, const int32_
   hipError_t e = launch_reduce_contiguous(static_cast<const uint16_t*>(y), topk_ids, topk_weights,
                                           expert_map, (int32_t)P.global_experts,
                                           static_cast<uint16_t*>(out), P.M, (int32_t)P.topk, P.K,
-                                          (int32_t)P.E, (hipStream_t)stream);
+                                          (int32_t)P.E, nullptr, 0, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 

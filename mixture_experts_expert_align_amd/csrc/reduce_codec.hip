@@ -42,7 +42,11 @@ __global__ void __launch_bounds__(NT) reduce_contiguous_kernel(const uint16_t* _
                                                                const float* __restrict__ w,
                                                                const int32_t* __restrict__ emap, int G,
                                                                uint16_t* __restrict__ out, int64_t M,
-                                                               int topk, int64_t K, int E) {
+                                                               int topk, int64_t K, int E,
+                                                               int32_t* __restrict__ sync_zero,
+                                                               int64_t sync_lines) {
+  if (sync_zero && blockIdx.x == 0)
+    for (int64_t i = threadIdx.x; i < sync_lines; i += NT) sync_zero[32 * i] = 0;
   const int64_t K8 = K / 8;
   const int64_t idx = (int64_t)blockIdx.x * NT + threadIdx.x;
   if (idx >= M * K8) return;
@@ -167,9 +171,10 @@ inline unsigned nblocks(int64_t n) { return (unsigned)((n + NT - 1) / NT); }
 
 hipError_t launch_reduce_contiguous(const uint16_t* y, const int32_t* ids, const float* w,
                                     const int32_t* expert_map, int32_t G, uint16_t* out, int64_t M,
-                                    int32_t topk, int64_t K, int32_t E, hipStream_t s) {
+                                    int32_t topk, int64_t K, int32_t E, int32_t* sync_zero,
+                                    int64_t sync_lines, hipStream_t s) {
   hipLaunchKernelGGL(reduce_contiguous_kernel, dim3(nblocks(M * (K / 8))), dim3(NT), 0, s, y, ids, w,
-                     expert_map, G, out, M, topk, K, E);
+                     expert_map, G, out, M, topk, K, E, sync_zero, sync_lines);
   return hipGetLastError();
 }
 

@@ -61,7 +61,7 @@ def test_plans_of_the_five_workloads(idx):
         assert p.out_rows == cfg.M and p.out_cols == cfg.K
     else:
         assert p.reduce_kind == moe.REDUCE_NAIVE_BATCHED and p.variant == moe.VARIANT_TILE
-    expected_variant = {0: moe.VARIANT_TILE, 1: moe.VARIANT_STREAM, 2: moe.VARIANT_TILE,
+    expected_variant = {0: moe.VARIANT_FUSED, 1: moe.VARIANT_STREAM, 2: moe.VARIANT_TILE,
                         3: moe.VARIANT_STREAM, 4: moe.VARIANT_TILE}[idx]
     assert p.variant == expected_variant, p.reason
     # sub-buffers are in order, 256-byte aligned, and inside ws13
@@ -86,12 +86,17 @@ def test_plans_of_the_five_workloads(idx):
     (dict(layout=1, max_tokens=64, variant=moe.VARIANT_STREAM), moe.MOE_EUNSUPPORTED),
     (dict(layout=1, max_tokens=64, w_dtype=moe.W_MXFP8), moe.MOE_EUNSUPPORTED),
     (dict(w_dtype=moe.W_MXFP8, variant=moe.VARIANT_TILE), moe.MOE_EUNSUPPORTED),
-    (dict(K=128), moe.MOE_EUNSUPPORTED),                  # contiguous tiles need K % 256
+    (dict(K=128, variant=moe.VARIANT_TILE), moe.MOE_EUNSUPPORTED),   # contiguous tiles need K % 256
     (dict(global_experts=4), moe.MOE_EINVAL),             # fewer global than local experts
     (dict(global_experts=1 << 31), moe.MOE_EINVAL),
     (dict(layout=1, max_tokens=64, global_experts=16), moe.MOE_EINVAL),
     (dict(K=128, I=96, layout=1, max_tokens=64), moe.MOE_EUNSUPPORTED),
     (dict(w1_order=moe.W1_INTERLEAVE16, I=72), moe.MOE_EINVAL),
+    (dict(variant=moe.VARIANT_FUSED, w_dtype=moe.W_MXFP8), moe.MOE_EUNSUPPORTED),
+    (dict(variant=moe.VARIANT_FUSED, layout=1, max_tokens=64), moe.MOE_EUNSUPPORTED),
+    (dict(variant=moe.VARIANT_FUSED, M=4097), moe.MOE_EUNSUPPORTED),      # M*topk > 8192
+    (dict(variant=moe.VARIANT_FUSED, E=2049), moe.MOE_EUNSUPPORTED),
+    (dict(variant=moe.VARIANT_FUSED, K=200), moe.MOE_EUNSUPPORTED),
 ])
 def test_plan_validation(kw, code):
     base = dict(M=64, K=256, I=512, E=8, topk=2)
@@ -117,9 +122,13 @@ def test_batched_tile_shapes():
 
 
 def test_variant_choice_and_override():
-    p = moe.moe_plan_init(moe.make_problem(16, 256, 512, 8, topk=2))
+    p = moe.moe_plan_init(moe.make_problem(64, 256, 512, 8, topk=2))          # small layer
+    assert p.variant == moe.VARIANT_FUSED
+    p = moe.moe_plan_init(moe.make_problem(300, 256, 512, 8, topk=2))         # 75 rows per expert
+    assert p.variant == moe.VARIANT_TILE and p.block_m == 128
+    p = moe.moe_plan_init(moe.make_problem(16, 4096, 8192, 64, topk=8))       # weights past 1 GiB
     assert p.variant == moe.VARIANT_STREAM
-    p = moe.moe_plan_init(moe.make_problem(17, 256, 512, 8, topk=2))
+    p = moe.moe_plan_init(moe.make_problem(17, 4096, 8192, 64, topk=8))
     assert p.variant == moe.VARIANT_TILE and p.block_m == 128
     p = moe.moe_plan_init(moe.make_problem(17, 256, 512, 8, topk=2, variant=moe.VARIANT_STREAM))
     assert p.variant == moe.VARIANT_STREAM and p.block_m == 16
@@ -133,3 +142,15 @@ def test_align_path_choice():
     assert big.align_blocks == 9                                                # chunks of 1024
     huge = moe.moe_plan_init(moe.make_problem(131073, 256, 512, 8, topk=8))    # R = 1048584
     assert huge.align_blocks == 1024                                            # at most 1024 chunks
+
+
+def test_fused_plan():
+    """The single-launch variant: streaming strips (block_m 16), the one-
+    workgroup align, and a zero-initialised sync area after the other buffers."""
+    p = moe.moe_plan_init(moe.make_problem(4096, 256, 512, 2048, topk=2, variant=moe.VARIANT_FUSED))
+    assert p.variant == moe.VARIANT_FUSED and p.block_m == 16 and p.align_blocks == 0
+    assert "fused" in moe.moe_plan_reason(p)
+    assert p.off_sync >= p.off_z + p.sorted_capacity * 512 * 2
+    assert p.ws13_bytes >= p.off_sync + 4 * (32 * (2 + p.max_active) + 4 * p.max_active)
+    q = moe.moe_plan_init(moe.make_problem(4, 256, 512, 8, topk=2, variant=moe.VARIANT_STREAM))
+    assert q.off_sync == -1

@@ -35,9 +35,11 @@ def free():
 
 
 SCALED = [
-    ("tiny", mi.config(0), moe.VARIANT_AUTO),
+    ("tiny", mi.config(0), moe.VARIANT_AUTO),                      # single launch
+    ("tiny_tile", mi.config(0), moe.VARIANT_TILE),
     ("tiny_stream", mi.config(0), moe.VARIANT_STREAM),
     ("decode_m4", mi.config(1).scaled(K=512, I=1024), moe.VARIANT_AUTO),
+    ("decode_m4_stream", mi.config(1).scaled(K=512, I=1024), moe.VARIANT_STREAM),
     ("decode_m13", mi.config(1).scaled(M=13, K=512, I=1024), moe.VARIANT_AUTO),
     ("decode_m4_tile", mi.config(1).scaled(K=512, I=1024), moe.VARIANT_TILE),
     ("prefill_m1000", mi.config(2).scaled(M=1000, K=256, I=256, E=16), moe.VARIANT_AUTO),
@@ -69,7 +71,7 @@ def test_tiny_intermediate_z():
     """z = silu(x W1g^T) * (x W1u^T) at each sorted position (tile path)."""
     cfg = mi.config(0)
     c = make_case(cfg)
-    out, plan, ws13, _ = run_contiguous(c)
+    out, plan, ws13, _ = run_contiguous(c, moe.VARIANT_TILE)
     sorted_ids = moe.ws_view(ws13, plan.off_sorted_ids, plan.sorted_capacity).cpu().numpy()
     npost = int(moe.ws_view(ws13, plan.off_num_post_padded, 1).cpu()[0])
     z = moe.ws_view(ws13, plan.off_z, plan.sorted_capacity * cfg.I, torch.bfloat16).view(-1, cfg.I)
