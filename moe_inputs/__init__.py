@@ -19,6 +19,12 @@ Five workloads are defined (``CONFIGS``), each with a seed equal to its index:
 * ``batched``   E=32 max_tokens=512 K=7168 I=2048, Zipf(1.2) row counts capped
                 at 512, 512 output tokens
 
+and the training grouped GEMMs' workloads (``TRAIN_CONFIGS``): ragged rows
+grouped by expert (balanced, or Zipf-sized with two empty groups), x [R, K],
+dy [R, N], W [E, N, K] and an fp32 main_grad [E, N, K], the shapes of one
+rank's gate/up (N = 2I = 4096, K = 6144) and down (N = 6144, K = 2048)
+projections with 32 local experts.
+
 Large tensors come from a counter-based generator defined with integer
 operations only (``ih4_normal``), so that the same values come out bit for bit
 on the CPU and on the GPU: each element is the centred sum of four 16-bit
@@ -38,13 +44,15 @@ import torch
 __all__ = [
     "MoEConfig", "CONFIGS", "config", "ih4_normal", "Inputs", "make_inputs",
     "routing_softmax_topk", "routing_affine_ep_share", "batched_zipf_rows",
-    "bf16_bits",
+    "bf16_bits", "TrainConfig", "TRAIN_CONFIGS", "train_config", "train_group_sizes",
+    "TrainInputs", "make_train_inputs",
 ]
 
 MASK32 = 0xFFFFFFFF
 
 # Stream tags: one per kind of tensor, so streams never share a key.
 TAG_X, TAG_W1, TAG_W2, TAG_A = 1, 2, 3, 4
+TAG_TX, TAG_TDY, TAG_TW, TAG_TG = 5, 6, 7, 8   # training grouped GEMMs
 
 
 @dataclasses.dataclass(frozen=True)
@@ -312,3 +320,90 @@ def make_inputs(cfg: MoEConfig, device="cpu", weights: bool = True) -> Inputs:
             inp.w1[e] = expert_w1(cfg, e, device)
             inp.w2[e] = expert_w2(cfg, e, device)
     return inp
+
+
+# --------------------------------------------------------------------------
+# Training grouped GEMMs
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class TrainConfig:
+    name: str
+    seed: int
+    E: int                   # groups (experts)
+    N: int                   # output features of the forward (W[e] is [N, K])
+    K: int                   # contraction of the forward
+    rows: int                # R: rows over all groups
+    balance: str = "balanced"  # "balanced" | "zipf" (Zipf(1.2) sizes, two empty groups)
+
+    def scaled(self, **kw) -> "TrainConfig":
+        return dataclasses.replace(self, **kw)
+
+
+TRAIN_CONFIGS = [
+    TrainConfig("train_small_e8_n256_k384_r1000", 20, E=8, N=256, K=384, rows=1000, balance="zipf"),
+    TrainConfig("train_gu_e32_n4096_k6144_r32768", 21, E=32, N=4096, K=6144, rows=32768),
+    TrainConfig("train_dn_e32_n6144_k2048_r32768", 22, E=32, N=6144, K=2048, rows=32768),
+]
+
+
+def train_config(name: str) -> TrainConfig:
+    for c in TRAIN_CONFIGS:
+        if c.name == name or c.name.split("_")[1] == name or "_".join(c.name.split("_")[:2]) == name:
+            return c
+    raise KeyError(name)
+
+
+def train_group_sizes(cfg: TrainConfig) -> np.ndarray:
+    """Rows per group: R/E each (the remainder to the first groups), or
+    Zipf(1.2)-distributed over all but groups 2 and E-1, which stay empty."""
+    if cfg.balance == "balanced":
+        sizes = np.full(cfg.E, cfg.rows // cfg.E, dtype=np.int64)
+        sizes[: cfg.rows % cfg.E] += 1
+        return sizes
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg.seed, 31])))
+    live = [e for e in range(cfg.E) if e not in (2, cfg.E - 1)]
+    p = np.arange(1, len(live) + 1, dtype=np.float64) ** -1.2
+    sizes = np.zeros(cfg.E, dtype=np.int64)
+    sizes[live] = rng.multinomial(cfg.rows, p / p.sum())
+    return sizes
+
+
+@dataclasses.dataclass
+class TrainInputs:
+    cfg: TrainConfig
+    offsets: np.ndarray          # int32 [E+1]
+    x: torch.Tensor              # bf16 [R, K]
+    dy: torch.Tensor             # bf16 [R, N]
+    w: torch.Tensor              # bf16 [E, N, K]
+    main_grad: torch.Tensor      # float32 [E, N, K]; groups without rows hold -0.0
+
+
+def make_train_inputs(cfg: TrainConfig, device="cpu") -> TrainInputs:
+    sizes = train_group_sizes(cfg)
+    off = np.zeros(cfg.E + 1, dtype=np.int32)
+    off[1:] = np.cumsum(sizes)
+    R = int(off[-1])
+
+    def big(n_rows, n_cols, sigma, tag):
+        out = torch.empty((n_rows, n_cols), dtype=torch.bfloat16, device=device)
+        step = max(1, (1 << 26) // n_cols)
+        for r0 in range(0, n_rows, step):
+            r1 = min(n_rows, r0 + step)
+            out[r0:r1] = ih4_normal((r1 - r0) * n_cols, sigma, cfg.seed, tag, 0, start=r0 * n_cols,
+                                    device=device).view(r1 - r0, n_cols)
+        return out
+
+    x = big(R, cfg.K, 1.0, TAG_TX)
+    dy = big(R, cfg.N, 1.0, TAG_TDY)
+    w = torch.empty((cfg.E, cfg.N, cfg.K), dtype=torch.bfloat16, device=device)
+    g = torch.empty((cfg.E, cfg.N, cfg.K), dtype=torch.float32, device=device)
+    for e in range(cfg.E):
+        w[e] = ih4_normal(cfg.N * cfg.K, 1.0 / math.sqrt(cfg.K), cfg.seed, TAG_TW, e,
+                          device=device).view(cfg.N, cfg.K)
+        g[e] = ih4_normal(cfg.N * cfg.K, 1.0, cfg.seed, TAG_TG, e, device=device,
+                          out_dtype=torch.float32).view(cfg.N, cfg.K)
+        if sizes[e] == 0:
+            g[e] = -0.0
+    return TrainInputs(cfg=cfg, offsets=off, x=x, dy=dy, w=w, main_grad=g)
+

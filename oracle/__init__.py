@@ -19,8 +19,11 @@ passage of the pages it restates:
          written per (token, top-k slot); ordered Top-K reduce).
 * [MEGA] "DeepGEMM Mega MoE as an EP implementation" (transformers PR 49606
          analysis), section 2: padded slots carry expert id -1 and weight 0.
-* [DET]  "Cake deterministic MoE grouped GEMM" (FlashInfer PR 9132 analysis),
-         section 2: an empty sum is +0.0.
+* [DET]  "Cake deterministic MoE grouped GEMM" (FlashInfer PR 9132 analysis):
+         introduction (a ragged bf16 grouped GEMM for training: forward, dgrad,
+         wgrad; the fp32 weight-gradient accumulate into main_grad), section 1
+         (the fused accumulate equals out.add_(dW)), section 2 (an empty sum is
+         +0.0, so an empty group turns -0.0 into +0.0).
 
 Readings where the pages are silent (each also listed in the design notes):
 * W1 rows [0, I) are the gate projection and [I, 2I) the up projection
@@ -37,6 +40,11 @@ Readings where the pages are silent (each also listed in the design notes):
 * With global expert ids, the map is applied first (``map_expert_ids``) and the
   steps then run on local ids; a slot whose expert another GPU holds is
   skipped without being counted as invalid.
+* Training grouped GEMMs: rows are grouped by expert, group e being rows
+  [offsets[e], offsets[e+1]) of the row-major operands; the weight of expert e
+  is W[e] [N, K] and the forward is y = x W[e]^T, so dgrad is dy W[e] and wgrad
+  sums dy^T x over the group's rows.  The accumulate adds that sum to the fp32
+  buffer once.
 
 parity pins: every function here is pinned by ``tests/test_oracle_*.py``
 (closed forms, library special cases, brute force, invariants); none is
@@ -53,7 +61,8 @@ __all__ = [
     "bf16_to_f64", "e4m3fn_table", "e4m3fn_encode", "mx_scale_exponent", "mx_scale_code",
     "mxfp8_quantize", "mxfp8_dequantize", "split_gate_up", "silu", "expert_ffn",
     "align_permute", "moe_contiguous", "moe_routes", "topk_reduce_contiguous",
-    "moe_batched_rows", "naive_batched_reduce",
+    "moe_batched_rows", "naive_batched_reduce", "grouped_forward", "grouped_dgrad",
+    "grouped_wgrad", "grouped_wgrad_accumulate",
 ]
 
 E4M3_MAX = 448.0
@@ -399,3 +408,51 @@ def naive_batched_reduce(y_of: Callable[[int, int], np.ndarray], counts: np.ndar
             if t in pos:
                 out[pos[t]] += float(row_weight[e, r]) * y_of(e, r)
     return out + 0.0
+
+
+# ------------------------------------------------------------ training ----
+# [DET] introduction: the ragged grouped GEMM of a MoE layer's training step.
+# Group e holds rows [offsets[e], offsets[e+1]); W[e] is [N, K].
+
+def _groups(offsets: np.ndarray):
+    offsets = np.asarray(offsets, dtype=np.int64)
+    assert offsets[0] == 0 and np.all(np.diff(offsets) >= 0)
+    return [(e, int(offsets[e]), int(offsets[e + 1])) for e in range(len(offsets) - 1)]
+
+
+def grouped_forward(x: np.ndarray, w: np.ndarray, offsets: np.ndarray) -> np.ndarray:
+    """y[r] = W[e] x[r] for the rows r of group e (x [R, K], w [E, N, K];
+    returns [R, N] float64)."""
+    y = np.zeros((x.shape[0], w.shape[1]), dtype=np.float64)
+    for e, a, b in _groups(offsets):
+        y[a:b] = x[a:b].astype(np.float64) @ w[e].astype(np.float64).T
+    return y
+
+
+def grouped_dgrad(dy: np.ndarray, w: np.ndarray, offsets: np.ndarray) -> np.ndarray:
+    """The input gradient of grouped_forward: dx[r] = W[e]^T dy[r] (dy [R, N];
+    returns [R, K] float64)."""
+    dx = np.zeros((dy.shape[0], w.shape[2]), dtype=np.float64)
+    for e, a, b in _groups(offsets):
+        dx[a:b] = dy[a:b].astype(np.float64) @ w[e].astype(np.float64)
+    return dx
+
+
+def grouped_wgrad(dy: np.ndarray, x: np.ndarray, offsets: np.ndarray) -> np.ndarray:
+    """The weight gradient of grouped_forward: dW[e] = sum over the rows r of
+    group e of dy[r] x[r]^T ([E, N, K] float64).  A group without rows gives
+    +0.0 everywhere ([DET] section 2)."""
+    groups = _groups(offsets)
+    dw = np.zeros((len(groups), dy.shape[1], x.shape[1]), dtype=np.float64)
+    for e, a, b in groups:
+        if b > a:
+            dw[e] = dy[a:b].astype(np.float64).T @ x[a:b].astype(np.float64)
+    return dw + 0.0   # +0.0, never -0.0
+
+
+def grouped_wgrad_accumulate(out: np.ndarray, dy: np.ndarray, x: np.ndarray,
+                             offsets: np.ndarray) -> np.ndarray:
+    """main_grad after the accumulate: out + dW ([DET] section 1: the same as
+    out.add_(dW)); float64 of the fp32 buffer plus the float64 gradient."""
+    return np.asarray(out, dtype=np.float64) + grouped_wgrad(dy, x, offsets)
+

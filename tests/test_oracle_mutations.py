@@ -12,13 +12,15 @@ import oracle
 import test_oracle_align as A
 import test_oracle_codec as C
 import test_oracle_ffn as FF
+import test_oracle_train as T
 
-ALL_PINS = C.PINS + A.PINS + FF.PINS
+ALL_PINS = C.PINS + A.PINS + FF.PINS + T.PINS
 
 _orig = {n: getattr(oracle, n) for n in ("split_gate_up", "silu", "expert_ffn", "align_permute",
                                          "mx_scale_exponent", "e4m3fn_encode",
                                          "topk_reduce_contiguous", "moe_contiguous",
-                                         "map_expert_ids")}
+                                         "map_expert_ids", "grouped_forward", "grouped_dgrad",
+                                         "grouped_wgrad", "grouped_wgrad_accumulate")}
 
 
 def m_swap_gate_up(w1, order):
@@ -105,7 +107,46 @@ def m_map_out_of_range_kept(ids, emap):
     return out                                           # ids past G silently skipped
 
 
+def m_forward_w_layout(x, w, off):
+    # W[e] read as [K, N] row-major instead of [N, K]
+    w = np.asarray(w)
+    return _orig["grouped_forward"](x, w.reshape(w.shape[0], w.shape[2], w.shape[1]).transpose(0, 2, 1), off)
+
+
+def m_dgrad_wrong_expert(dy, w, off):
+    return _orig["grouped_dgrad"](dy, np.roll(np.asarray(w), 1, axis=0), off)
+
+
+def m_dgrad_w_layout(dy, w, off):
+    w = np.asarray(w)
+    return _orig["grouped_dgrad"](dy, w.reshape(w.shape[0], w.shape[2], w.shape[1]).transpose(0, 2, 1), off)
+
+
+def m_wgrad_drops_last_row(dy, x, off):
+    off = np.asarray(off, np.int64)
+    dw = np.zeros((len(off) - 1, dy.shape[1], x.shape[1]))
+    for e in range(len(off) - 1):
+        a, b = int(off[e]), int(off[e + 1]) - 1
+        if b > a:
+            dw[e] = dy[a:b].T @ x[a:b]
+    return dw
+
+
+def m_wgrad_minus_zero(dy, x, off):
+    dw = _orig["grouped_wgrad"](dy, x, off)
+    empty = np.diff(np.asarray(off)) == 0
+    dw[empty] = -0.0
+    return dw
+
+
+def m_accumulate_ignores_out(out, dy, x, off):
+    return _orig["grouped_wgrad"](dy, x, off)
+
+
 MUTATIONS = [
+    ("grouped_forward", m_forward_w_layout), ("grouped_dgrad", m_dgrad_wrong_expert),
+    ("grouped_dgrad", m_dgrad_w_layout), ("grouped_wgrad", m_wgrad_drops_last_row),
+    ("grouped_wgrad", m_wgrad_minus_zero), ("grouped_wgrad_accumulate", m_accumulate_ignores_out),
     ("split_gate_up", m_swap_gate_up), ("split_gate_up", m_interleave_up_first),
     ("silu", m_silu_sign), ("expert_ffn", m_ffn_no_act), ("expert_ffn", m_ffn_w2_transposed),
     ("align_permute", m_align_descending), ("align_permute", m_align_no_padding),
