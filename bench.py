@@ -37,7 +37,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="decode",
-                    help="tiny | decode | prefill | mxfp8 | batched (or a full workload name)")
+                    help="tiny | decode | prefill | mxfp8 | batched (or a full workload name); "
+                         "train_gu | train_dn: the training grouped GEMMs of one projection")
     ap.add_argument("--variant", default="auto", choices=["auto", "tile", "stream", "fused"],
                     help="kernel family (auto: the plan's choice); fused: one launch for align, "
                          "W1 and W2, then the reduce, timed as one stage")
@@ -109,7 +110,10 @@ def counter_values(path: str, counter: str, kernel_substr: str):
 
 def traffic_from(args):
     import numpy as np
-    cfg_name = args.config.split("_")[0] + ("" if args.variant == "auto" else "_" + args.variant)
+    if args.config.startswith("train"):
+        cfg_name = "_".join(args.config.split("_")[:2])
+    else:
+        cfg_name = args.config.split("_")[0] + ("" if args.variant == "auto" else "_" + args.variant)
     kerns = DOMINANT_KERNEL[cfg_name]
     # per kernel of the timed stage: the median over its dispatches; the
     # stage's traffic is the sum over its kernels
@@ -150,10 +154,12 @@ DOMINANT_KERNEL = {"tiny": FUSED_KERNELS, "decode": ["gemm_stream_bf16_kernel<0,
                    "prefill": ["gemm_tile_bf16_kernel<0,"],
                    "mxfp8": ["quantize_gather_kernel", "gemm_stream_mxfp8_kernel<0,"],
                    "batched": ["gemm_tile_bf16_kernel<0,", "gemm_tile_bf16_kernel<1,"],
-                   "decode_fused": FUSED_KERNELS, "tiny_fused": FUSED_KERNELS}
+                   "decode_fused": FUSED_KERNELS, "tiny_fused": FUSED_KERNELS,
+                   "train_gu": ["train_wgrad_kernel"], "train_dn": ["train_wgrad_kernel"]}
 KERNEL_FILES = {"tiny": FUSED_FILES, "decode": ["gemm_stream.hip", "stream_bf16.h"],
                 "prefill": ["gemm_tile.hip"], "mxfp8": ["reduce_codec.hip", "gemm_mxfp8.hip"],
-                "batched": ["gemm_tile.hip"], "decode_fused": FUSED_FILES, "tiny_fused": FUSED_FILES}
+                "batched": ["gemm_tile.hip"], "decode_fused": FUSED_FILES, "tiny_fused": FUSED_FILES,
+                "train_gu": ["train.hip"], "train_dn": ["train.hip"]}
 
 
 def main():
@@ -169,6 +175,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.config.startswith("train"):
+        main_train(args)
         return
 
     import numpy as np
@@ -266,35 +275,8 @@ def main():
                                               wsr, stream)
             ev[2].record(stream)
 
-    nev = len(stages) + 1
-    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
-    for _ in range(args.warmup):
-        step(mk())
-    torch.cuda.synchronize()
-    events = [mk() for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(events[k])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    stage_ms = {s: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in events]))
-                for i, s in enumerate(stages)}
+    elapsed, stage_ms, step_ev, cold_ev = time_steps(step, stages, args, dev)
     ms_per_step = elapsed * 1e3 / args.steps
-    step_ev = [ev[0].elapsed_time(ev[-1]) for ev in events]
-
-    # the same steps with L2 and the Infinity Cache flushed before each (a
-    # 512 MiB fill between steps, outside each step's event pair): the cold
-    # figure for workloads whose weights would otherwise stay cached
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    cold = [mk() for _ in range(args.steps)]
-    for k in range(args.steps):
-        flush.fill_(k & 0xFF)
-        step(cold[k])
-    torch.cuda.synchronize()
-    cold_ev = [ev[0].elapsed_time(ev[-1]) for ev in cold]
-    del flush
-    pct = lambda v: {f"p{q}": round(float(np.percentile(v, q)), 4) for q in (10, 50, 90)}
     tokens = cfg.M
     value = tokens * args.steps / elapsed
 
@@ -365,6 +347,143 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def pct(v):
+    import numpy as np
+    return {f"p{q}": round(float(np.percentile(v, q)), 4) for q in (10, 50, 90)}
+
+
+def time_steps(step, stages, args, dev):
+    """W untimed steps, then exactly K timed ones between two synchronisations
+    (wall clock), with HIP events between the stages on the launch stream;
+    then K more, each after a 512 MiB fill that flushes L2 and the Infinity
+    Cache (outside each step's events and outside the wall-clock steps).
+    Returns (seconds for the K steps, mean ms per stage, per-step event ms,
+    per-step event ms of the flushed steps)."""
+    import numpy as np
+    import torch
+    nev = len(stages) + 1
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+    for _ in range(args.warmup):
+        step(mk())
+    torch.cuda.synchronize()
+    events = [mk() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stage_ms = {s: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in events]))
+                for i, s in enumerate(stages)}
+    step_ev = [ev[0].elapsed_time(ev[-1]) for ev in events]
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = [mk() for _ in range(args.steps)]
+    for k in range(args.steps):
+        flush.fill_(k & 0xFF)
+        step(cold[k])
+    torch.cuda.synchronize()
+    cold_ev = [ev[0].elapsed_time(ev[-1]) for ev in cold]
+    del flush
+    return elapsed, stage_ms, step_ev, cold_ev
+
+
+TRAIN_METRIC = "training grouped GEMM rows/s (forward + dgrad + fp32 wgrad accumulate); TFLOP/s vs MFMA peak"
+
+
+def main_train(args):
+    """A training step of one MoE projection ([DET]): the ragged grouped
+    forward, dgrad and wgrad with the fp32 accumulate into main_grad, through
+    the C ABI on one stream."""
+    import numpy as np
+    import torch
+
+    import moe_inputs as mi
+    import mixture_experts_expert_align_amd as moe
+
+    cfg = mi.train_config(args.config)
+    dev = "cuda"
+    torch.cuda.init()
+    print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
+    ti = mi.make_train_inputs(cfg, device=dev)
+    off = torch.from_numpy(ti.offsets).to(dev)
+    R = int(ti.offsets[-1])
+    y = torch.empty((R, cfg.N), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty((R, cfg.K), dtype=torch.bfloat16, device=dev)
+    main_grad = ti.main_grad
+    stream = torch.cuda.current_stream()
+    stages = ["forward", "dgrad", "wgrad_acc"]
+
+    def step(ev):
+        ev[0].record(stream)
+        moe.moe_grouped_forward(ti.x, ti.w, off, y, stream)
+        ev[1].record(stream)
+        moe.moe_grouped_dgrad(ti.dy, ti.w, off, dx, stream)
+        ev[2].record(stream)
+        moe.moe_grouped_wgrad(ti.dy, ti.x, off, main_grad, accumulate=True, stream=stream)
+        ev[3].record(stream)
+
+    elapsed, stage_ms, step_ev, cold_ev = time_steps(step, stages, args, dev)
+    ms_per_step = elapsed * 1e3 / args.steps
+    flops = 2.0 * R * cfg.N * cfg.K           # per GEMM
+    tf = {s: round(flops / (stage_ms[s] * 1e-3) / 1e12, 1) for s in stages}
+    short = "_".join(cfg.name.split("_")[:2])
+    dom = "wgrad_acc"
+    achieved = flops / (stage_ms[dom] * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_TFLOPS["bf16"], 4), "kernel": dom,
+            "kernel_ms": round(stage_ms[dom], 4),
+            "algorithmic_per_launch": {"flops": int(flops),
+                                       "bytes": int(R * (cfg.N + cfg.K) * 2 + 2 * cfg.E * cfg.N * cfg.K * 4)},
+            "traffic": traffic_record(short, KERNEL_FILES[short]) if short in KERNEL_FILES else None}
+    cpu = None if args.no_cpu_baseline else cpu_baseline_train(cfg, ti, args.cpu_seconds)
+    rec = {
+        "metric": TRAIN_METRIC, "value": round(R * args.steps / elapsed, 2), "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded counter-based generator; random-init expert weights)",
+        "config": {"workload": cfg.name, "E": cfg.E, "N": cfg.N, "K": cfg.K, "rows": R,
+                   "groups": cfg.balance, "accumulate": "fp32 main_grad, in the kernel"},
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "stage_TFLOPs": tf,
+        "step_event_ms": pct(step_ev), "step_event_ms_cache_flushed": pct(cold_ev),
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline_train(cfg, ti, min_seconds):
+    """The oracle's forward, dgrad and wgrad on one group's rows (the
+    lightest non-empty group), repeated to about ``min_seconds``: rows/s."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    sizes = np.diff(ti.offsets)
+    e = int(np.argmin(np.where(sizes > 0, sizes, 1 << 30)))
+    a, b = int(ti.offsets[e]), int(ti.offsets[e + 1])
+    x = ti.x[a:b].float().cpu().numpy().astype(np.float64)
+    dy = ti.dy[a:b].float().cpu().numpy().astype(np.float64)
+    w = ti.w[e:e + 1].float().cpu().numpy().astype(np.float64)
+    off = np.array([0, b - a])
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.grouped_forward(x, w, off)
+        oracle.grouped_dgrad(dy, w, off)
+        oracle.grouped_wgrad(dy, x, off)
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round((b - a) * reps / dt, 4), "unit": "rows/s", "cores": int(blas_threads),
+            "kind": "oracle", "sample": f"group {e} ({b - a} rows, N={cfg.N}, K={cfg.K}), {reps} passes",
+            "seconds": round(dt, 2), "host_cpus": os.cpu_count()}
 
 
 def cpu_baseline(cfg, inp, w1, w2, w_f32, sample, min_seconds):

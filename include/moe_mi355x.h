@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 /* Status codes. */
 enum {
@@ -298,6 +298,50 @@ int moe_topk_reduce_naive_batched(const moe_plan* plan, const void* y,
  * how MXFP8 weights are produced for moe_apply_*. */
 int moe_quantize_mxfp8(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* codes,
                        uint8_t* scales, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Training grouped GEMMs (page "Cake deterministic MoE grouped GEMM":
+ * introduction — a ragged bf16 grouped GEMM for training whose forward,
+ * dgrad and wgrad give the same bits on every run; section 1 — the fp32
+ * weight gradient added into the fp32 main_grad inside the kernel, the same
+ * bits as out.add_(dW); section 2 — an empty group's sum is +0.0).
+ *
+ * Rows are grouped by expert: group e is rows [group_offsets[e],
+ * group_offsets[e+1]) of x [R, K] and dy [R, N] (row-major bf16); W is
+ * [E, N, K] bf16 (expert e's forward maps K features to N).  group_offsets:
+ * device int32 [E+1], non-decreasing from 0 to R (entries are clamped to
+ * [0, R], so a malformed array reads no row outside the buffers but gives
+ * undefined results).  bf16 products accumulate in fp32 in a fixed order; no
+ * result depends on the run.  Each call launches one kernel on `stream`,
+ * allocates nothing and does not synchronise.  With R = 0 the row matrices
+ * (x, dy, y, dx) and w may be NULL.  Errors: MOE_EINVAL (null or
+ * misaligned pointer: 16 bytes for the matrices, 4 for group_offsets; E
+ * outside [1, 65535]; R outside [0, 2^31); N or K not positive),
+ * MOE_EUNSUPPORTED (N or K not a multiple of 128, or R * max(N, K) * 2 or
+ * N * K * 2 bytes at or past 2^31), MOE_EHIP (launch failure).
+ * ------------------------------------------------------------------------- */
+typedef struct moe_grouped_problem {
+  int64_t R;   /* rows over all groups                                      */
+  int64_t N;   /* forward output features                                   */
+  int64_t K;   /* forward contraction                                       */
+  int64_t E;   /* groups (experts)                                          */
+} moe_grouped_problem;
+
+/* y[r] = W[e] x[r] for the rows r of group e: y device bf16 [R, N]. */
+int moe_grouped_forward(const moe_grouped_problem* p, const void* x, const void* w,
+                        const int32_t* group_offsets, void* y, void* stream);
+
+/* dgrad: dx[r] = W[e]^T dy[r]: dx device bf16 [R, K]. */
+int moe_grouped_dgrad(const moe_grouped_problem* p, const void* dy, const void* w,
+                      const int32_t* group_offsets, void* dx, void* stream);
+
+/* wgrad: dW[e] = sum over the rows r of group e of dy[r] x[r]^T, fp32.
+ * dw: device float32 [E, N, K]; accumulate = 0 writes dW (+0.0 for an empty
+ * group), accumulate = 1 adds it: dw[e] = dw[e] + dW[e] in one fp32 add per
+ * element, bit for bit what the overwrite followed by dw.add_(dW) gives (an
+ * empty group adds +0.0, which turns -0.0 into +0.0). */
+int moe_grouped_wgrad(const moe_grouped_problem* p, const void* dy, const void* x,
+                      const int32_t* group_offsets, float* dw, int accumulate, void* stream);
 
 #ifdef __cplusplus
 }

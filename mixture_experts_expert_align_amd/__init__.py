@@ -23,9 +23,10 @@ __all__ = [
     "moe_gate_up_act", "moe_down_unpermute",
     "moe_topk_reduce_contiguous", "moe_naive_batched_ws_bytes", "moe_topk_reduce_naive_batched",
     "moe_quantize_mxfp8", "make_problem", "allocate_workspaces", "ws_view",
+    "MoeGroupedProblem", "moe_grouped_forward", "moe_grouped_dgrad", "moe_grouped_wgrad",
 ]
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, 1, 2, 3
 LAYOUT_CONTIGUOUS, LAYOUT_BATCHED = 0, 1
 W_BF16, W_MXFP8 = 0, 1
@@ -40,6 +41,10 @@ class MoeProblem(ctypes.Structure):
     _fields_ = [("M", _i64), ("K", _i64), ("I", _i64), ("E", _i64), ("topk", _i64),
                 ("max_tokens", _i64), ("global_experts", _i64), ("layout", _i32), ("w_dtype", _i32),
                 ("w1_order", _i32), ("variant", _i32)]
+
+
+class MoeGroupedProblem(ctypes.Structure):
+    _fields_ = [("R", _i64), ("N", _i64), ("K", _i64), ("E", _i64)]
 
 
 class MoePlan(ctypes.Structure):
@@ -99,6 +104,9 @@ def load_library() -> ctypes.CDLL:
         "moe_naive_batched_ws_bytes": (_i64, [_vp, _i64]),
         "moe_topk_reduce_naive_batched": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp]),
         "moe_quantize_mxfp8": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _vp]),
+        "moe_grouped_forward": (_i32, [_vp] * 6),
+        "moe_grouped_dgrad": (_i32, [_vp] * 6),
+        "moe_grouped_wgrad": (_i32, [_vp] * 5 + [_i32, _vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -253,3 +261,35 @@ def moe_quantize_mxfp8(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tenso
     st = load_library().moe_quantize_mxfp8(_ptr(x), 0 if x.dtype == torch.float32 else 1, rows,
                                            x.shape[-1], _ptr(codes), _ptr(scales), _stream(stream))
     _check("moe_quantize_mxfp8", st)
+
+
+# ------------------------------------------------------------- training ----
+
+def _grouped(R, N, K, E) -> MoeGroupedProblem:
+    return MoeGroupedProblem(R=R, N=N, K=K, E=E)
+
+
+def moe_grouped_forward(x, w, group_offsets, y, stream=None):
+    """y[r] = W[e] x[r] over the rows of each group (x [R,K], w [E,N,K], y [R,N] bf16)."""
+    p = _grouped(x.shape[0], w.shape[1], w.shape[2], w.shape[0])
+    st = load_library().moe_grouped_forward(ctypes.byref(p), _ptr(x), _ptr(w), _ptr(group_offsets),
+                                            _ptr(y), _stream(stream))
+    _check("moe_grouped_forward", st)
+
+
+def moe_grouped_dgrad(dy, w, group_offsets, dx, stream=None):
+    """dx[r] = W[e]^T dy[r] (dy [R,N], w [E,N,K], dx [R,K] bf16)."""
+    p = _grouped(dy.shape[0], w.shape[1], w.shape[2], w.shape[0])
+    st = load_library().moe_grouped_dgrad(ctypes.byref(p), _ptr(dy), _ptr(w), _ptr(group_offsets),
+                                          _ptr(dx), _stream(stream))
+    _check("moe_grouped_dgrad", st)
+
+
+def moe_grouped_wgrad(dy, x, group_offsets, dw, accumulate: bool = False, stream=None):
+    """dW[e] = sum over group e's rows of dy[r] x[r]^T into dw [E,N,K] float32
+    (written, or added when ``accumulate``)."""
+    p = _grouped(dy.shape[0], dw.shape[1], dw.shape[2], dw.shape[0])
+    st = load_library().moe_grouped_wgrad(ctypes.byref(p), _ptr(dy), _ptr(x), _ptr(group_offsets),
+                                          _ptr(dw), 1 if accumulate else 0, _stream(stream))
+    _check("moe_grouped_wgrad", st)
+

@@ -137,6 +137,25 @@ struct FusedArgs {
 
 hipError_t launch_fused_stream_bf16(FusedArgs f, hipStream_t s);
 
+// ------------------------------------------------------------- training ----
+// Deterministic ragged grouped GEMMs (see train.hip): group e is rows
+// [offsets[e], offsets[e+1]) of x [R, K] and dy [R, N]; w is [E, N, K].
+enum TrainMode { kTrainForward = 0, kTrainDgrad = 1, kTrainWgrad = 2 };
+
+struct TrainArgs {
+  int32_t mode;
+  const uint16_t* x;           // forward, wgrad
+  const uint16_t* dy;          // dgrad, wgrad
+  const uint16_t* w;           // forward, dgrad
+  const int32_t* offsets;      // [E+1]
+  void* out;                   // y [R,N] bf16 / dx [R,K] bf16 / dW [E,N,K] fp32
+  int64_t R;
+  int32_t N, K, E;
+  int32_t accumulate;          // wgrad: add into out instead of writing it
+};
+
+hipError_t launch_train(const TrainArgs& t, hipStream_t s);
+
 // --------------------------------------------------------------- reduce ----
 // out[t] = sum over slots j (ascending) whose id (mapped through expert_map
 // when given: ids in [0, G)) is a local expert in [0, E) of w[t,j] * y[t*topk+j]

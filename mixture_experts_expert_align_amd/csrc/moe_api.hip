@@ -532,4 +532,64 @@ int moe_quantize_mxfp8(const void* x, int x_dtype, int64_t rows, int64_t cols, u
   return e == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
+
+// ------------------------------------------------------------- training ----
+
+static int grouped_ok(const moe_grouped_problem* p, const int32_t* offsets) {
+  if (!p || !aligned4(offsets)) return MOE_EINVAL;
+  if (p->E < 1 || p->E > 65535 || p->R < 0 || p->R >= (1ll << 31) || p->N <= 0 || p->K <= 0)
+    return MOE_EINVAL;
+  if (p->N % 128 || p->K % 128) return MOE_EUNSUPPORTED;
+  const int64_t wide = p->N > p->K ? p->N : p->K;
+  if (p->R * wide * 2 >= (1ll << 31) || p->N * p->K * 2 >= (1ll << 31)) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+static TrainArgs train_args(const moe_grouped_problem* p, int mode, const int32_t* offsets, void* out) {
+  TrainArgs t{};
+  t.mode = mode;
+  t.offsets = offsets;
+  t.out = out;
+  t.R = p->R;
+  t.N = (int32_t)p->N;
+  t.K = (int32_t)p->K;
+  t.E = (int32_t)p->E;
+  return t;
+}
+
+int moe_grouped_forward(const moe_grouped_problem* p, const void* x, const void* w,
+                        const int32_t* group_offsets, void* y, void* stream) {
+  const int st = grouped_ok(p, group_offsets);
+  if (st != MOE_OK) return st;
+  if (p->R > 0 && (!aligned16(x) || !aligned16(w) || !aligned16(y))) return MOE_EINVAL;
+  TrainArgs t = train_args(p, kTrainForward, group_offsets, y);
+  t.x = static_cast<const uint16_t*>(x);
+  t.w = static_cast<const uint16_t*>(w);
+  return launch_train(t, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+int moe_grouped_dgrad(const moe_grouped_problem* p, const void* dy, const void* w,
+                      const int32_t* group_offsets, void* dx, void* stream) {
+  const int st = grouped_ok(p, group_offsets);
+  if (st != MOE_OK) return st;
+  if (p->R > 0 && (!aligned16(dy) || !aligned16(w) || !aligned16(dx))) return MOE_EINVAL;
+  TrainArgs t = train_args(p, kTrainDgrad, group_offsets, dx);
+  t.dy = static_cast<const uint16_t*>(dy);
+  t.w = static_cast<const uint16_t*>(w);
+  return launch_train(t, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+int moe_grouped_wgrad(const moe_grouped_problem* p, const void* dy, const void* x,
+                      const int32_t* group_offsets, float* dw, int accumulate, void* stream) {
+  const int st = grouped_ok(p, group_offsets);
+  if (st != MOE_OK) return st;
+  if (!aligned16(dw) || (accumulate != 0 && accumulate != 1)) return MOE_EINVAL;
+  if (p->R > 0 && (!aligned16(dy) || !aligned16(x))) return MOE_EINVAL;
+  TrainArgs t = train_args(p, kTrainWgrad, group_offsets, dw);
+  t.dy = static_cast<const uint16_t*>(dy);
+  t.x = static_cast<const uint16_t*>(x);
+  t.accumulate = accumulate;
+  return launch_train(t, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
 }  // extern "C"

@@ -1,0 +1,337 @@
+// Deterministic grouped GEMMs for training a MoE layer (page "Cake
+// deterministic MoE grouped GEMM", introduction: a ragged bf16 grouped GEMM
+// whose forward, dgrad and wgrad give the same bits on every run, and whose
+// fp32 weight gradient is added into the fp32 main_grad inside the kernel,
+// the same bits as out.add_(dW), section 1).
+//
+// Rows are grouped by expert: group e is rows [offsets[e], offsets[e+1]) of
+// x [R, K] and dy [R, N]; W is [E, N, K].
+//   forward  y[r]  = W[e] x[r]                      ([R, N] bf16)
+//   dgrad    dx[r] = W[e]^T dy[r]                   ([R, K] bf16)
+//   wgrad    dW[e] = sum over the group's rows of dy[r] x[r]^T
+//                    ([E, N, K] fp32, written, or added to the fp32 buffer)
+//
+// One kernel computes C[i][j] = sum_c A(i, c) B(j, c) for a 128 x 128 tile
+// of C, the contraction in 32-wide slices staged in LDS (two buffers), four
+// waves of 64 x 64 as 2 x 2 tiles of v_mfma_f32_32x32x16_bf16.  Each operand
+// is stored either with c contiguous (x and W for the forward, dy for dgrad)
+// or with its own index contiguous (W for dgrad, dy and x for wgrad): MFMA
+// wants 8 consecutive c per lane, so the second kind is staged transposed —
+// a thread loads two rows of c (16 bytes of 8 consecutive i each), pairs up
+// the values of the same i, and writes 8 four-byte words, each at its i row.
+//
+// Determinism: every output element is computed by one workgroup, whose
+// MFMAs add the contraction in a fixed order; nothing is split across
+// workgroups and no atomics touch floating point.  The accumulate adds the
+// finished fp32 sum to the buffer once (a plain fp32 add), so it equals the
+// overwrite followed by out.add_.  An empty group's sum stays +0.0 (the
+// accumulators start at +0.0), which turns a -0.0 in the buffer into +0.0
+// (section 2).
+#include <type_traits>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace train {
+
+constexpr int BI = 128, BJ = 128, BC = 32;   // tile of C, contraction slice
+constexpr int NT = 256;                      // 4 waves: 2 (j) x 2 (i) of 64 x 64
+constexpr int CH = BC / 8;                   // 16-byte chunks per LDS row
+
+// chunk c of LDS row `row` (BC = 32: 64-byte rows, four per 256-byte bank
+// window): XOR-swizzled so 8 consecutive rows read by an MFMA fragment fall
+// in distinct banks
+__device__ __forceinline__ int lds_off(int row, int c) {
+  const int x = (row >> 2) & (CH - 1);
+  return row * BC + ((c ^ x) << 3);
+}
+
+// An operand of C: element (i, c) at byte offset 2 * (i * ld + c) (c
+// contiguous) or 2 * (c * ld + i) (i contiguous) from `base`, valid for
+// ilo <= i < ihi and c < nc; the others load zeros (an offset past the end,
+// which the buffer range check turns into 0).
+struct Operand {
+  const uint16_t* base;
+  int64_t bytes;      // readable bytes from base (range check)
+  int32_t ld;         // elements between consecutive rows of storage
+  int32_t ilo, ihi;   // valid i
+  int32_t nc;         // valid c
+};
+
+constexpr uint32_t kPast = 0x80000000u;   // an offset past every buffer
+
+// c-contiguous operand: 128 rows x 4 chunks = 512 chunks, two per thread.
+struct RowStager {
+  i32x4 v[2];
+  uint32_t off[2];
+  int row[2], chunk[2];
+  __device__ void setup(const Operand& o, int i0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = threadIdx.x + NT * u;
+      row[u] = q / CH;
+      chunk[u] = q % CH;
+      const int i = i0 + row[u];
+      off[u] = i >= o.ilo && i < o.ihi ? (uint32_t)(((int64_t)i * o.ld + 8 * chunk[u]) * 2) : kPast;
+    }
+  }
+  __device__ void load(const __amdgpu_buffer_rsrc_t& r, int c0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, off[u] == kPast ? kPast : off[u] + 2 * c0, 0, 0);
+  }
+  __device__ void store(uint16_t* lds) const {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) *reinterpret_cast<i32x4*>(lds + lds_off(row[u], chunk[u])) = v[u];
+  }
+};
+
+// i-contiguous operand: thread t takes c rows 2p, 2p+1 (p = t / 16) and the 8
+// i at 8 * (t % 16): 16 lanes read 256 contiguous bytes of one c row.
+struct ColStager {
+  i32x4 v[2];
+  int p, ic;
+  uint32_t ioff;
+  bool ivalid;
+  __device__ void setup(const Operand& o, int i0) {
+    p = threadIdx.x / 16;
+    ic = threadIdx.x % 16;
+    const int i = i0 + 8 * ic;           // i-contiguous extents are multiples of 8
+    ivalid = i >= o.ilo && i < o.ihi;
+    ioff = (uint32_t)(2 * i);
+  }
+  __device__ void load(const __amdgpu_buffer_rsrc_t& r, const Operand& o, int c0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = c0 + 2 * p + u;
+      const uint32_t off = ivalid && c < o.nc ? (uint32_t)((int64_t)c * o.ld * 2) + ioff : kPast;
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    }
+  }
+  // word t: (i = 8 ic + t; c = 2p, 2p+1) -> LDS row i, element 2p of the slice
+  __device__ void store(uint16_t* lds) const {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t a = (uint32_t)v[0][t / 2], b = (uint32_t)v[1][t / 2];
+      const uint32_t w = (t & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+      const int row = 8 * ic + t;
+      *reinterpret_cast<uint32_t*>(lds + lds_off(row, (2 * p) / 8) + (2 * p) % 8) = w;
+    }
+  }
+};
+
+template <bool ACOL, bool BCOL>
+struct Stagers {
+  typename std::conditional<ACOL, ColStager, RowStager>::type a;
+  typename std::conditional<BCOL, ColStager, RowStager>::type b;
+};
+
+template <typename S>
+__device__ __forceinline__ void stage_load(S& s, const __amdgpu_buffer_rsrc_t& r, const Operand& o, int c0) {
+  if constexpr (std::is_same<S, ColStager>::value) s.load(r, o, c0);
+  else s.load(r, c0);
+}
+
+// C tile [i0, i0+128) x [j0, j0+128) over the contraction [0, nc): returns
+// the accumulators.  acc[tw][tx][r]: j = 64 wn + 32 tw + 8 (r/4) + 4 (lane/32)
+// + r%4, i = 64 wm + 32 tx + lane%32.
+template <bool ACOL, bool BCOL>
+__device__ __forceinline__ void tile_mma(const Operand& A, const Operand& B, int i0, int j0, int nc,
+                                         uint16_t (*sA)[BI * BC], uint16_t (*sB)[BJ * BC],
+                                         f32x16 (&acc)[2][2]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wn = wave >> 1, wm = wave & 1;
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(A.base, A.bytes);
+  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(B.base, B.bytes);
+  Stagers<ACOL, BCOL> st;
+  st.a.setup(A, i0);
+  st.b.setup(B, j0);
+#pragma unroll
+  for (int tw = 0; tw < 2; ++tw)
+#pragma unroll
+    for (int tx = 0; tx < 2; ++tx)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[tw][tx][r] = 0.0f;
+  const int ns = (nc + BC - 1) / BC;
+  if (ns == 0) return;
+  const int jrow = 64 * wn + (lane & 31);
+  const int irow = 64 * wm + (lane & 31);
+
+  stage_load(st.a, ra, A, 0);
+  stage_load(st.b, rb, B, 0);
+  st.a.store(sA[0]);
+  st.b.store(sB[0]);
+  lds_barrier();
+  for (int s = 0; s < ns; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < ns) {                       // next slice into registers
+      stage_load(st.a, ra, A, BC * (s + 1));
+      stage_load(st.b, rb, B, BC * (s + 1));
+    }
+#pragma unroll
+    for (int k = 0; k < BC / 16; ++k) {
+      const int c = 2 * k + (lane >> 5);
+      bf16x8 fb[2], fa[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        fb[t] = as_bf16x8(*reinterpret_cast<const i32x4*>(&sB[buf][lds_off(jrow + 32 * t, c)]));
+        fa[t] = as_bf16x8(*reinterpret_cast<const i32x4*>(&sA[buf][lds_off(irow + 32 * t, c)]));
+      }
+#pragma unroll
+      for (int tw = 0; tw < 2; ++tw)
+#pragma unroll
+        for (int tx = 0; tx < 2; ++tx)
+          acc[tw][tx] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[tw], fa[tx], acc[tw][tx], 0, 0, 0);
+    }
+    if (s + 1 < ns) {
+      st.a.store(sA[buf ^ 1]);
+      st.b.store(sB[buf ^ 1]);
+    }
+    lds_barrier();
+  }
+}
+
+// Group e's rows, clamped to [0, R] (a malformed offsets array reads no row
+// outside the buffers).
+__device__ __forceinline__ void group_rows(const TrainArgs& t, int e, int& a, int& b) {
+  a = min(max(t.offsets[e], 0), (int)t.R);
+  b = min(max(t.offsets[e + 1], a), (int)t.R);
+}
+
+// forward / dgrad: C rows are rows r of x / dy, C columns the n / k of the
+// output; a 128-row tile loops over the groups it meets.
+template <int MODE>
+__global__ void __launch_bounds__(NT, 2) train_rows_kernel(TrainArgs t) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BI * BC];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BJ * BC];
+  const int r0 = blockIdx.x * BI;
+  const int j0 = blockIdx.y * BJ;
+  const int ncol = MODE == kTrainForward ? t.N : t.K;   // output columns
+  const int nc = MODE == kTrainForward ? t.K : t.N;     // contraction
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wn = wave >> 1, wm = wave & 1;
+  // first group with rows past r0
+  int lo = 0, hi = t.E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (min(max(t.offsets[mid + 1], 0), (int)t.R) > r0) hi = mid; else lo = mid + 1;
+  }
+  uint16_t* out = static_cast<uint16_t*>(t.out);
+  for (int e = lo; e < t.E; ++e) {
+    int a, b;
+    group_rows(t, e, a, b);
+    if (a >= r0 + BI) break;
+    const int s0 = max(a, r0), s1 = min(b, r0 + BI);
+    if (s1 <= s0) continue;
+    // A: rows [r0, r0 + 128) of x or dy, valid only inside the group
+    Operand A;
+    const uint16_t* arows = MODE == kTrainForward ? t.x : t.dy;
+    A.base = arows + (int64_t)r0 * nc;
+    A.bytes = (int64_t)(s1 - r0) * nc * 2;
+    A.ld = nc;
+    A.ilo = s0 - r0;
+    A.ihi = s1 - r0;
+    A.nc = nc;
+    // B(j, c): forward W[e][n = j][k = c] (c contiguous); dgrad W[e][n = c][k = j]
+    Operand B;
+    B.base = t.w + (int64_t)e * t.N * t.K;
+    B.bytes = (int64_t)t.N * t.K * 2;
+    B.ld = t.K;
+    B.ilo = 0;
+    B.ihi = ncol;
+    B.nc = nc;
+    f32x16 acc[2][2];
+    tile_mma<false, MODE == kTrainDgrad>(A, B, 0, j0, nc, sA, sB, acc);
+#pragma unroll
+    for (int tx = 0; tx < 2; ++tx) {
+      const int r = r0 + 64 * wm + 32 * tx + (lane & 31);
+      if (r < s0 || r >= s1) continue;
+      uint16_t* o = out + (int64_t)r * ncol;
+#pragma unroll
+      for (int tw = 0; tw < 2; ++tw)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          uint32_t v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = f32_to_bf16_rne(acc[tw][tx][4 * h + q]);
+          const int j = j0 + 64 * wn + 32 * tw + 8 * h + 4 * (lane >> 5);
+          *reinterpret_cast<uint2*>(o + j) = make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
+        }
+    }
+  }
+}
+
+// wgrad: C = dW[e] tile [n0, n0+128) x [k0, k0+128), contraction over the
+// group's rows: A(n, r) = dy[r][n], B(k, r) = x[r][k], both i-contiguous.
+__global__ void __launch_bounds__(NT, 2) train_wgrad_kernel(TrainArgs t) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BI * BC];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BJ * BC];
+  const int kt = t.K / BJ;
+  const int n0 = (blockIdx.x / kt) * BI;
+  const int k0 = (blockIdx.x % kt) * BJ;
+  const int e = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wn = wave >> 1, wm = wave & 1;
+  int a, b;
+  group_rows(t, e, a, b);
+  const int m = b - a;
+  Operand A, B;
+  A.base = t.dy + (int64_t)a * t.N;
+  A.bytes = (int64_t)m * t.N * 2;
+  A.ld = t.N;
+  A.ilo = 0;
+  A.ihi = t.N;
+  A.nc = m;
+  B.base = t.x + (int64_t)a * t.K;
+  B.bytes = (int64_t)m * t.K * 2;
+  B.ld = t.K;
+  B.ilo = 0;
+  B.ihi = t.K;
+  B.nc = m;
+  f32x16 acc[2][2];
+  tile_mma<true, true>(A, B, n0, k0, m, sA, sB, acc);
+  float* out = static_cast<float*>(t.out) + (int64_t)e * t.N * t.K;
+#pragma unroll
+  for (int tx = 0; tx < 2; ++tx) {
+    const int n = n0 + 64 * wm + 32 * tx + (lane & 31);
+    float* o = out + (int64_t)n * t.K;
+#pragma unroll
+    for (int tw = 0; tw < 2; ++tw)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int k = k0 + 64 * wn + 32 * tw + 8 * h + 4 * (lane >> 5);
+        f32x4 v = {acc[tw][tx][4 * h], acc[tw][tx][4 * h + 1], acc[tw][tx][4 * h + 2], acc[tw][tx][4 * h + 3]};
+        f32x4* dst = reinterpret_cast<f32x4*>(o + k);
+        if (t.accumulate) {
+          const f32x4 prev = *dst;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = prev[q] + v[q];
+        }
+        *dst = v;
+      }
+  }
+}
+
+}  // namespace train
+
+hipError_t launch_train(const TrainArgs& t, hipStream_t s) {
+  using namespace train;
+  if (t.mode == kTrainWgrad) {
+    hipLaunchKernelGGL(train_wgrad_kernel, dim3((t.N / BI) * (t.K / BJ), t.E), dim3(NT), 0, s, t);
+  } else {
+    if (t.R == 0) return hipSuccess;
+    const int ncol = t.mode == kTrainForward ? t.N : t.K;
+    const dim3 grid((unsigned)((t.R + BI - 1) / BI), ncol / BJ);
+    if (t.mode == kTrainForward)
+      hipLaunchKernelGGL(train_rows_kernel<kTrainForward>, grid, dim3(NT), 0, s, t);
+    else
+      hipLaunchKernelGGL(train_rows_kernel<kTrainDgrad>, grid, dim3(NT), 0, s, t);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

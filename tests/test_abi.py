@@ -154,3 +154,24 @@ def test_fused_plan():
     assert p.ws13_bytes >= p.off_sync + 4 * (32 * (2 + p.max_active) + 4 * p.max_active)
     q = moe.moe_plan_init(moe.make_problem(4, 256, 512, 8, topk=2, variant=moe.VARIANT_STREAM))
     assert q.off_sync == -1
+
+
+# every case fails validation before any launch, so the fake (aligned,
+# non-null) pointers are never dereferenced
+@pytest.mark.parametrize("R,N,K,E,acc,misalign,code", [
+    (1000, 256, 384, 0, 0, 0, moe.MOE_EINVAL), (1000, 256, 384, 65536, 0, 0, moe.MOE_EINVAL),
+    (-1, 256, 384, 8, 0, 0, moe.MOE_EINVAL), (1 << 31, 256, 384, 8, 0, 0, moe.MOE_EINVAL),
+    (1000, 0, 384, 8, 0, 0, moe.MOE_EINVAL), (1000, 200, 384, 8, 0, 0, moe.MOE_EUNSUPPORTED),
+    (1000, 256, 100, 8, 0, 0, moe.MOE_EUNSUPPORTED), (1 << 20, 2048, 128, 8, 0, 0, moe.MOE_EUNSUPPORTED),
+    (1000, 256, 384, 8, 2, 0, moe.MOE_EINVAL), (1000, 256, 384, 8, 0, 8, moe.MOE_EINVAL),
+])
+def test_grouped_validation(R, N, K, E, acc, misalign, code):
+    import ctypes
+    lib = moe.load_library()
+    p = moe.MoeGroupedProblem(R=R, N=N, K=K, E=E)
+    fake = ctypes.c_void_p(1 << 20)
+    out = ctypes.c_void_p((1 << 20) + misalign)
+    assert lib.moe_grouped_wgrad(ctypes.byref(p), fake, fake, fake, out, acc, None) == code
+    if acc == 0:
+        assert lib.moe_grouped_dgrad(ctypes.byref(p), fake, fake, fake, out, None) == code
+        assert lib.moe_grouped_forward(ctypes.byref(p), fake, fake, fake, out, None) == code
