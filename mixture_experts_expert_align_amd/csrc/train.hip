@@ -12,7 +12,8 @@
 //                    ([E, N, K] fp32, written, or added to the fp32 buffer)
 //
 // One kernel computes C[i][j] = sum_c A(i, c) B(j, c) for a 128 x 128 tile
-// of C, the contraction in 32-wide slices staged in LDS (two buffers), four
+// of C, the contraction in 64-wide slices staged in LDS (two buffers; each
+// slice loaded into registers two slices ahead of its LDS store), four
 // waves of 64 x 64 as 2 x 2 tiles of v_mfma_f32_32x32x16_bf16.  Each operand
 // is stored either with c contiguous (x and W for the forward, dy for dgrad)
 // or with its own index contiguous (W for dgrad, dy and x for wgrad): MFMA
@@ -35,15 +36,18 @@
 namespace moe {
 namespace train {
 
-constexpr int BI = 128, BJ = 128, BC = 32;   // tile of C, contraction slice
+constexpr int BI = 128, BJ = 128, BC = 64;   // tile of C, contraction slice
 constexpr int NT = 256;                      // 4 waves: 2 (j) x 2 (i) of 64 x 64
 constexpr int CH = BC / 8;                   // 16-byte chunks per LDS row
+constexpr int RPW = 256 / (BC * 2);          // LDS rows per 256-byte bank window
 
-// chunk c of LDS row `row` (BC = 32: 64-byte rows, four per 256-byte bank
-// window): XOR-swizzled so 8 consecutive rows read by an MFMA fragment fall
-// in distinct banks
+// chunk c of LDS row `row`, XOR-swizzled.  (row / RPW) puts the 8
+// consecutive rows one 128-byte quarter of an MFMA fragment read touches in
+// distinct banks; (row / 16), constant over such 8 rows, spreads the
+// transposed stores, whose 16 lanes of one c pair write rows 8 apart (with
+// the first term alone they met in 2 chunks, an 8-way bank conflict).
 __device__ __forceinline__ int lds_off(int row, int c) {
-  const int x = (row >> 2) & (CH - 1);
+  const int x = ((row / RPW) ^ (row / 16)) & (CH - 1);
   return row * BC + ((c ^ x) << 3);
 }
 
@@ -61,14 +65,18 @@ struct Operand {
 
 constexpr uint32_t kPast = 0x80000000u;   // an offset past every buffer
 
-// c-contiguous operand: 128 rows x 4 chunks = 512 chunks, two per thread.
+// Each stager keeps two register sets: slice t is loaded into set t % 2 two
+// slices before its LDS store, so each load has two slices of MFMAs to land.
+
+// c-contiguous operand: 128 rows x CH chunks, NU per thread.
 struct RowStager {
-  i32x4 v[2];
-  uint32_t off[2];
-  int row[2], chunk[2];
+  static constexpr int NU = BI * CH / NT;
+  i32x4 v[2][NU];
+  uint32_t off[NU];
+  int row[NU], chunk[NU];
   __device__ void setup(const Operand& o, int i0) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < NU; ++u) {
       const int q = threadIdx.x + NT * u;
       row[u] = q / CH;
       chunk[u] = q % CH;
@@ -76,47 +84,53 @@ struct RowStager {
       off[u] = i >= o.ilo && i < o.ihi ? (uint32_t)(((int64_t)i * o.ld + 8 * chunk[u]) * 2) : kPast;
     }
   }
-  __device__ void load(const __amdgpu_buffer_rsrc_t& r, int c0) {
+  __device__ void load(int set, const __amdgpu_buffer_rsrc_t& r, const Operand&, int c0) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-      v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, off[u] == kPast ? kPast : off[u] + 2 * c0, 0, 0);
+    for (int u = 0; u < NU; ++u)
+      v[set][u] = __builtin_amdgcn_raw_buffer_load_b128(r, off[u] == kPast ? kPast : off[u] + 2 * c0, 0, 0);
   }
-  __device__ void store(uint16_t* lds) const {
+  __device__ void store(int set, uint16_t* lds) const {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) *reinterpret_cast<i32x4*>(lds + lds_off(row[u], chunk[u])) = v[u];
+    for (int u = 0; u < NU; ++u) *reinterpret_cast<i32x4*>(lds + lds_off(row[u], chunk[u])) = v[set][u];
   }
 };
 
-// i-contiguous operand: thread t takes c rows 2p, 2p+1 (p = t / 16) and the 8
-// i at 8 * (t % 16): 16 lanes read 256 contiguous bytes of one c row.
+// i-contiguous operand: a block is two c rows (2p, 2p+1) x 8 consecutive i;
+// thread t takes i chunk t % 16 of c pairs p = t / 16 + 16 u: 16 lanes read
+// 256 contiguous bytes of one c row.
 struct ColStager {
-  i32x4 v[2];
-  int p, ic;
+  static constexpr int NU = (BC / 2) * 16 / NT;
+  i32x4 v[2][NU][2];
+  int ic;
   uint32_t ioff;
   bool ivalid;
   __device__ void setup(const Operand& o, int i0) {
-    p = threadIdx.x / 16;
     ic = threadIdx.x % 16;
     const int i = i0 + 8 * ic;           // i-contiguous extents are multiples of 8
     ivalid = i >= o.ilo && i < o.ihi;
     ioff = (uint32_t)(2 * i);
   }
-  __device__ void load(const __amdgpu_buffer_rsrc_t& r, const Operand& o, int c0) {
+  __device__ void load(int set, const __amdgpu_buffer_rsrc_t& r, const Operand& o, int c0) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int c = c0 + 2 * p + u;
-      const uint32_t off = ivalid && c < o.nc ? (uint32_t)((int64_t)c * o.ld * 2) + ioff : kPast;
-      v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    }
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = c0 + 2 * (threadIdx.x / 16 + 16 * u) + h;
+        const uint32_t off = ivalid && c < o.nc ? (uint32_t)((int64_t)c * o.ld * 2) + ioff : kPast;
+        v[set][u][h] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+      }
   }
-  // word t: (i = 8 ic + t; c = 2p, 2p+1) -> LDS row i, element 2p of the slice
-  __device__ void store(uint16_t* lds) const {
+  // word t of block u: (i = 8 ic + t; c = 2p, 2p+1) -> LDS row i, element 2p
+  __device__ void store(int set, uint16_t* lds) const {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const uint32_t a = (uint32_t)v[0][t / 2], b = (uint32_t)v[1][t / 2];
-      const uint32_t w = (t & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-      const int row = 8 * ic + t;
-      *reinterpret_cast<uint32_t*>(lds + lds_off(row, (2 * p) / 8) + (2 * p) % 8) = w;
+    for (int u = 0; u < NU; ++u) {
+      const int p = threadIdx.x / 16 + 16 * u;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t a = (uint32_t)v[set][u][0][t / 2], b = (uint32_t)v[set][u][1][t / 2];
+        const uint32_t w = (t & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+        *reinterpret_cast<uint32_t*>(lds + lds_off(8 * ic + t, (2 * p) / 8) + (2 * p) % 8) = w;
+      }
     }
   }
 };
@@ -126,12 +140,6 @@ struct Stagers {
   typename std::conditional<ACOL, ColStager, RowStager>::type a;
   typename std::conditional<BCOL, ColStager, RowStager>::type b;
 };
-
-template <typename S>
-__device__ __forceinline__ void stage_load(S& s, const __amdgpu_buffer_rsrc_t& r, const Operand& o, int c0) {
-  if constexpr (std::is_same<S, ColStager>::value) s.load(r, o, c0);
-  else s.load(r, c0);
-}
 
 // C tile [i0, i0+128) x [j0, j0+128) over the contraction [0, nc): returns
 // the accumulators.  acc[tw][tx][r]: j = 64 wn + 32 tw + 8 (r/4) + 4 (lane/32)
@@ -159,17 +167,17 @@ __device__ __forceinline__ void tile_mma(const Operand& A, const Operand& B, int
   const int jrow = 64 * wn + (lane & 31);
   const int irow = 64 * wm + (lane & 31);
 
-  stage_load(st.a, ra, A, 0);
-  stage_load(st.b, rb, B, 0);
-  st.a.store(sA[0]);
-  st.b.store(sB[0]);
-  lds_barrier();
-  for (int s = 0; s < ns; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < ns) {                       // next slice into registers
-      stage_load(st.a, ra, A, BC * (s + 1));
-      stage_load(st.b, rb, B, BC * (s + 1));
-    }
+  // set `set` <- slice kt (past the end: the last slice again, unused)
+  auto gload = [&](int set, int kt) {
+    const int c0 = BC * min(kt, ns - 1);
+    st.a.load(set, ra, A, c0);
+    st.b.load(set, rb, B, c0);
+  };
+  auto sstore = [&](int buf, int set) {
+    st.a.store(set, sA[buf]);
+    st.b.store(set, sB[buf]);
+  };
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int k = 0; k < BC / 16; ++k) {
       const int c = 2 * k + (lane >> 5);
@@ -185,12 +193,31 @@ __device__ __forceinline__ void tile_mma(const Operand& A, const Operand& B, int
         for (int tx = 0; tx < 2; ++tx)
           acc[tw][tx] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[tw], fa[tx], acc[tw][tx], 0, 0, 0);
     }
-    if (s + 1 < ns) {
-      st.a.store(sA[buf ^ 1]);
-      st.b.store(sB[buf ^ 1]);
-    }
+  };
+  // slice kt sits in LDS buffer p (= kt % 2): multiply it, store slice kt+1
+  // (register set p ^ 1) to the other buffer, refill that set with kt+3
+  auto step = [&](int p, int kt) {
+    compute(p);
+    __builtin_amdgcn_sched_barrier(0);
+    sstore(p ^ 1, p ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    gload(p ^ 1, kt + 3);
+    __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
+  };
+
+  gload(0, 0);
+  gload(1, 1);
+  sstore(0, 0);
+  gload(0, 2);
+  lds_barrier();
+  int kt = 0;
+  for (; kt + 2 <= ns; kt += 2) {
+    step(0, kt);
+    step(1, kt + 1);
   }
+  if (kt < ns) compute(0);
+  lds_barrier();   // every wave is done with LDS before it is reused
 }
 
 // Group e's rows, clamped to [0, R] (a malformed offsets array reads no row
