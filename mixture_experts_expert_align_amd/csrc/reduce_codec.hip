@@ -19,6 +19,7 @@ namespace moe {
 namespace {
 
 constexpr int NT = 256;
+constexpr int kBatch = 8;   // reduce terms whose loads are issued together
 
 __device__ __forceinline__ void fma8(float* acc, float w, i32x4 v) {
 #pragma unroll
@@ -37,6 +38,16 @@ __device__ __forceinline__ i32x4 pack8(const float* acc) {
   return o;
 }
 
+// One workgroup per token and span of NT * cpt chunks of 8 columns: the
+// token's slots are read once per thread, then each thread reduces up to cpt
+// (<= kChunks) chunks of its columns — more per thread for many tokens (the
+// slot reads amortised), one for few (more workgroups in flight).  Slots go
+// in batches of kBatch: all ids,
+// then all map entries, then every valid slot's row, then the FMAs in
+// ascending slot order (the same sum as one slot at a time, without a chain
+// of dependent loads per slot).
+constexpr int kChunks = 4;
+
 __global__ void __launch_bounds__(NT) reduce_contiguous_kernel(const uint16_t* __restrict__ y,
                                                                const int32_t* __restrict__ ids,
                                                                const float* __restrict__ w,
@@ -44,45 +55,90 @@ __global__ void __launch_bounds__(NT) reduce_contiguous_kernel(const uint16_t* _
                                                                uint16_t* __restrict__ out, int64_t M,
                                                                int topk, int64_t K, int E,
                                                                int32_t* __restrict__ sync_zero,
-                                                               int64_t sync_lines) {
-  if (sync_zero && blockIdx.x == 0)
+                                                               int64_t sync_lines, int cpt) {
+  if (sync_zero && blockIdx.x == 0 && blockIdx.y == 0)
     for (int64_t i = threadIdx.x; i < sync_lines; i += NT) sync_zero[32 * i] = 0;
+  const int64_t t = blockIdx.x;
   const int64_t K8 = K / 8;
-  const int64_t idx = (int64_t)blockIdx.x * NT + threadIdx.x;
-  if (idx >= M * K8) return;
-  const int64_t t = idx / K8;
-  const int64_t c = (idx - t * K8) * 8;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < topk; ++j) {
-    const int64_t s = t * topk + j;
-    int id = ids[s];
-    if (emap) id = (id >= 0 && id < G) ? emap[id] : -1;   // global -> local (-1: held elsewhere)
-    if (id < 0 || id >= E) continue;
-    const i32x4 v = *reinterpret_cast<const i32x4*>(y + s * K + c);
-    fma8(acc, w[s], v);
+  const int64_t cbeg = (int64_t)blockIdx.y * NT * cpt + threadIdx.x;
+  float acc[kChunks][8];
+#pragma unroll
+  for (int u = 0; u < kChunks; ++u)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[u][q] = 0.f;
+  for (int j0 = 0; j0 < topk; j0 += kBatch) {
+    const int64_t s0 = t * topk + j0;
+    int id[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) id[q] = j0 + q < topk ? ids[s0 + q] : -1;
+    if (emap) {
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) id[q] = (id[q] >= 0 && id[q] < G) ? emap[id[q]] : -1;   // global -> local
+    }
+    float wt[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) wt[q] = id[q] >= 0 && id[q] < E ? w[s0 + q] : 0.f;
+#pragma unroll
+    for (int u = 0; u < kChunks; ++u) {
+      const int64_t c = cbeg + (int64_t)NT * u;
+      if (u >= cpt || c >= K8) break;
+      i32x4 v[kBatch];
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q)
+        if (id[q] >= 0 && id[q] < E) v[q] = *reinterpret_cast<const i32x4*>(y + (s0 + q) * K + 8 * c);
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q)
+        if (id[q] >= 0 && id[q] < E) fma8(acc[u], wt[q], v[q]);
+    }
   }
-  *reinterpret_cast<i32x4*>(out + t * K + c) = pack8(acc);
+#pragma unroll
+  for (int u = 0; u < kChunks; ++u) {
+    const int64_t c = cbeg + (int64_t)NT * u;
+    if (u < cpt && c < K8) *reinterpret_cast<i32x4*>(out + t * K + 8 * c) = pack8(acc[u]);
+  }
 }
 
+// The same layout for the batched format's CSR list of each output token.
 __global__ void __launch_bounds__(NT) reduce_csr_kernel(const uint16_t* __restrict__ y,
                                                         const float* __restrict__ w,
                                                         const int32_t* __restrict__ offsets,
                                                         const int32_t* __restrict__ rows,
                                                         uint16_t* __restrict__ out, int64_t n_out,
-                                                        int64_t K) {
+                                                        int64_t K, int cpt) {
+  const int64_t t = blockIdx.x;
   const int64_t K8 = K / 8;
-  const int64_t idx = (int64_t)blockIdx.x * NT + threadIdx.x;
-  if (idx >= n_out * K8) return;
-  const int64_t t = idx / K8;
-  const int64_t c = (idx - t * K8) * 8;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int64_t cbeg = (int64_t)blockIdx.y * NT * cpt + threadIdx.x;
+  float acc[kChunks][8];
+#pragma unroll
+  for (int u = 0; u < kChunks; ++u)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[u][q] = 0.f;
   const int b = offsets[t], e = offsets[t + 1];
-  for (int i = b; i < e; ++i) {
-    const int64_t r = rows[i];
-    const i32x4 v = *reinterpret_cast<const i32x4*>(y + r * K + c);
-    fma8(acc, w[r], v);
+  for (int i0 = b; i0 < e; i0 += kBatch) {
+    int64_t r[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) r[q] = i0 + q < e ? rows[i0 + q] : -1;
+    float wt[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) wt[q] = r[q] >= 0 ? w[r[q]] : 0.f;
+#pragma unroll
+    for (int u = 0; u < kChunks; ++u) {
+      const int64_t c = cbeg + (int64_t)NT * u;
+      if (u >= cpt || c >= K8) break;
+      i32x4 v[kBatch];
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q)
+        if (r[q] >= 0) v[q] = *reinterpret_cast<const i32x4*>(y + r[q] * K + 8 * c);
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q)
+        if (r[q] >= 0) fma8(acc[u], wt[q], v[q]);
+    }
   }
-  *reinterpret_cast<i32x4*>(out + t * K + c) = pack8(acc);
+#pragma unroll
+  for (int u = 0; u < kChunks; ++u) {
+    const int64_t c = cbeg + (int64_t)NT * u;
+    if (u < cpt && c < K8) *reinterpret_cast<i32x4*>(out + t * K + 8 * c) = pack8(acc[u]);
+  }
 }
 
 // Quantise one 32-element block held in v[0..31].
@@ -167,22 +223,35 @@ __global__ void __launch_bounds__(NT) quantize_gather_kernel(
 
 inline unsigned nblocks(int64_t n) { return (unsigned)((n + NT - 1) / NT); }
 
+// Chunks per thread of the reduces: as many (up to kChunks) as keep about
+// 2048 workgroups (eight per CU) in the grid.
+inline int reduce_cpt(int64_t rows, int64_t K8) {
+  int cpt = 1;
+  while (cpt < kChunks && rows * ((K8 + NT * 2 * cpt - 1) / (NT * 2 * cpt)) >= 2048) cpt *= 2;
+  return cpt;
+}
+
 }  // namespace
 
 hipError_t launch_reduce_contiguous(const uint16_t* y, const int32_t* ids, const float* w,
                                     const int32_t* expert_map, int32_t G, uint16_t* out, int64_t M,
                                     int32_t topk, int64_t K, int32_t E, int32_t* sync_zero,
                                     int64_t sync_lines, hipStream_t s) {
-  hipLaunchKernelGGL(reduce_contiguous_kernel, dim3(nblocks(M * (K / 8))), dim3(NT), 0, s, y, ids, w,
-                     expert_map, G, out, M, topk, K, E, sync_zero, sync_lines);
+  if (M == 0) return hipSuccess;
+  const int cpt = reduce_cpt(M, K / 8);
+  const dim3 grid((unsigned)M, (unsigned)((K / 8 + NT * cpt - 1) / (NT * cpt)));
+  hipLaunchKernelGGL(reduce_contiguous_kernel, grid, dim3(NT), 0, s, y, ids, w, expert_map, G, out, M,
+                     topk, K, E, sync_zero, sync_lines, cpt);
   return hipGetLastError();
 }
 
 hipError_t launch_reduce_csr(const uint16_t* y, const float* w, const int32_t* offsets,
                              const int32_t* rows, uint16_t* out, int64_t n_out, int64_t K,
                              hipStream_t s) {
-  hipLaunchKernelGGL(reduce_csr_kernel, dim3(nblocks(n_out * (K / 8))), dim3(NT), 0, s, y, w, offsets,
-                     rows, out, n_out, K);
+  if (n_out == 0) return hipSuccess;
+  const int cpt = reduce_cpt(n_out, K / 8);
+  const dim3 grid((unsigned)n_out, (unsigned)((K / 8 + NT * cpt - 1) / (NT * cpt)));
+  hipLaunchKernelGGL(reduce_csr_kernel, grid, dim3(NT), 0, s, y, w, offsets, rows, out, n_out, K, cpt);
   return hipGetLastError();
 }
 
