@@ -76,10 +76,16 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // CS: steps per chunk (4, 2 or 1, dividing the contraction's step count);
-// the weights stream CS steps ahead.
-template <int EPI, int CS>
+// the weights stream CS steps ahead.  TT: 16-row weight tiles per wave (2
+// for W1: each staged activation fragment then feeds two MFMAs, and the
+// workgroup's 256 weight rows amortise the activation staging, which costs
+// the address unit as many lane requests per byte as the weights do).
+template <int EPI, int CS, int TT>
 __global__ void __launch_bounds__(64 * kMxWaves, 4) gemm_stream_mxfp8_kernel(GemmArgs g) {
   constexpr int kChunk = CS * kMxStepA + kMxWaves * kMxStepAS;   // one LDS buffer
+  // the W1 epilogue gathers every wave's accumulators ([wave][tile][token tile][lane])
+  constexpr int kOutBytes = EPI == kEpiGateUp ? kMxWaves * TT * 4 * 64 * 16 : 0;
+  constexpr int kLds = 2 * kChunk > kOutBytes ? 2 * kChunk : kOutBytes;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const RowMap& rm = g.rows;
@@ -92,7 +98,7 @@ __global__ void __launch_bounds__(64 * kMxWaves, 4) gemm_stream_mxfp8_kernel(Gem
   const int KB = K / 32;
   const int q = lane >> 4;
   const int l16 = lane & 15;
-  const int f0 = blockIdx.x * (EPI == kEpiGateUp ? 64 : 128);
+  const int f0 = blockIdx.x * (EPI == kEpiGateUp ? 64 : 128) * TT;
   const int nsteps = K / 128;
   const int nchunks = nsteps / CS;
 
@@ -102,18 +108,25 @@ __global__ void __launch_bounds__(64 * kMxWaves, 4) gemm_stream_mxfp8_kernel(Gem
   const __amdgpu_buffer_rsrc_t wsr = buffer_rsrc(wsexp, g.w_expert_stride / 32);
   const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(g.act, g.act_bytes);
   const __amdgpu_buffer_rsrc_t asr = buffer_rsrc(g.act_scale, g.act_bytes / 32);
-  const int row = EPI == kEpiGateUp ? w1_row(f0 + 16 * (wave >> 1) + l16, (wave & 1) != 0, g.I, g.w1_order)
-                                    : f0 + 16 * wave + l16;
-  const uint32_t wo = (uint32_t)(row * K + 16 * q);     // lane: row l16, bytes 16q of a step (+64)
+  // tile tt of wave w: W1 gate (w even) or up (w odd) rows of features
+  // f0 + 16 (TT (w / 2) + tt) + l16; W2 rows f0 + 16 (TT w + tt) + l16
+  uint32_t wo[TT], wso[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    const int row = EPI == kEpiGateUp
+                        ? w1_row(f0 + 16 * (TT * (wave >> 1) + tt) + l16, (wave & 1) != 0, g.I, g.w1_order)
+                        : f0 + 16 * (TT * wave + tt) + l16;
+    wo[tt] = (uint32_t)(row * K + 16 * q);     // lane: row l16, bytes 16q of a step (+64)
+    wso[tt] = (uint32_t)(row * KB + 16 * q);
+  }
   // weight scales, 16 steps at a time: lane (row l16, group q) loads the 4
   // words of steps 4q .. 4q+3 of a 16-step group (16 bytes), and each step
   // takes its word from the lane that holds it (one load per chunk instead
   // of one per step: every load instruction costs the address unit 64 lane
   // requests, whatever its width)
-  const uint32_t wso = (uint32_t)(row * KB + 16 * q);
   const int ngroups = (nsteps + 15) / 16;
 
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2 * kChunk];
+  __shared__ __attribute__((aligned(16))) uint8_t sA[kLds];
   // within a buffer: step sub's codes at sub * kMxStepA, laid out [token tile
   // c][half j][lane] (1 KB blocks: lane i holds token 16c + i % 16, bytes
   // 64j + 16 (i / 16) of the step), then one 256-byte slot per wave: wave w
@@ -136,28 +149,39 @@ __global__ void __launch_bounds__(64 * kMxWaves, 4) gemm_stream_mxfp8_kernel(Gem
         lds_load16(ar, base + sub * kMxStepA + wave * 1024, xo, (ch * CS + sub) * 128);
       lds_load4(asr, base + CS * kMxStepA + wave * kMxStepAS, xso, (ch * CS + ssub) * 4);
     };
-    // 2 loads: the weights of step st into register set i
-    i32x8 wa[CS];
+    // 2 TT loads: the weights of step st into register set i
+    i32x8 wa[CS][TT];
     auto wload = [&](int i, int st) {
       const int k = st * 128;
-      const i32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(wr, wo, k, 0);
-      const i32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(wr, wo + 64, k, 0);
-      wa[i] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    };
-    // 1 load: the scale words of 16-step group gi (past the end: the last)
-    auto sload = [&](int gi) {
-      return __builtin_amdgcn_raw_buffer_load_b128(wsr, wso, 64 * min(gi, ngroups - 1), 0);
-    };
-    i32x4 scur, snext;   // the current chunk's group, the next chunk's
-    f32x4 acc[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int tt = 0; tt < TT; ++tt) {
+        const i32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(wr, wo[tt], k, 0);
+        const i32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(wr, wo[tt] + 64, k, 0);
+        wa[i][tt] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+    };
+    // TT loads: the scale words of 16-step group gi (past the end: the last)
+    i32x4 scur[TT], snext[TT];   // the current chunk's group, the next chunk's
+    auto sload = [&](int gi) {
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+        snext[tt] = __builtin_amdgcn_raw_buffer_load_b128(wsr, wso[tt], 64 * min(gi, ngroups - 1), 0);
+    };
+    f32x4 acc[TT][4];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[tt][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
     auto mma = [&](int i, int buf, int sub, int st) {
       const uint8_t* base = sA + buf * kChunk;
       // step st is word st % 4 of the lanes of group q = (st % 16) / 4
       const int w4 = st & 3;
-      const int word = w4 == 0 ? scur[0] : w4 == 1 ? scur[1] : w4 == 2 ? scur[2] : scur[3];
-      const uint32_t wsw = (uint32_t)__shfl(word, l16 + 16 * ((st & 15) >> 2));
+      uint32_t wsw[TT];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        const int word = w4 == 0 ? scur[tt][0] : w4 == 1 ? scur[tt][1] : w4 == 2 ? scur[tt][2] : scur[tt][3];
+        wsw[tt] = (uint32_t)__shfl(word, l16 + 16 * ((st & 15) >> 2));
+      }
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const i32x4 xl = *reinterpret_cast<const i32x4*>(base + sub * kMxStepA + (2 * c) * 1024 + 16 * lane);
@@ -165,16 +189,19 @@ __global__ void __launch_bounds__(64 * kMxWaves, 4) gemm_stream_mxfp8_kernel(Gem
         const i32x8 xb = (i32x8){xl[0], xl[1], xl[2], xl[3], xh[0], xh[1], xh[2], xh[3]};
         const uint32_t xsw =   // wave sub's slot holds step sub
             *reinterpret_cast<const uint32_t*>(base + CS * kMxStepA + sub * kMxStepAS + 4 * (16 * c + l16));
-        acc[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa[i], xb, acc[c], 0, 0, 0,
-                                                                 (int)(wsw >> (8 * q)), 0, (int)(xsw >> (8 * q)));
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+          acc[tt][c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              wa[i][tt], xb, acc[tt][c], 0, 0, 0, (int)(wsw[tt] >> (8 * q)), 0, (int)(xsw >> (8 * q)));
       }
     };
     // the CS steps of chunk ch (LDS buffer buf): multiply step s, then load
     // the weights of step s + CS into the freed register set (past the end:
     // the last step again, unused)
     auto chunk = [&](int ch, int buf) {
-      scur = snext;                                   // loaded a chunk ago
-      snext = sload(((ch + 1) * CS) / 16);
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) scur[tt] = snext[tt];   // loaded a chunk ago
+      sload(((ch + 1) * CS) / 16);
       issue_order();
 #pragma unroll
       for (int sub = 0; sub < CS; ++sub) {
@@ -189,7 +216,7 @@ __global__ void __launch_bounds__(64 * kMxWaves, 4) gemm_stream_mxfp8_kernel(Gem
     // staged (the loop's issue order: weights, then the next staging)
     stage(0, 0);
     issue_order();
-    snext = sload(0);
+    sload(0);
     issue_order();
 #pragma unroll
     for (int sub = 0; sub < CS; ++sub) {
@@ -198,17 +225,17 @@ __global__ void __launch_bounds__(64 * kMxWaves, 4) gemm_stream_mxfp8_kernel(Gem
     }
     stage(min(1, nchunks - 1), 1);
     issue_order();
-    // chunk 0's loads are older than the scale group's (1), the weights' (2 CS)
-    // and chunk 1's (CS + 1)
-    wait_vm<3 * CS + 2>();
+    // chunk 0's loads are older than the scale groups' (TT), the weights'
+    // (2 TT CS) and chunk 1's (CS + 1)
+    wait_vm<TT + 2 * TT * CS + CS + 1>();
     lds_barrier();
     for (int ch = 0; ch + 1 < nchunks; ++ch) {
       const int buf = ch & 1;
       chunk(ch, buf);
-      // chunk ch+1's staging loads are older than the scale group and the 2 CS
-      // weight loads of this chunk; then every wave's share is in place and
-      // chunk ch is read
-      wait_vm<2 * CS + 1>();
+      // chunk ch+1's staging loads are older than the TT scale groups and
+      // the 2 TT CS weight loads of this chunk; then every wave's share is in
+      // place and chunk ch is read
+      wait_vm<TT + 2 * TT * CS>();
       lds_barrier();
       stage(min(ch + 2, nchunks - 1), buf);   // past the end: reloads the last chunk, unused
       issue_order();
@@ -218,17 +245,31 @@ __global__ void __launch_bounds__(64 * kMxWaves, 4) gemm_stream_mxfp8_kernel(Gem
     wait_vm<0>();
     lds_barrier();
 
-    // acc[c][r]: weight row 4*q + r of this wave's tile, token tg*64 + 16*c + l16
+    // acc[tt][c][r]: weight row 4*q + r of this wave's tile tt, token
+    // tg*64 + 16*c + l16
     if (EPI == kEpiGateUp) {
-      f32x4* sOut = reinterpret_cast<f32x4*>(sA);      // [wave][token tile][lane]
+      f32x4* sOut = reinterpret_cast<f32x4*>(sA);      // [wave][tile][token tile][lane]
 #pragma unroll
-      for (int c = 0; c < 4; ++c) sOut[(wave * 4 + c) * 64 + lane] = acc[c];
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sOut[((wave * TT + tt) * 4 + c) * 64 + lane] = acc[tt][c];
       lds_barrier();
-      // wave w finishes token tile c = w % 4 of MX block b = w / 4 (features
-      // f0 + 32 b .. +31: gate/up tiles of waves 4b .. 4b+3)
-      const int c = wave & 3, b = wave >> 2;
-      const f32x4 g0 = sOut[((4 * b + 0) * 4 + c) * 64 + lane], u0 = sOut[((4 * b + 1) * 4 + c) * 64 + lane];
-      const f32x4 g1 = sOut[((4 * b + 2) * 4 + c) * 64 + lane], u1 = sOut[((4 * b + 3) * 4 + c) * 64 + lane];
+      // units (MX block b = features f0 + 32 b .. +31, token tile c): 8 TT
+      // of them, wave w finishes units w + 8 v (v < TT), unit u being
+      // (b, c) = (u / 4, u % 4).  The gate rows of features 32 b + 16 h +
+      // (0..15) are tile h' of wave gw and the up rows tile h' of wave gw + 1,
+      // with (gw, h') = (4 b + 2 h, 0) for TT = 1 and (2 b, h) for TT = 2.
+#pragma unroll
+      for (int v = 0; v < TT; ++v) {
+      const int unit = wave + kMxWaves * v;
+      const int c = unit & 3, b = unit >> 2;
+      auto tile = [&](int h, int up) {
+        const int gw = TT == 1 ? 4 * b + 2 * h : 2 * b;
+        const int ht = TT == 1 ? 0 : h;
+        return sOut[(((gw + up) * TT + ht) * 4 + c) * 64 + lane];
+      };
+      const f32x4 g0 = tile(0, 0), u0 = tile(0, 1);
+      const f32x4 g1 = tile(1, 0), u1 = tile(1, 1);
       float z[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -258,17 +299,21 @@ __global__ void __launch_bounds__(64 * kMxWaves, 4) gemm_stream_mxfp8_kernel(Gem
         *reinterpret_cast<uint32_t*>(o + fb + 16 + 4 * q) = w1;
         if (q == 0) g.out_scale[pos * (g.out_ld / 32) + fb / 32] = (uint8_t)sc;
       }
+      }
     } else {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int t = tg * kMxTok + 16 * c + l16;
         if (t < cnt) {
           const int64_t orow = rm.sorted_ids[pos0 + t];
-          uint16_t* o = static_cast<uint16_t*>(g.out) + orow * g.out_ld + f0 + 16 * wave + 4 * q;
-          uint32_t h[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(acc[c][r]);
-          *reinterpret_cast<uint2*>(o) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+          for (int tt = 0; tt < TT; ++tt) {
+            uint16_t* o = static_cast<uint16_t*>(g.out) + orow * g.out_ld + f0 + 16 * (TT * wave + tt) + 4 * q;
+            uint32_t h[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(acc[tt][c][r]);
+            *reinterpret_cast<uint2*>(o) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+          }
         }
       }
     }
@@ -280,16 +325,23 @@ __global__ void __launch_bounds__(64 * kMxWaves, 4) gemm_stream_mxfp8_kernel(Gem
 
 template <int EPI>
 static hipError_t launch_mxfp8(const GemmArgs& g, hipStream_t s) {
-  const dim3 grid(g.nfeat / (EPI == kEpiGateUp ? 64 : 128), (unsigned)g.max_active);
   const int nsteps = g.kdim / 128;
-  // W2 keeps chunks of 2 steps: with 4 its epilogue's registers no longer
-  // fit the 128 that let two workgroups share a CU
+  // W1: two tiles per wave (128 features per workgroup) and chunks of 2
+  // steps when the features divide; W2 keeps one tile and chunks of 2 steps:
+  // with more, its epilogue's registers no longer fit the 128 that let two
+  // workgroups share a CU
+  if (EPI == kEpiGateUp && g.nfeat % 128 == 0 && nsteps % 2 == 0) {
+    const dim3 grid(g.nfeat / 128, (unsigned)g.max_active);
+    hipLaunchKernelGGL((gemm_stream_mxfp8_kernel<kEpiGateUp, 2, 2>), grid, dim3(64 * kMxWaves), 0, s, g);
+    return hipGetLastError();
+  }
+  const dim3 grid(g.nfeat / (EPI == kEpiGateUp ? 64 : 128), (unsigned)g.max_active);
   if (EPI == kEpiGateUp && nsteps % 4 == 0)
-    hipLaunchKernelGGL((gemm_stream_mxfp8_kernel<kEpiGateUp, 4>), grid, dim3(64 * kMxWaves), 0, s, g);
+    hipLaunchKernelGGL((gemm_stream_mxfp8_kernel<kEpiGateUp, 4, 1>), grid, dim3(64 * kMxWaves), 0, s, g);
   else if (nsteps % 2 == 0)
-    hipLaunchKernelGGL((gemm_stream_mxfp8_kernel<EPI, 2>), grid, dim3(64 * kMxWaves), 0, s, g);
+    hipLaunchKernelGGL((gemm_stream_mxfp8_kernel<EPI, 2, 1>), grid, dim3(64 * kMxWaves), 0, s, g);
   else
-    hipLaunchKernelGGL((gemm_stream_mxfp8_kernel<EPI, 1>), grid, dim3(64 * kMxWaves), 0, s, g);
+    hipLaunchKernelGGL((gemm_stream_mxfp8_kernel<EPI, 1, 1>), grid, dim3(64 * kMxWaves), 0, s, g);
   return hipGetLastError();
 }
 
