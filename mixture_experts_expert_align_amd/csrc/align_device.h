@@ -143,7 +143,9 @@ __device__ void scatter_range(const AlignArgs& a, int64_t begin, int64_t end, in
     int rank, gsize;
     bool last;
     wave_match_rank(kr.key, kr.valid, a.nbits, rank, gsize, last);
-    for (int w = 0; w < nwaves; ++w) {
+    // only the waves that hold keys of this block take a turn
+    const int nturns = (int)min<int64_t>(nwaves, (end - base + kWave - 1) / kWave);
+    for (int w = 0; w < nturns; ++w) {
       if (w == wave && kr.valid) {
         const int b0 = s_cur[kr.key];
         a.sorted[b0 + rank] = (int32_t)i;
