@@ -58,7 +58,7 @@ __device__ __forceinline__ int lds_off(int row, int c) {
 struct TileCoord {
   int expert, col0;
   int64_t row0;   // contiguous: sorted position; batched: slab row e*max_tokens + r0
-  int nvalid;     // route rows of the tile that exist (batched); BM for contiguous
+  int nvalid;     // route rows of the tile that exist (the rest are padding)
 };
 
 __host__ __device__ inline int64_t padded_blocks(int64_t nlog) {
@@ -94,7 +94,8 @@ __device__ __forceinline__ bool tile_coord(const GemmArgs& g, int ncol, int64_t 
       tc.col0 = (int)(local / ne) * BN;
       tc.row0 = (t0 + local % ne) * BM;
     }
-    tc.nvalid = BM;
+    // the expert's run holds counts[lo] routes, then padding to a tile
+    tc.nvalid = (int)max<int64_t>(0, min<int64_t>(BM, rm.counts[lo] - (tc.row0 - rm.offsets[lo])));
     return true;
   }
   const int tpe = (rm.max_tokens + BM - 1) / BM;
@@ -207,6 +208,11 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmA
     }
   }
   const int xrow_l = wm * (BM / WM) + (lane & 31);
+  // a wave whose route rows all lie past the tile's valid rows holds only
+  // padding: it skips its fragment reads and MFMAs (its accumulators stay 0,
+  // what zero-filled padding rows would give) but still stages and meets
+  // the barriers; a wave-uniform branch
+  const bool wlive = __builtin_amdgcn_readfirstlane(wm) * (BM / WM) < tc.nvalid;
 
   f32x16 acc[TW][TX];
 #pragma unroll
@@ -227,6 +233,7 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmA
       fx[fb][j] = as_bf16x8(*reinterpret_cast<const i32x4*>(&sX[buf][lds_off<BK>(xrow_l + 32 * j, c)]));
   };
   auto compute = [&](int buf) {
+    if (!wlive) return;
     fload(0, buf, 0);
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
@@ -269,7 +276,7 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmA
 #pragma unroll
   for (int j = 0; j < TX; ++j) {
     const int m = wm * (BM / WM) + 32 * j + (lane & 31);
-    if (m >= tc.nvalid) continue;
+    if (rm.layout != 0 && m >= tc.nvalid) continue;   // contiguous: padding rows of z are written (zeros)
     int64_t orow;
     if (EPI == kEpiGateUp || rm.layout != 0) {
       orow = tc.row0 + m;
