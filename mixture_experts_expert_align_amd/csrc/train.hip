@@ -11,10 +11,11 @@
 //   wgrad    dW[e] = sum over the group's rows of dy[r] x[r]^T
 //                    ([E, N, K] fp32, written, or added to the fp32 buffer)
 //
-// One kernel computes C[i][j] = sum_c A(i, c) B(j, c) for a 128 x 128 tile
-// of C, the contraction in 64-wide slices staged in LDS (two buffers; each
-// slice loaded into registers two slices ahead of its LDS store), four
-// waves of 64 x 64 as 2 x 2 tiles of v_mfma_f32_32x32x16_bf16.  Each operand
+// One kernel body computes C[i][j] = sum_c A(i, c) B(j, c) for a tile of C,
+// the contraction in slices staged in LDS (two buffers; each slice loaded
+// into registers two slices ahead of its LDS store), waves of 64 x 64 as
+// 2 x 2 tiles of v_mfma_f32_32x32x16_bf16: 128 x 256 tiles of eight waves
+// for forward and dgrad, 128 x 128 tiles of four waves for wgrad.  Each operand
 // is stored either with c contiguous (x and W for the forward, dy for dgrad)
 // or with its own index contiguous (W for dgrad, dy and x for wgrad): MFMA
 // wants 8 consecutive c per lane, so the second kind is staged transposed —
@@ -36,19 +37,34 @@
 namespace moe {
 namespace train {
 
-constexpr int BI = 128, BJ = 128, BC = 64;   // tile of C, contraction slice
-constexpr int NT = 256;                      // 4 waves: 2 (j) x 2 (i) of 64 x 64
-constexpr int CH = BC / 8;                   // 16-byte chunks per LDS row
-constexpr int RPW = 256 / (BC * 2);          // LDS rows per 256-byte bank window
+// A tile configuration: C tile BI x BJ, contraction slice BC, WN x WM waves
+// of 64 x 64.
+template <int BI_, int BJ_, int BC_, int WN_, int WM_>
+struct Tile {
+  static constexpr int BI = BI_, BJ = BJ_, BC = BC_, WN = WN_, WM = WM_;
+  static constexpr int NT = 64 * WN * WM;
+  static constexpr int CH = BC / 8;            // 16-byte chunks per LDS row
+  static constexpr int RPW = 256 / (BC * 2);   // LDS rows per 256-byte bank window
+};
+// forward and dgrad: 8 waves, 128 x 256, two workgroups per CU (128 VGPRs)
+using RowsTile = Tile<128, 256, 32, 4, 2>;
+// wgrad (both operands staged transposed): 4 waves, 128 x 128 and 64-wide
+// slices, whose 128-byte LDS rows keep the transposed stores at 2-way bank
+// conflicts (64-byte rows reach 8-way) and whose registers fit without spills
+using WgradTile = Tile<128, 128, 64, 2, 2>;
+
+constexpr int kNumXcd = 8;    // workgroups are dealt to the XCDs round robin
+constexpr int kXcdRun = 8;    // consecutive logical tiles one XCD takes
 
 // chunk c of LDS row `row`, XOR-swizzled.  (row / RPW) puts the 8
 // consecutive rows one 128-byte quarter of an MFMA fragment read touches in
 // distinct banks; (row / 16), constant over such 8 rows, spreads the
 // transposed stores, whose 16 lanes of one c pair write rows 8 apart (with
 // the first term alone they met in 2 chunks, an 8-way bank conflict).
+template <class T>
 __device__ __forceinline__ int lds_off(int row, int c) {
-  const int x = ((row / RPW) ^ (row / 16)) & (CH - 1);
-  return row * BC + ((c ^ x) << 3);
+  const int x = ((row / T::RPW) ^ (row / 16)) & (T::CH - 1);
+  return row * T::BC + ((c ^ x) << 3);
 }
 
 // An operand of C: element (i, c) at byte offset 2 * (i * ld + c) (c
@@ -68,20 +84,22 @@ constexpr uint32_t kPast = 0x80000000u;   // an offset past every buffer
 // Each stager keeps two register sets: slice t is loaded into set t % 2 two
 // slices before its LDS store, so each load has two slices of MFMAs to land.
 
-// c-contiguous operand: 128 rows x CH chunks, NU per thread.
+// c-contiguous operand: EXT rows x CH chunks, NU per thread.
+template <class T, int EXT>
 struct RowStager {
-  static constexpr int NU = BI * CH / NT;
+  static constexpr int CH = T::CH, NT = T::NT;
+  static constexpr int NU = EXT * CH / NT;
+  static_assert(NU * NT == EXT * CH, "rows x chunks must fill the threads");
+  // unit u of this thread: row (tid + NT u) / CH, chunk (tid + NT u) % CH
+  // (recomputed where used: registers are the scarce resource here)
   i32x4 v[2][NU];
   uint32_t off[NU];
-  int row[NU], chunk[NU];
   __device__ void setup(const Operand& o, int i0) {
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int q = threadIdx.x + NT * u;
-      row[u] = q / CH;
-      chunk[u] = q % CH;
-      const int i = i0 + row[u];
-      off[u] = i >= o.ilo && i < o.ihi ? (uint32_t)(((int64_t)i * o.ld + 8 * chunk[u]) * 2) : kPast;
+      const int i = i0 + q / CH;
+      off[u] = i >= o.ilo && i < o.ihi ? (uint32_t)(((int64_t)i * o.ld + 8 * (q % CH)) * 2) : kPast;
     }
   }
   __device__ void load(int set, const __amdgpu_buffer_rsrc_t& r, const Operand&, int c0) {
@@ -91,69 +109,85 @@ struct RowStager {
   }
   __device__ void store(int set, uint16_t* lds) const {
 #pragma unroll
-    for (int u = 0; u < NU; ++u) *reinterpret_cast<i32x4*>(lds + lds_off(row[u], chunk[u])) = v[set][u];
+    for (int u = 0; u < NU; ++u) {
+      const int q = threadIdx.x + NT * u;
+      *reinterpret_cast<i32x4*>(lds + lds_off<T>(q / CH, q % CH)) = v[set][u];
+    }
   }
 };
 
-// i-contiguous operand: a block is two c rows (2p, 2p+1) x 8 consecutive i;
-// thread t takes i chunk t % 16 of c pairs p = t / 16 + 16 u: 16 lanes read
-// 256 contiguous bytes of one c row.
+// i-contiguous operand: a block is two c rows (2p, 2p+1) x 8 consecutive i,
+// NB = (BC / 2) (EXT / 8) blocks; block b = thread + NT u takes i chunk
+// b % (EXT / 8) of c pair b / (EXT / 8), so the lanes of one c pair read
+// contiguous bytes of one c row.  With fewer blocks than threads the
+// remaining threads stage nothing.
+template <class T, int EXT>
 struct ColStager {
-  static constexpr int NU = (BC / 2) * 16 / NT;
+  static constexpr int NT = T::NT;
+  static constexpr int NCX = EXT / 8;                 // i chunks
+  static constexpr int NB = (T::BC / 2) * NCX;
+  static constexpr int NU = (NB + NT - 1) / NT;
+  // block u of this thread: b = tid + NT u, c pair b / NCX, i chunk b % NCX
+  // (recomputed where used)
   i32x4 v[2][NU][2];
-  int ic;
-  uint32_t ioff;
-  bool ivalid;
+  uint32_t ioff[NU];   // kPast when the block stages nothing or its i are invalid
   __device__ void setup(const Operand& o, int i0) {
-    ic = threadIdx.x % 16;
-    const int i = i0 + 8 * ic;           // i-contiguous extents are multiples of 8
-    ivalid = i >= o.ilo && i < o.ihi;
-    ioff = (uint32_t)(2 * i);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int b = threadIdx.x + NT * u;
+      const int i = i0 + 8 * (b % NCX);    // i-contiguous extents are multiples of 8
+      ioff[u] = b < NB && i >= o.ilo && i < o.ihi ? (uint32_t)(2 * i) : kPast;
+    }
   }
   __device__ void load(int set, const __amdgpu_buffer_rsrc_t& r, const Operand& o, int c0) {
 #pragma unroll
-    for (int u = 0; u < NU; ++u)
+    for (int u = 0; u < NU; ++u) {
+      const int p = (threadIdx.x + NT * u) / NCX;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int c = c0 + 2 * (threadIdx.x / 16 + 16 * u) + h;
-        const uint32_t off = ivalid && c < o.nc ? (uint32_t)((int64_t)c * o.ld * 2) + ioff : kPast;
+        const int c = c0 + 2 * p + h;
+        const uint32_t off = ioff[u] != kPast && c < o.nc ? (uint32_t)((int64_t)c * o.ld * 2) + ioff[u] : kPast;
         v[set][u][h] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
       }
+    }
   }
   // word t of block u: (i = 8 ic + t; c = 2p, 2p+1) -> LDS row i, element 2p
   __device__ void store(int set, uint16_t* lds) const {
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      const int p = threadIdx.x / 16 + 16 * u;
+      const int b = threadIdx.x + NT * u;
+      if (NB % NT != 0 && b >= NB) continue;   // this thread stages no block u
+      const int p = b / NCX, ic = b % NCX;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const uint32_t a = (uint32_t)v[set][u][0][t / 2], b = (uint32_t)v[set][u][1][t / 2];
-        const uint32_t w = (t & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-        *reinterpret_cast<uint32_t*>(lds + lds_off(8 * ic + t, (2 * p) / 8) + (2 * p) % 8) = w;
+        const uint32_t a = (uint32_t)v[set][u][0][t / 2], w2 = (uint32_t)v[set][u][1][t / 2];
+        const uint32_t w = (t & 1) ? ((a >> 16) | (w2 & 0xffff0000u)) : ((a & 0xffffu) | (w2 << 16));
+        *reinterpret_cast<uint32_t*>(lds + lds_off<T>(8 * ic + t, (2 * p) / 8) + (2 * p) % 8) = w;
       }
     }
   }
 };
 
-template <bool ACOL, bool BCOL>
+template <class T, bool ACOL, bool BCOL>
 struct Stagers {
-  typename std::conditional<ACOL, ColStager, RowStager>::type a;
-  typename std::conditional<BCOL, ColStager, RowStager>::type b;
+  typename std::conditional<ACOL, ColStager<T, T::BI>, RowStager<T, T::BI>>::type a;
+  typename std::conditional<BCOL, ColStager<T, T::BJ>, RowStager<T, T::BJ>>::type b;
 };
 
-// C tile [i0, i0+128) x [j0, j0+128) over the contraction [0, nc): returns
+// C tile [i0, i0+BI) x [j0, j0+BJ) over the contraction [0, nc): returns
 // the accumulators.  acc[tw][tx][r]: j = 64 wn + 32 tw + 8 (r/4) + 4 (lane/32)
-// + r%4, i = 64 wm + 32 tx + lane%32.
-template <bool ACOL, bool BCOL>
+// + r%4, i = 64 wm + 32 tx + lane%32 (wave = WM wn + wm).
+template <class T, bool ACOL, bool BCOL>
 __device__ __forceinline__ void tile_mma(const Operand& A, const Operand& B, int i0, int j0, int nc,
-                                         uint16_t (*sA)[BI * BC], uint16_t (*sB)[BJ * BC],
+                                         uint16_t (*sA)[T::BI * T::BC], uint16_t (*sB)[T::BJ * T::BC],
                                          f32x16 (&acc)[2][2]) {
+  constexpr int BC = T::BC;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int wn = wave >> 1, wm = wave & 1;
+  const int wn = wave / T::WM, wm = wave % T::WM;
   const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(A.base, A.bytes);
   const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(B.base, B.bytes);
-  Stagers<ACOL, BCOL> st;
+  Stagers<T, ACOL, BCOL> st;
   st.a.setup(A, i0);
   st.b.setup(B, j0);
 #pragma unroll
@@ -184,8 +218,8 @@ __device__ __forceinline__ void tile_mma(const Operand& A, const Operand& B, int
       bf16x8 fb[2], fa[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        fb[t] = as_bf16x8(*reinterpret_cast<const i32x4*>(&sB[buf][lds_off(jrow + 32 * t, c)]));
-        fa[t] = as_bf16x8(*reinterpret_cast<const i32x4*>(&sA[buf][lds_off(irow + 32 * t, c)]));
+        fb[t] = as_bf16x8(*reinterpret_cast<const i32x4*>(&sB[buf][lds_off<T>(jrow + 32 * t, c)]));
+        fa[t] = as_bf16x8(*reinterpret_cast<const i32x4*>(&sA[buf][lds_off<T>(irow + 32 * t, c)]));
       }
 #pragma unroll
       for (int tw = 0; tw < 2; ++tw)
@@ -230,16 +264,27 @@ __device__ __forceinline__ void group_rows(const TrainArgs& t, int e, int& a, in
 // forward / dgrad: C rows are rows r of x / dy, C columns the n / k of the
 // output; a 128-row tile loops over the groups it meets.
 template <int MODE>
-__global__ void __launch_bounds__(NT, 2) train_rows_kernel(TrainArgs t) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BI * BC];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BJ * BC];
-  const int r0 = blockIdx.x * BI;
-  const int j0 = blockIdx.y * BJ;
+__global__ void __launch_bounds__(RowsTile::NT, 4) train_rows_kernel(TrainArgs t) {
+  using T = RowsTile;
+  constexpr int BI = T::BI, BJ = T::BJ;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][T::BI * T::BC];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][T::BJ * T::BC];
   const int ncol = MODE == kTrainForward ? t.N : t.K;   // output columns
+  // Logical tiles in column-tile-major order (the row tiles of one weight
+  // column tile in a row), dealt to the 8 XCDs in runs of kXcdRun: block b
+  // runs on XCD b % 8 as its (b / 8)-th block, so each XCD's L2 serves one
+  // weight tile to kXcdRun consecutive row tiles (of one group, mostly).
+  const int64_t rt = (t.R + BI - 1) / BI;
+  const int64_t nlog = rt * ((ncol + BJ - 1) / BJ);
+  const int64_t bk = blockIdx.x / kNumXcd;
+  const int64_t L = ((bk / kXcdRun) * kNumXcd + blockIdx.x % kNumXcd) * kXcdRun + bk % kXcdRun;
+  if (L >= nlog) return;
+  const int r0 = (int)(L % rt) * BI;
+  const int j0 = (int)(L / rt) * BJ;
   const int nc = MODE == kTrainForward ? t.K : t.N;     // contraction
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int wn = wave >> 1, wm = wave & 1;
+  const int wn = wave / T::WM, wm = wave % T::WM;
   // first group with rows past r0
   int lo = 0, hi = t.E - 1;
   while (lo < hi) {
@@ -271,7 +316,7 @@ __global__ void __launch_bounds__(NT, 2) train_rows_kernel(TrainArgs t) {
     B.ihi = ncol;
     B.nc = nc;
     f32x16 acc[2][2];
-    tile_mma<false, MODE == kTrainDgrad>(A, B, 0, j0, nc, sA, sB, acc);
+    tile_mma<T, false, MODE == kTrainDgrad>(A, B, 0, j0, nc, sA, sB, acc);
 #pragma unroll
     for (int tx = 0; tx < 2; ++tx) {
       const int r = r0 + 64 * wm + 32 * tx + (lane & 31);
@@ -285,7 +330,8 @@ __global__ void __launch_bounds__(NT, 2) train_rows_kernel(TrainArgs t) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) v[q] = f32_to_bf16_rne(acc[tw][tx][4 * h + q]);
           const int j = j0 + 64 * wn + 32 * tw + 8 * h + 4 * (lane >> 5);
-          *reinterpret_cast<uint2*>(o + j) = make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
+          if (j < ncol)   // a partial last column tile
+            *reinterpret_cast<uint2*>(o + j) = make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
         }
     }
   }
@@ -293,16 +339,18 @@ __global__ void __launch_bounds__(NT, 2) train_rows_kernel(TrainArgs t) {
 
 // wgrad: C = dW[e] tile [n0, n0+128) x [k0, k0+128), contraction over the
 // group's rows: A(n, r) = dy[r][n], B(k, r) = x[r][k], both i-contiguous.
-__global__ void __launch_bounds__(NT, 2) train_wgrad_kernel(TrainArgs t) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BI * BC];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BJ * BC];
-  const int kt = t.K / BJ;
+__global__ void __launch_bounds__(WgradTile::NT, 2) train_wgrad_kernel(TrainArgs t) {
+  using T = WgradTile;
+  constexpr int BI = T::BI, BJ = T::BJ;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][T::BI * T::BC];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][T::BJ * T::BC];
+  const int kt = (t.K + BJ - 1) / BJ;
   const int n0 = (blockIdx.x / kt) * BI;
   const int k0 = (blockIdx.x % kt) * BJ;
   const int e = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int wn = wave >> 1, wm = wave & 1;
+  const int wn = wave / T::WM, wm = wave % T::WM;
   int a, b;
   group_rows(t, e, a, b);
   const int m = b - a;
@@ -320,7 +368,7 @@ __global__ void __launch_bounds__(NT, 2) train_wgrad_kernel(TrainArgs t) {
   B.ihi = t.K;
   B.nc = m;
   f32x16 acc[2][2];
-  tile_mma<true, true>(A, B, n0, k0, m, sA, sB, acc);
+  tile_mma<T, true, true>(A, B, n0, k0, m, sA, sB, acc);
   float* out = static_cast<float*>(t.out) + (int64_t)e * t.N * t.K;
 #pragma unroll
   for (int tx = 0; tx < 2; ++tx) {
@@ -331,6 +379,7 @@ __global__ void __launch_bounds__(NT, 2) train_wgrad_kernel(TrainArgs t) {
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         const int k = k0 + 64 * wn + 32 * tw + 8 * h + 4 * (lane >> 5);
+        if (k >= t.K) continue;   // a partial last column tile
         f32x4 v = {acc[tw][tx][4 * h], acc[tw][tx][4 * h + 1], acc[tw][tx][4 * h + 2], acc[tw][tx][4 * h + 3]};
         f32x4* dst = reinterpret_cast<f32x4*>(o + k);
         if (t.accumulate) {
@@ -348,15 +397,20 @@ __global__ void __launch_bounds__(NT, 2) train_wgrad_kernel(TrainArgs t) {
 hipError_t launch_train(const TrainArgs& t, hipStream_t s) {
   using namespace train;
   if (t.mode == kTrainWgrad) {
-    hipLaunchKernelGGL(train_wgrad_kernel, dim3((t.N / BI) * (t.K / BJ), t.E), dim3(NT), 0, s, t);
+    using W = WgradTile;
+    hipLaunchKernelGGL(train_wgrad_kernel, dim3((t.N / W::BI) * ((t.K + W::BJ - 1) / W::BJ), t.E),
+                       dim3(W::NT), 0, s, t);
   } else {
     if (t.R == 0) return hipSuccess;
     const int ncol = t.mode == kTrainForward ? t.N : t.K;
-    const dim3 grid((unsigned)((t.R + BI - 1) / BI), ncol / BJ);
+    using T = RowsTile;
+    const int64_t nlog = (t.R + T::BI - 1) / T::BI * ((ncol + T::BJ - 1) / T::BJ);
+    const int64_t unit = (int64_t)kNumXcd * kXcdRun;
+    const dim3 grid((unsigned)((nlog + unit - 1) / unit * unit));
     if (t.mode == kTrainForward)
-      hipLaunchKernelGGL(train_rows_kernel<kTrainForward>, grid, dim3(NT), 0, s, t);
+      hipLaunchKernelGGL(train_rows_kernel<kTrainForward>, grid, dim3(T::NT), 0, s, t);
     else
-      hipLaunchKernelGGL(train_rows_kernel<kTrainDgrad>, grid, dim3(NT), 0, s, t);
+      hipLaunchKernelGGL(train_rows_kernel<kTrainDgrad>, grid, dim3(T::NT), 0, s, t);
   }
   return hipGetLastError();
 }
