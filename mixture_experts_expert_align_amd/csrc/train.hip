@@ -344,9 +344,13 @@ __global__ void __launch_bounds__(WgradTile::NT, 2) train_wgrad_kernel(TrainArgs
   constexpr int BI = T::BI, BJ = T::BJ;
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][T::BI * T::BC];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][T::BJ * T::BC];
+  // blocks (n tile, k tile) with k fastest, per group: dealt round robin,
+  // XCD x sees the k tiles congruent to x mod 8 for every n tile, so those x
+  // slices stay in its L2 (runs of 8 consecutive k tiles per XCD measured
+  // slower: every XCD then cycles through all the x slices)
   const int kt = (t.K + BJ - 1) / BJ;
-  const int n0 = (blockIdx.x / kt) * BI;
-  const int k0 = (blockIdx.x % kt) * BJ;
+  const int n0 = (int)(blockIdx.x / kt) * BI;
+  const int k0 = (int)(blockIdx.x % kt) * BJ;
   const int e = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
