@@ -48,6 +48,10 @@ SCALED = [
     ("mxfp8_m512", mi.config(3).scaled(M=512, K=512, I=256), moe.VARIANT_AUTO),
     ("mxfp8_m4160", mi.config(3).scaled(M=4160, K=512, I=256), moe.VARIANT_AUTO),
     ("mxfp8_m12000", mi.config(3).scaled(M=12000, K=256, I=128), moe.VARIANT_AUTO),
+    # W1 weights 8 steps ahead: one trip of two chunks (8 steps), and a full
+    # trip before the last (16 steps) with two 64-token passes per expert
+    ("mxfp8_k1024", mi.config(3).scaled(M=512, K=1024, I=256), moe.VARIANT_AUTO),
+    ("mxfp8_m4160_k2048", mi.config(3).scaled(M=4160, K=2048, I=128), moe.VARIANT_AUTO),
 ]
 
 
