@@ -30,17 +30,15 @@ namespace {
 //
 // A workgroup of 8 waves owns 128 weight rows of one expert, 16 per wave, and
 // the expert's routed tokens, 64 per pass.  Weights stream from HBM straight
-// into registers, D 128-wide steps ahead (D register sets).  The tokens'
-// codes and scales are staged in LDS a chunk of CS steps at a time (two
-// buffers), by buffer loads that write LDS directly, so staging costs no
-// registers and the waves meet at a barrier once per chunk.  The compiler
-// does not track those loads, so the wait before each chunk's barrier is
-// explicit, counted from a fixed issue order: a chunk issues one
+// into registers, CS 128-wide steps ahead (CS register sets, one per step of
+// a chunk).  The tokens' codes and scales are staged in LDS a chunk of CS
+// steps at a time (two buffers), by buffer loads that write LDS directly, so
+// staging costs no registers and the waves meet at a barrier once per chunk.
+// The compiler does not track those loads, so the wait before each chunk's
+// barrier is explicit, counted from a fixed issue order: a chunk issues one
 // weight-scale load (a 16-step group), then in each step the 2 weight loads
-// of the step D ahead, and after its barrier the CS + 1 staging loads of the
-// chunk after next.  A streaming kernel reaches HBM's rate only with enough
-// bytes in flight: with the weights one chunk ahead (8 KB per wave) W1 ran at
-// about half of it, so W1 keeps them two chunks ahead.
+// of the step CS ahead, and after its barrier the CS + 1 staging loads of the
+// chunk after next.
 //   kGateUp: wave w holds the gate (w even) or up (w odd) rows of features
 //            f0 + 16 (w / 2) .. +15; z = silu(gate) * up per token, quantised
 //            per 32 features (one MX block = waves 4b .. 4b+3) in the
@@ -77,16 +75,13 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("" ::: "memory");
 }
 
-// CS: steps per chunk (4, 2 or 1, dividing the contraction's step count).
-// D: steps the weights stream ahead, a multiple of CS such that the chunk
-// count is a multiple of D / CS.  TT: 16-row weight tiles per wave (with 2,
-// each staged activation fragment feeds two MFMAs and the workgroup's 256
-// weight rows amortise the activation staging; it needs registers that
-// deeper weight prefetch uses better).
-template <int EPI, int CS, int TT, int D>
+// CS: steps per chunk (4, 2 or 1, dividing the contraction's step count);
+// the weights stream CS steps ahead.  TT: 16-row weight tiles per wave (2
+// for W1: each staged activation fragment then feeds two MFMAs, and the
+// workgroup's 256 weight rows amortise the activation staging, which costs
+// the address unit as many lane requests per byte as the weights do).
+template <int EPI, int CS, int TT>
 __global__ void __launch_bounds__(64 * kMxWaves, 4) gemm_stream_mxfp8_kernel(GemmArgs g) {
-  static_assert(D % CS == 0, "the weights run whole chunks ahead");
-  constexpr int R = D / CS;   // chunks the weights run ahead
   constexpr int kChunk = CS * kMxStepA + kMxWaves * kMxStepAS;   // one LDS buffer
   // the W1 epilogue gathers every wave's accumulators ([wave][tile][token tile][lane])
   constexpr int kOutBytes = EPI == kEpiGateUp ? kMxWaves * TT * 4 * 64 * 16 : 0;
@@ -154,9 +149,8 @@ __global__ void __launch_bounds__(64 * kMxWaves, 4) gemm_stream_mxfp8_kernel(Gem
         lds_load16(ar, base + sub * kMxStepA + wave * 1024, xo, (ch * CS + sub) * 128);
       lds_load4(asr, base + CS * kMxStepA + wave * kMxStepAS, xso, (ch * CS + ssub) * 4);
     };
-    // 2 TT loads: the weights of step st into register set i (step s lives
-    // in set s % D from its load, D steps ahead, to its multiply)
-    i32x8 wa[D][TT];
+    // 2 TT loads: the weights of step st into register set i
+    i32x8 wa[CS][TT];
     auto wload = [&](int i, int st) {
       const int k = st * 128;
 #pragma unroll
@@ -201,66 +195,52 @@ __global__ void __launch_bounds__(64 * kMxWaves, 4) gemm_stream_mxfp8_kernel(Gem
               wa[i][tt], xb, acc[tt][c], 0, 0, 0, (int)(wsw[tt] >> (8 * q)), 0, (int)(xsw >> (8 * q)));
       }
     };
-    // the CS steps of chunk ch (LDS buffer buf, register sets r CS ..):
-    // multiply step s, then load the weights of step s + D into the freed
-    // register set (past the end: the last step again, unused)
-    auto chunk = [&](int ch, int buf, int r) {
+    // the CS steps of chunk ch (LDS buffer buf): multiply step s, then load
+    // the weights of step s + CS into the freed register set (past the end:
+    // the last step again, unused)
+    auto chunk = [&](int ch, int buf) {
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) scur[tt] = snext[tt];   // loaded a chunk ago
       sload(((ch + 1) * CS) / 16);
       issue_order();
 #pragma unroll
       for (int sub = 0; sub < CS; ++sub) {
-        mma(r * CS + sub, buf, sub, ch * CS + sub);
-        wload(r * CS + sub, min(ch * CS + sub + D, nsteps - 1));
+        mma(sub, buf, sub, ch * CS + sub);
+        wload(sub, min((ch + 1) * CS + sub, nsteps - 1));
         // also: one step's token fragments live at a time
         issue_order();
       }
     };
 
-    // prologue: chunk 0 staged, the weights of steps 0 .. D-1 loaded, chunk 1
+    // prologue: chunk 0 staged, the weights of steps 0 .. CS-1 loaded, chunk 1
     // staged (the loop's issue order: weights, then the next staging)
     stage(0, 0);
     issue_order();
     sload(0);
     issue_order();
 #pragma unroll
-    for (int st = 0; st < D; ++st) {
-      wload(st, min(st, nsteps - 1));
+    for (int sub = 0; sub < CS; ++sub) {
+      wload(sub, min(sub, nsteps - 1));
       issue_order();
     }
     stage(min(1, nchunks - 1), 1);
     issue_order();
     // chunk 0's loads are older than the scale groups' (TT), the weights'
-    // (2 TT D) and chunk 1's (CS + 1)
-    wait_vm<TT + 2 * TT * D + CS + 1>();
+    // (2 TT CS) and chunk 1's (CS + 1)
+    wait_vm<TT + 2 * TT * CS + CS + 1>();
     lds_barrier();
-    // R chunks per trip, so that each chunk's register sets are known at
-    // compile time (the chunk count is a multiple of R); the last trip is
-    // peeled: its last chunk has no next chunk to wait for
-    auto next = [&](int ch) {
+    for (int ch = 0; ch + 1 < nchunks; ++ch) {
+      const int buf = ch & 1;
+      chunk(ch, buf);
       // chunk ch+1's staging loads are older than the TT scale groups and
-      // the 2 TT CS weight loads of chunk ch (the weights loaded before
-      // them are older still); then every wave's share is in place and
-      // chunk ch is read
+      // the 2 TT CS weight loads of this chunk; then every wave's share is in
+      // place and chunk ch is read
       wait_vm<TT + 2 * TT * CS>();
       lds_barrier();
-      stage(min(ch + 2, nchunks - 1), ch & 1);   // past the end: reloads the last chunk, unused
+      stage(min(ch + 2, nchunks - 1), buf);   // past the end: reloads the last chunk, unused
       issue_order();
-    };
-    int ch0 = 0;
-    for (; ch0 + R < nchunks; ch0 += R) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        chunk(ch0 + r, (ch0 + r) & 1, r);
-        next(ch0 + r);
-      }
     }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      chunk(ch0 + r, (ch0 + r) & 1, r);
-      if (r + 1 < R) next(ch0 + r);
-    }
+    chunk(nchunks - 1, (nchunks - 1) & 1);
     // drain the remaining (unused) loads before LDS is reused
     wait_vm<0>();
     lds_barrier();
@@ -346,20 +326,22 @@ __global__ void __launch_bounds__(64 * kMxWaves, 4) gemm_stream_mxfp8_kernel(Gem
 template <int EPI>
 static hipError_t launch_mxfp8(const GemmArgs& g, hipStream_t s) {
   const int nsteps = g.kdim / 128;
+  // W1: two tiles per wave (128 features per workgroup) and chunks of 2
+  // steps when the features divide; W2 keeps one tile and chunks of 2 steps:
+  // with more, its epilogue's registers no longer fit the 128 that let two
+  // workgroups share a CU
+  if (EPI == kEpiGateUp && g.nfeat % 128 == 0 && nsteps % 2 == 0) {
+    const dim3 grid(g.nfeat / 128, (unsigned)g.max_active);
+    hipLaunchKernelGGL((gemm_stream_mxfp8_kernel<kEpiGateUp, 2, 2>), grid, dim3(64 * kMxWaves), 0, s, g);
+    return hipGetLastError();
+  }
   const dim3 grid(g.nfeat / (EPI == kEpiGateUp ? 64 : 128), (unsigned)g.max_active);
-  // W1: one tile per wave, chunks of 4 steps and the weights 8 steps ahead
-  // (64 registers of weights in flight per wave) when the step count allows.
-  // W2 keeps chunks of 2 steps with the weights one chunk ahead: with more,
-  // its epilogue's registers no longer fit the 128 that let two workgroups
-  // share a CU.
-  if (EPI == kEpiGateUp && nsteps % 8 == 0)
-    hipLaunchKernelGGL((gemm_stream_mxfp8_kernel<kEpiGateUp, 4, 1, 8>), grid, dim3(64 * kMxWaves), 0, s, g);
-  else if (EPI == kEpiGateUp && nsteps % 4 == 0)
-    hipLaunchKernelGGL((gemm_stream_mxfp8_kernel<kEpiGateUp, 4, 1, 4>), grid, dim3(64 * kMxWaves), 0, s, g);
+  if (EPI == kEpiGateUp && nsteps % 4 == 0)
+    hipLaunchKernelGGL((gemm_stream_mxfp8_kernel<kEpiGateUp, 4, 1>), grid, dim3(64 * kMxWaves), 0, s, g);
   else if (nsteps % 2 == 0)
-    hipLaunchKernelGGL((gemm_stream_mxfp8_kernel<EPI, 2, 1, 2>), grid, dim3(64 * kMxWaves), 0, s, g);
+    hipLaunchKernelGGL((gemm_stream_mxfp8_kernel<EPI, 2, 1>), grid, dim3(64 * kMxWaves), 0, s, g);
   else
-    hipLaunchKernelGGL((gemm_stream_mxfp8_kernel<EPI, 1, 1, 1>), grid, dim3(64 * kMxWaves), 0, s, g);
+    hipLaunchKernelGGL((gemm_stream_mxfp8_kernel<EPI, 1, 1>), grid, dim3(64 * kMxWaves), 0, s, g);
   return hipGetLastError();
 }
 
