@@ -41,7 +41,7 @@ namespace moe {
 namespace tile {
 
 constexpr int NXCD = 8;
-constexpr int kXcdChunk = 8;
+constexpr int kXcdChunk = 32;
 enum Order { kWeightMajor = 0, kRouteMajor = 1 };
 
 template <int BK>
@@ -72,10 +72,23 @@ __device__ __forceinline__ bool tile_coord(const GemmArgs& g, int ncol, int64_t 
   // block b runs on XCD b % 8 as that XCD's (b / 8)-th block
   const int64_t b = blockIdx.x;
   const int64_t k = b / NXCD;
-  const int64_t L = ORDER == kRouteMajor ? b : ((k / kXcdChunk) * NXCD + (b % NXCD)) * kXcdChunk + (k % kXcdChunk);
-  if (L >= nlog) return false;
+  int64_t L = b;
   if (rm.layout == 0) {
     const int64_t total = (int64_t)rm.num_post[0] / BM * ncol;
+    if (ORDER == kWeightMajor) {
+      // full rounds of 8 chunks; the tiles left after them are split evenly
+      // over the 8 XCDs so that none idles through the last round
+      const int64_t full = total / (NXCD * kXcdChunk);
+      const int64_t x = b % NXCD;
+      if (k < full * kXcdChunk) {
+        L = ((k / kXcdChunk) * NXCD + x) * kXcdChunk + (k % kXcdChunk);
+      } else {
+        const int64_t c2 = (total - full * NXCD * kXcdChunk + NXCD - 1) / NXCD;
+        const int64_t kk = k - full * kXcdChunk;
+        if (kk >= c2) return false;
+        L = full * NXCD * kXcdChunk + x * c2 + kk;
+      }
+    }
     if (L >= total) return false;
     // expert e owns logical tiles [offsets[e]/BM*ncol, offsets[e+1]/BM*ncol)
     int lo = 0, hi = g.E - 1;
@@ -98,6 +111,7 @@ __device__ __forceinline__ bool tile_coord(const GemmArgs& g, int ncol, int64_t 
     tc.nvalid = (int)max<int64_t>(0, min<int64_t>(BM, rm.counts[lo] - (tc.row0 - rm.offsets[lo])));
     return true;
   }
+  if (L >= nlog) return false;
   const int tpe = (rm.max_tokens + BM - 1) / BM;
   const int e = (int)(L / ((int64_t)ncol * tpe));
   const int local = (int)(L - (int64_t)e * ncol * tpe);
@@ -109,6 +123,55 @@ __device__ __forceinline__ bool tile_coord(const GemmArgs& g, int ncol, int64_t 
   tc.row0 = (int64_t)e * rm.max_tokens + r0;
   tc.nvalid = min(BM, cnt - r0);
   return true;
+}
+
+// Epilogue shared by the tile kernels.  acc[i][j][r]: weight row (tile i)
+// 8*(r/4) + 4*(lane/32) + r%4, route wm*(BM/WM) + 32*j + lane%32; registers
+// 4h..4h+3 are 4 consecutive rows.
+template <int EPI, int BM, int BN, int WN, int WM, int TW, int TX>
+__device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const TileCoord& tc,
+                                              const f32x16 (&acc)[TW][TX], int wn, int wm, int lane) {
+  const RowMap& rm = g.rows;
+  uint16_t* out = static_cast<uint16_t*>(g.out);
+#pragma unroll
+  for (int j = 0; j < TX; ++j) {
+    const int m = wm * (BM / WM) + 32 * j + (lane & 31);
+    if (rm.layout != 0 && m >= tc.nvalid) continue;   // contiguous: padding rows of z are written (zeros)
+    int64_t orow;
+    if (EPI == kEpiGateUp || rm.layout != 0) {
+      orow = tc.row0 + m;
+    } else {
+      const int sid = rm.sorted_ids[tc.row0 + m];
+      if (sid == rm.sentinel) continue;
+      orow = sid;
+    }
+    uint16_t* o = out + orow * g.out_ld;
+    if (EPI == kEpiGateUp) {
+      constexpr int FW = BN / 2 / WN;
+#pragma unroll
+      for (int i = 0; i < TW / 2; ++i)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          uint32_t v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            v[r] = f32_to_bf16_rne(silu_f32(acc[i][j][4 * h + r]) * acc[i + TW / 2][j][4 * h + r]);
+          const int f = tc.col0 / 2 + wn * FW + 32 * i + 8 * h + 4 * (lane >> 5);
+          *reinterpret_cast<uint2*>(o + f) = make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TW; ++i)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          uint32_t v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = f32_to_bf16_rne(acc[i][j][4 * h + r]);
+          const int n = tc.col0 + wn * (BN / WN) + 32 * i + 8 * h + 4 * (lane >> 5);
+          *reinterpret_cast<uint2*>(o + n) = make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
+        }
+    }
+  }
 }
 
 template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, int ORDER>
@@ -270,48 +333,188 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmA
   }
   if (kt < nk) compute(0);
 
-  // ---- epilogue.  acc[i][j][r]: weight row (tile i) 8*(r/4) + 4*(lane/32) + r%4,
-  // route wm*(BM/WM) + 32*j + lane%32.  Registers 4h..4h+3 are 4 consecutive rows.
-  uint16_t* out = static_cast<uint16_t*>(g.out);
+  tile_epilogue<EPI, BM, BN, WN, WM>(g, tc, acc, wn, wm, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Tile kernel with direct-to-LDS staging (contiguous format).
+//
+// The same tiles, fragments and epilogue as gemm_tile_bf16_kernel, but the
+// slices reach LDS by buffer loads that write LDS themselves (no registers,
+// no LDS store instructions), into a ring of NS slice buffers: slice kt+NS-1
+// is requested while slice kt is multiplied, so every load has NS-2 whole
+// slices of MFMA work to land, and each slice costs one wait and one
+// barrier.  One such load writes the 64 lanes' 16 bytes to 1 KB of LDS at a
+// wave-uniform address, lane i at byte 16 i; each lane therefore fetches the
+// chunk that the swizzled layout of lds_off places at its position.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, uint16_t* dst, uint32_t vo, int so) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, vo, so, 0, 0);
+}
+
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).  The compiler does not count the
+// LDS-writing loads, so the waits that cover them are explicit; the memory
+// clobbers keep loads from moving across them.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xf00);
+  asm volatile("" ::: "memory");
+}
+
+template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, int NS>
+__global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_dma_kernel(GemmArgs g, int ncol,
+                                                                          int64_t nlog) {
+  constexpr int NW = WN * WM;
+  constexpr int CH = BK / 8;                 // 16-byte chunks per row
+  constexpr int RPB = 64 / CH;               // rows per 1 KB block (one load instruction)
+  constexpr int RPW = 256 / (BK * 2) > 0 ? 256 / (BK * 2) : 1;   // as in lds_off
+  constexpr int LW = BN / RPB / NW;          // weight blocks per wave per slice
+  constexpr int LX = BM / RPB / NW;          // route blocks per wave per slice
+  static_assert(LW * NW * RPB == BN && LX * NW * RPB == BM, "blocks / waves mismatch");
+  constexpr int LPW = LW + LX;               // loads per wave per slice
+  static_assert((NS - 2) * LPW < 64 && NS >= 3, "ring depth");
+  constexpr int STAGE = (BN + BM) * BK;      // elements per ring slot: weight rows, then routes
+  constexpr int TW = BN / WN / 32;
+  constexpr int TX = BM / WM / 32;
+  static_assert(EPI != kEpiGateUp || TW % 2 == 0, "gate/up pairs need an even tile count");
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * STAGE];
+
+  TileCoord tc;
+  if (!tile_coord<BM, BN, kWeightMajor>(g, ncol, nlog, tc)) return;
+  const RowMap& rm = g.rows;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave / WM;
+  const int wm = wave % WM;
+  const int K = g.kdim;
+
+  const uint16_t* wexp = static_cast<const uint16_t*>(g.w) + (int64_t)tc.expert * g.w_expert_stride;
+  const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(wexp, g.w_expert_stride * 2);
+  const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(g.act, g.act_bytes);
+  // block b of a slot (b = wave + NW * i) holds rows RPB*b .. RPB*b + RPB-1 of
+  // its region; lane l lands on row RPB*b + l/CH, physical chunk l%CH, which
+  // holds logical chunk (l%CH) ^ x(row)
+  uint32_t ow[LW], ox[LX];
 #pragma unroll
-  for (int j = 0; j < TX; ++j) {
-    const int m = wm * (BM / WM) + 32 * j + (lane & 31);
-    if (rm.layout != 0 && m >= tc.nvalid) continue;   // contiguous: padding rows of z are written (zeros)
-    int64_t orow;
-    if (EPI == kEpiGateUp || rm.layout != 0) {
-      orow = tc.row0 + m;
+  for (int i = 0; i < LW; ++i) {
+    const int n = (wave + NW * i) * RPB + lane / CH;
+    const int c = (lane % CH) ^ ((n / RPW) & (CH - 1));
+    int wrow;
+    if (EPI == kEpiGateUp) {
+      const int f = tc.col0 / 2 + (n % (BN / 2));
+      const bool up = n >= BN / 2;
+      wrow = g.w1_order == 0 ? (up ? g.I + f : f) : (32 * (f >> 4) + (f & 15) + (up ? 16 : 0));
     } else {
-      const int sid = rm.sorted_ids[tc.row0 + m];
-      if (sid == rm.sentinel) continue;
-      orow = sid;
+      wrow = tc.col0 + n;
     }
-    uint16_t* o = out + orow * g.out_ld;
+    ow[i] = (uint32_t)((wrow * K + c * 8) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < LX; ++i) {
+    const int m = (wave + NW * i) * RPB + lane / CH;
+    const int c = (lane % CH) ^ ((m / RPW) & (CH - 1));
+    int64_t row = -1;
+    if (EPI == kEpiGateUp) {
+      const int sid = rm.sorted_ids[tc.row0 + m];
+      if (sid != rm.sentinel) row = sid / rm.topk;
+    } else {
+      row = tc.row0 + m;
+    }
+    ox[i] = row >= 0 ? (uint32_t)((row * g.act_ld + c * 8) * 2) : 0x80000000u;
+  }
+
+  const int nk = K / BK;
+  // request slice kt (past the end: the last slice again, never read) into slot st
+  auto issue = [&](int kt, int st) {
+    const int kb = min(kt, nk - 1) * BK * 2;
+    uint16_t* slot = smem + st * STAGE;
+#pragma unroll
+    for (int i = 0; i < LW; ++i)
+      load_to_lds16(wr, slot + (wave + NW * i) * RPB * BK, ow[i], kb);
+#pragma unroll
+    for (int i = 0; i < LX; ++i)
+      load_to_lds16(ar, slot + BN * BK + (wave + NW * i) * RPB * BK, ox[i], kb);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  int wrow_l[TW];
+#pragma unroll
+  for (int i = 0; i < TW; ++i) {
     if (EPI == kEpiGateUp) {
       constexpr int FW = BN / 2 / WN;
-#pragma unroll
-      for (int i = 0; i < TW / 2; ++i)
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          uint32_t v[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            v[r] = f32_to_bf16_rne(silu_f32(acc[i][j][4 * h + r]) * acc[i + TW / 2][j][4 * h + r]);
-          const int f = tc.col0 / 2 + wn * FW + 32 * i + 8 * h + 4 * (lane >> 5);
-          *reinterpret_cast<uint2*>(o + f) = make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
-        }
+      wrow_l[i] = (i < TW / 2 ? 0 : BN / 2) + wn * FW + 32 * (i % (TW / 2)) + (lane & 31);
     } else {
+      wrow_l[i] = wn * (BN / WN) + 32 * i + (lane & 31);
+    }
+  }
+  const int xrow_l = wm * (BM / WM) + (lane & 31);
+  const bool wlive = wm * (BM / WM) < tc.nvalid;   // see gemm_tile_bf16_kernel
+
+  f32x16 acc[TW][TX];
+#pragma unroll
+  for (int i = 0; i < TW; ++i)
+#pragma unroll
+    for (int j = 0; j < TX; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  bf16x8 fw[2][TW], fx[2][TX];
+  auto fload = [&](int fb, const uint16_t* slot, int s) {
+    const int c = 2 * s + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < TW; ++i)
+      fw[fb][i] = as_bf16x8(*reinterpret_cast<const i32x4*>(&slot[lds_off<BK>(wrow_l[i], c)]));
+#pragma unroll
+    for (int j = 0; j < TX; ++j)
+      fx[fb][j] = as_bf16x8(*reinterpret_cast<const i32x4*>(&slot[BN * BK + lds_off<BK>(xrow_l + 32 * j, c)]));
+  };
+  auto compute = [&](int st) {
+    if (!wlive) return;
+    const uint16_t* slot = smem + st * STAGE;
+    fload(0, slot, 0);
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      if (s + 1 < BK / 16) fload((s + 1) & 1, slot, s + 1);
 #pragma unroll
       for (int i = 0; i < TW; ++i)
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          uint32_t v[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = f32_to_bf16_rne(acc[i][j][4 * h + r]);
-          const int n = tc.col0 + wn * (BN / WN) + 32 * i + 8 * h + 4 * (lane >> 5);
-          *reinterpret_cast<uint2*>(o + n) = make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
-        }
+        for (int j = 0; j < TX; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[s & 1][i], fx[s & 1][j], acc[i][j], 0, 0, 0);
     }
+  };
+
+  // slices 0 .. NS-2 in flight; wait for slice 0
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p) issue(p, p);
+  wait_vmem<(NS - 2) * LPW>();
+  lds_barrier();
+  int st = 0;   // slot of slice kt
+  for (int kt = 0; kt < nk; ++kt) {
+    // slot (kt + NS - 1) % NS was read in iteration kt - 1, before the barrier that ended it
+    issue(kt + NS - 1, st == 0 ? NS - 1 : st - 1);
+    compute(st);
+    // slice kt+1 has landed once at most the NS-2 younger slices' loads remain
+    wait_vmem<(NS - 2) * LPW>();
+    lds_barrier();
+    st = st + 1 == NS ? 0 : st + 1;
   }
+  wait_vmem<0>();   // no load may write LDS after the workgroup has left it
+
+  tile_epilogue<EPI, BM, BN, WN, WM>(g, tc, acc, wn, wm, lane);
+}
+
+template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, int NS>
+hipError_t launch_dma(const GemmArgs& g, hipStream_t s) {
+  const int ncol = EPI == kEpiGateUp ? g.nfeat / (BN / 2) : g.nfeat / BN;
+  const int64_t nlog = g.max_tiles * 128 / BM * ncol;   // plan tiles are 128 routes
+  dim3 grid((unsigned)padded_blocks(nlog));
+  hipLaunchKernelGGL((gemm_tile_dma_kernel<EPI, BM, BN, BK, WN, WM, OCC, NS>), grid, dim3(64 * WN * WM), 0, s,
+                     g, ncol, nlog);
+  return hipGetLastError();
 }
 
 // Grid and launch of one tile configuration.
@@ -332,7 +535,7 @@ template <int EPI>
 hipError_t launch_layout(const GemmArgs& g, hipStream_t s) {
   // contiguous: 128 routes x 256 weight rows, 8 waves of 64x64, two
   // workgroups per CU; batched: 128 x 128, 4 waves of 64x64, route-major
-  if (g.rows.layout == 0) return launch<EPI, 128, 256, 32, 4, 2, 2, kWeightMajor>(g, s);
+  if (g.rows.layout == 0) return launch_dma<EPI, 128, 256, 32, 4, 2, 2, 3>(g, s);
   return launch<EPI, 128, 128, 64, 2, 2, 1, kRouteMajor>(g, s);
 }
 
