@@ -342,8 +342,8 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmA
 // The same tiles, fragments and epilogue as gemm_tile_bf16_kernel, but the
 // slices reach LDS by buffer loads that write LDS themselves (no registers,
 // no LDS store instructions), into a ring of NS slice buffers: slice kt+NS-1
-// is requested while slice kt is multiplied, so every load has NS-2 whole
-// slices of MFMA work to land, and each slice costs one wait and one
+// is requested as the multiplication of slice kt starts, so every load has
+// NS-1 slices of MFMA work to land, and each slice costs one wait and one
 // barrier.  One such load writes the 64 lanes' 16 bytes to 1 KB of LDS at a
 // wave-uniform address, lane i at byte 16 i; each lane therefore fetches the
 // chunk that the swizzled layout of lds_off places at its position.
@@ -375,7 +375,7 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_dma_kernel(GemmAr
   constexpr int LX = BM / RPB / NW;          // route blocks per wave per slice
   static_assert(LW * NW * RPB == BN && LX * NW * RPB == BM, "blocks / waves mismatch");
   constexpr int LPW = LW + LX;               // loads per wave per slice
-  static_assert((NS - 2) * LPW < 64 && NS >= 3, "ring depth");
+  static_assert((NS - 2) * LPW < 64 && NS >= 2, "ring depth");
   constexpr int STAGE = (BN + BM) * BK;      // elements per ring slot: weight rows, then routes
   constexpr int TW = BN / WN / 32;
   constexpr int TX = BM / WM / 32;
@@ -510,7 +510,8 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_dma_kernel(GemmAr
 template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, int NS>
 hipError_t launch_dma(const GemmArgs& g, hipStream_t s) {
   const int ncol = EPI == kEpiGateUp ? g.nfeat / (BN / 2) : g.nfeat / BN;
-  const int64_t nlog = g.max_tiles * 128 / BM * ncol;   // plan tiles are 128 routes
+  static_assert(BM == kTileRoutesContiguous, "a tile is one plan tile of routes");
+  const int64_t nlog = g.max_tiles * ncol;
   dim3 grid((unsigned)padded_blocks(nlog));
   hipLaunchKernelGGL((gemm_tile_dma_kernel<EPI, BM, BN, BK, WN, WM, OCC, NS>), grid, dim3(64 * WN * WM), 0, s,
                      g, ncol, nlog);
@@ -522,7 +523,7 @@ template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, int ORDER>
 hipError_t launch(const GemmArgs& g, hipStream_t s) {
   const int ncol = EPI == kEpiGateUp ? g.nfeat / (BN / 2) : g.nfeat / BN;
   int64_t nrow;
-  if (g.rows.layout == 0) nrow = g.max_tiles * 128 / BM;   // plan tiles are 128 routes
+  if (g.rows.layout == 0) nrow = g.max_tiles * kTileRoutesContiguous / BM;
   else nrow = (int64_t)g.E * ((g.rows.max_tokens + BM - 1) / BM);
   const int64_t nlog = nrow * ncol;
   dim3 grid((unsigned)(ORDER == kRouteMajor ? nlog : padded_blocks(nlog)));
@@ -533,15 +534,15 @@ hipError_t launch(const GemmArgs& g, hipStream_t s) {
 
 template <int EPI>
 hipError_t launch_layout(const GemmArgs& g, hipStream_t s) {
-  // contiguous: 128 routes x 256 weight rows, 8 waves of 64x64, two
-  // workgroups per CU; batched: 128 x 128, 4 waves of 64x64, route-major
-  if (g.rows.layout == 0) return launch_dma<EPI, 128, 256, 32, 4, 2, 2, 3>(g, s);
+  // contiguous: 256 routes x 256 weight rows, 16 waves of 64x64, 64-wide
+  // slices loaded straight into a 2-slot LDS ring (128 KB, one workgroup
+  // per CU); batched: 128 x 128, 4 waves of 64x64, route-major
+  if (g.rows.layout == 0) return launch_dma<EPI, 256, 256, 64, 4, 4, 4, 2>(g, s);
   return launch<EPI, 128, 128, 64, 2, 2, 1, kRouteMajor>(g, s);
 }
 
 }  // namespace tile
 
-// Plan tiles are 128 routes (block_m).
 hipError_t launch_gemm_tile_bf16(const GemmArgs& g, hipStream_t s) {
   if (g.epi == kEpiGateUp) return tile::launch_layout<kEpiGateUp>(g, s);
   return tile::launch_layout<kEpiDown>(g, s);

@@ -101,6 +101,12 @@ struct GemmArgs {
   int64_t out_ld;
 };
 
+// Routes per plan tile of the tiled kernels: the contiguous format's align
+// pads each expert's run to a multiple of kTileRoutesContiguous, which is
+// the route count of one contiguous tile; the batched tiles hold 128 rows.
+constexpr int kTileRoutesContiguous = 256;
+constexpr int kTileRowsBatched = 128;
+
 hipError_t launch_gemm_tile_bf16(const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_stream_bf16(const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_stream_mxfp8(const GemmArgs& g, hipStream_t s);

@@ -180,13 +180,13 @@ int moe_plan_init(moe_plan* plan, const moe_problem* prob) {
       // 32-bit buffer offsets: one expert's W1, the activation rows and z
       const int64_t act_rows = contiguous ? P.M : P.E * P.max_tokens;
       if (4 * P.I * P.K >= (1ll << 31) || 2 * act_rows * P.K >= (1ll << 31) ||
-          2 * (contiguous ? R + P.E * 128 : act_rows) * P.I >= (1ll << 31))
+          2 * (contiguous ? R + P.E * kTileRoutesContiguous : act_rows) * P.I >= (1ll << 31))
         return fail(plan, MOE_EUNSUPPORTED, "tiled kernels address one expert and the activations with 32-bit offsets");
       if (contiguous) {
         if (P.K % 256 || P.I % 128)
           return fail(plan, MOE_EUNSUPPORTED, "contiguous tiled kernels need K % 256 == 0 and I % 128 == 0");
         snprintf(plan->reason, sizeof(plan->reason),
-                 "tile: 256 weight rows x 128 routes per workgroup, LDS-staged MFMA");
+                 "tile: 256 weight rows x 256 routes per workgroup, slices loaded straight into LDS");
       } else {
         if (P.K % 128 || P.I % 64)
           return fail(plan, MOE_EUNSUPPORTED, "batched tiled kernels need K % 128 == 0 and I % 64 == 0");
@@ -196,7 +196,7 @@ int moe_plan_init(moe_plan* plan, const moe_problem* prob) {
     }
   }
   plan->variant = variant;
-  plan->block_m = variant == MOE_VARIANT_TILE ? 128 : 16;
+  plan->block_m = variant != MOE_VARIANT_TILE ? 16 : contiguous ? kTileRoutesContiguous : kTileRowsBatched;
   plan->reduce_kind = contiguous ? MOE_REDUCE_NOOP : MOE_REDUCE_NAIVE_BATCHED;
   plan->routes = R;
   const int64_t B = plan->block_m;

@@ -72,7 +72,7 @@ def test_plans_of_the_five_workloads(idx):
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert offs[-1] < p.ws13_bytes
     if idx == 2:
-        assert p.sorted_capacity == 81792            # 65536 + 128 * 127
+        assert p.sorted_capacity == 98048            # floor((65536 + 128 * 255) / 256) * 256
     if idx == 4:
         assert moe.moe_naive_batched_ws_bytes(p, 512) > 0
 
@@ -125,11 +125,11 @@ def test_variant_choice_and_override():
     p = moe.moe_plan_init(moe.make_problem(64, 256, 512, 8, topk=2))          # small layer
     assert p.variant == moe.VARIANT_FUSED
     p = moe.moe_plan_init(moe.make_problem(300, 256, 512, 8, topk=2))         # 75 rows per expert
-    assert p.variant == moe.VARIANT_TILE and p.block_m == 128
+    assert p.variant == moe.VARIANT_TILE and p.block_m == 256
     p = moe.moe_plan_init(moe.make_problem(16, 4096, 8192, 64, topk=8))       # weights past 1 GiB
     assert p.variant == moe.VARIANT_STREAM
     p = moe.moe_plan_init(moe.make_problem(17, 4096, 8192, 64, topk=8))
-    assert p.variant == moe.VARIANT_TILE and p.block_m == 128
+    assert p.variant == moe.VARIANT_TILE and p.block_m == 256
     p = moe.moe_plan_init(moe.make_problem(17, 256, 512, 8, topk=2, variant=moe.VARIANT_STREAM))
     assert p.variant == moe.VARIANT_STREAM and p.block_m == 16
     assert "stream" in moe.moe_plan_reason(p)

@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 def run_align(ids: np.ndarray, E: int, variant: int, expert_map=None):
     M, topk = ids.shape
     G = 0 if expert_map is None else len(expert_map)
-    plan = moe.moe_plan_init(moe.make_problem(M, 256, 512, E, topk=topk, variant=variant,
+    plan = moe.moe_plan_init(moe.make_problem(M, 256, 128, E, topk=topk, variant=variant,
                                               global_experts=G))
     ws13 = torch.full((plan.ws13_bytes,), 0xAB, dtype=torch.uint8, device="cuda")   # poison
     dev = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
