@@ -3,14 +3,20 @@
 // W1, act + mul, matmul with W2, unpermute) when experts hold many rows.
 //
 // A workgroup computes BN weight rows x BM route rows of one expert, stepping
-// through the contraction in BK-wide slices staged in LDS (double buffered;
-// 16-byte chunks XOR-swizzled so the 32-row fragment reads of an MFMA hit
-// distinct banks).  The waves form a WN x WM grid; each owns (BN/WN) weight
-// rows x (BM/WM) routes as tiles of v_mfma_f32_32x32x16_bf16 with the weight
-// rows in the MFMA row operand, so a lane's accumulators hold 4 consecutive
-// output features of one route and the epilogue writes 8-byte runs.  Inside
-// a slice the fragments of the next 16-wide k step are read from LDS while
-// the MFMAs of the current one run.
+// through the contraction in BK-wide slices.  The slices reach LDS by buffer
+// loads that write LDS themselves (no registers, no LDS store instructions)
+// into a ring of NS slice buffers: slice kt+NS-1 is requested as the
+// multiplication of slice kt starts, so every load has NS-1 slices of MFMA
+// work to land, and each slice costs one wait and one barrier.  In LDS the
+// 16-byte chunks of a row are XOR-swizzled so the 32-row fragment reads of an
+// MFMA hit distinct banks; one such load writes the 64 lanes' 16 bytes to
+// 1 KB of LDS at a wave-uniform address, lane i at byte 16 i, so each lane
+// fetches the chunk that the swizzle places at its position.  The waves form
+// a WN x WM grid; each owns (BN/WN) weight rows x (BM/WM) routes as tiles of
+// v_mfma_f32_32x32x16_bf16 with the weight rows in the MFMA row operand, so a
+// lane's accumulators hold 4 consecutive output features of one route and
+// the epilogue writes 8-byte runs.  Inside a slice the fragments of the next
+// 16-wide k step are read from LDS while the MFMAs of the current one run.
 //
 // W1 (kGateUp): the BN weight rows are BN/2 gate rows and the BN/2 matching up
 // rows; each wave holds gate and up values of the same (feature, route) in
@@ -174,179 +180,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const TileCoord
   }
 }
 
-template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, int ORDER>
-__global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmArgs g, int ncol,
-                                                                           int64_t nlog) {
-  constexpr int NT = 64 * WN * WM;
-  constexpr int CH = BK / 8;
-  constexpr int TW = BN / WN / 32;   // weight tiles per wave
-  constexpr int TX = BM / WM / 32;   // route tiles per wave
-  static_assert(EPI != kEpiGateUp || TW % 2 == 0, "gate/up pairs need an even tile count");
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2][BN * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t sX[2][BM * BK];
-
-  TileCoord tc;
-  if (!tile_coord<BM, BN, ORDER>(g, ncol, nlog, tc)) return;
-  const RowMap& rm = g.rows;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wn = wave / WM;
-  const int wm = wave % WM;
-  const int K = g.kdim;
-
-  // ---- global -> register staging: 16-byte chunk c = tid + NT*i -> row c/CH, chunk c%CH.
-  // Buffer loads with per-lane byte offsets and the slice's byte offset in
-  // the scalar operand; a padding route gets an offset past the buffer, which
-  // the range check turns into zeros.
-  constexpr int WCH = BN * CH / NT;   // weight chunks per thread
-  constexpr int XCH = BM * CH / NT;   // route chunks per thread
-  static_assert(WCH * NT == BN * CH && XCH * NT == BM * CH, "tile / thread mismatch");
-  const int kc = tid % CH;
-  const uint16_t* wexp = static_cast<const uint16_t*>(g.w) + (int64_t)tc.expert * g.w_expert_stride;
-  const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(wexp, g.w_expert_stride * 2);
-  const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(g.act, g.act_bytes);
-  uint32_t ow[WCH], ox[XCH];
-#pragma unroll
-  for (int i = 0; i < WCH; ++i) {
-    const int n = (tid + NT * i) / CH;
-    int wrow;
-    if (EPI == kEpiGateUp) {
-      const int f = tc.col0 / 2 + (n % (BN / 2));
-      const bool up = n >= BN / 2;
-      wrow = g.w1_order == 0 ? (up ? g.I + f : f) : (32 * (f >> 4) + (f & 15) + (up ? 16 : 0));
-    } else {
-      wrow = tc.col0 + n;
-    }
-    ow[i] = (uint32_t)((wrow * K + kc * 8) * 2);
-  }
-#pragma unroll
-  for (int i = 0; i < XCH; ++i) {
-    const int m = (tid + NT * i) / CH;
-    int64_t row = -1;
-    if (rm.layout == 0) {
-      if (EPI == kEpiGateUp) {
-        const int sid = rm.sorted_ids[tc.row0 + m];
-        if (sid != rm.sentinel) row = sid / rm.topk;
-      } else {
-        row = tc.row0 + m;
-      }
-    } else if (m < tc.nvalid) {
-      row = tc.row0 + m;
-    }
-    ox[i] = row >= 0 ? (uint32_t)((row * g.act_ld + kc * 8) * 2) : 0x80000000u;
-  }
-
-  // Two register sets: slice t lives in set t % 2 from its load to its LDS
-  // store two slices later, so each load has two slices of MFMA work to
-  // arrive.
-  i32x4 rw[2][WCH], rx[2][XCH];
-  const int nk = K / BK;
-  auto gload = [&](int set, int kt) {
-    const int kb = min(kt, nk - 1) * BK * 2;   // past the end: repeat the last slice (unused)
-#pragma unroll
-    for (int i = 0; i < WCH; ++i) rw[set][i] = __builtin_amdgcn_raw_buffer_load_b128(wr, ow[i], kb, 0);
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) rx[set][i] = __builtin_amdgcn_raw_buffer_load_b128(ar, ox[i], kb, 0);
-  };
-  auto sstore = [&](int buf, int set) {
-#pragma unroll
-    for (int i = 0; i < WCH; ++i)
-      *reinterpret_cast<i32x4*>(&sW[buf][lds_off<BK>((tid + NT * i) / CH, kc)]) = rw[set][i];
-#pragma unroll
-    for (int i = 0; i < XCH; ++i)
-      *reinterpret_cast<i32x4*>(&sX[buf][lds_off<BK>((tid + NT * i) / CH, kc)]) = rx[set][i];
-  };
-
-  // ---- this wave's MFMA tiles.  kGateUp: weight tiles [0, TW/2) are gate
-  // rows of the wave's features, tiles [TW/2, TW) the matching up rows.
-  int wrow_l[TW];
-#pragma unroll
-  for (int i = 0; i < TW; ++i) {
-    if (EPI == kEpiGateUp) {
-      constexpr int FW = BN / 2 / WN;   // features per wave
-      wrow_l[i] = (i < TW / 2 ? 0 : BN / 2) + wn * FW + 32 * (i % (TW / 2)) + (lane & 31);
-    } else {
-      wrow_l[i] = wn * (BN / WN) + 32 * i + (lane & 31);
-    }
-  }
-  const int xrow_l = wm * (BM / WM) + (lane & 31);
-  // a wave whose route rows all lie past the tile's valid rows holds only
-  // padding: it skips its fragment reads and MFMAs (its accumulators stay 0,
-  // what zero-filled padding rows would give) but still stages and meets
-  // the barriers; a wave-uniform branch
-  const bool wlive = __builtin_amdgcn_readfirstlane(wm) * (BM / WM) < tc.nvalid;
-
-  f32x16 acc[TW][TX];
-#pragma unroll
-  for (int i = 0; i < TW; ++i)
-#pragma unroll
-    for (int j = 0; j < TX; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  bf16x8 fw[2][TW], fx[2][TX];
-  auto fload = [&](int fb, int buf, int s) {
-    const int c = 2 * s + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < TW; ++i)
-      fw[fb][i] = as_bf16x8(*reinterpret_cast<const i32x4*>(&sW[buf][lds_off<BK>(wrow_l[i], c)]));
-#pragma unroll
-    for (int j = 0; j < TX; ++j)
-      fx[fb][j] = as_bf16x8(*reinterpret_cast<const i32x4*>(&sX[buf][lds_off<BK>(xrow_l + 32 * j, c)]));
-  };
-  auto compute = [&](int buf) {
-    if (!wlive) return;
-    fload(0, buf, 0);
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      if (s + 1 < BK / 16) fload((s + 1) & 1, buf, s + 1);
-#pragma unroll
-      for (int i = 0; i < TW; ++i)
-#pragma unroll
-        for (int j = 0; j < TX; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[s & 1][i], fx[s & 1][j], acc[i][j], 0, 0, 0);
-    }
-  };
-  // slice kt (LDS buffer and register set kt % 2, literals at each call):
-  // multiply it, store slice kt+1 (register set (kt+1) % 2) to the other
-  // buffer, refill that set with slice kt+3
-  auto step = [&](int p, int kt) {
-    compute(p);
-    __builtin_amdgcn_sched_barrier(0);
-    sstore(p ^ 1, p ^ 1);
-    __builtin_amdgcn_sched_barrier(0);
-    gload(p ^ 1, kt + 3);
-    __builtin_amdgcn_sched_barrier(0);
-    lds_barrier();
-  };
-
-  gload(0, 0);
-  gload(1, 1);
-  sstore(0, 0);
-  gload(0, 2);
-  lds_barrier();
-  int kt = 0;
-  for (; kt + 2 <= nk; kt += 2) {
-    step(0, kt);
-    step(1, kt + 1);
-  }
-  if (kt < nk) compute(0);
-
-  tile_epilogue<EPI, BM, BN, WN, WM>(g, tc, acc, wn, wm, lane);
-}
-
-// ---------------------------------------------------------------------------
-// Tile kernel with direct-to-LDS staging (contiguous format).
-//
-// The same tiles, fragments and epilogue as gemm_tile_bf16_kernel, but the
-// slices reach LDS by buffer loads that write LDS themselves (no registers,
-// no LDS store instructions), into a ring of NS slice buffers: slice kt+NS-1
-// is requested as the multiplication of slice kt starts, so every load has
-// NS-1 slices of MFMA work to land, and each slice costs one wait and one
-// barrier.  One such load writes the 64 lanes' 16 bytes to 1 KB of LDS at a
-// wave-uniform address, lane i at byte 16 i; each lane therefore fetches the
-// chunk that the swizzled layout of lds_off places at its position.
+// Loads that write LDS directly (see the top of the file).
 typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, uint16_t* dst, uint32_t vo, int so) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, vo, so, 0, 0);
@@ -364,8 +198,8 @@ __device__ __forceinline__ void wait_vmem() {
   asm volatile("" ::: "memory");
 }
 
-template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, int NS>
-__global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_dma_kernel(GemmArgs g, int ncol,
+template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, int NS, int ORDER>
+__global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmArgs g, int ncol,
                                                                           int64_t nlog) {
   constexpr int NW = WN * WM;
   constexpr int CH = BK / 8;                 // 16-byte chunks per row
@@ -383,7 +217,7 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_dma_kernel(GemmAr
   __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * STAGE];
 
   TileCoord tc;
-  if (!tile_coord<BM, BN, kWeightMajor>(g, ncol, nlog, tc)) return;
+  if (!tile_coord<BM, BN, ORDER>(g, ncol, nlog, tc)) return;
   const RowMap& rm = g.rows;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -417,7 +251,9 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_dma_kernel(GemmAr
     const int m = (wave + NW * i) * RPB + lane / CH;
     const int c = (lane % CH) ^ ((m / RPW) & (CH - 1));
     int64_t row = -1;
-    if (EPI == kEpiGateUp) {
+    if (rm.layout != 0) {
+      if (m < tc.nvalid) row = tc.row0 + m;   // rows past the expert's count are never read
+    } else if (EPI == kEpiGateUp) {
       const int sid = rm.sorted_ids[tc.row0 + m];
       if (sid != rm.sentinel) row = sid / rm.topk;
     } else {
@@ -452,7 +288,11 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_dma_kernel(GemmAr
     }
   }
   const int xrow_l = wm * (BM / WM) + (lane & 31);
-  const bool wlive = wm * (BM / WM) < tc.nvalid;   // see gemm_tile_bf16_kernel
+  // a wave whose route rows all lie past the tile's valid rows holds only
+  // padding: it skips its fragment reads and MFMAs (its accumulators stay 0,
+  // what zero-filled padding rows would give) but still issues its share of
+  // the loads and meets the barriers; a wave-uniform branch
+  const bool wlive = wm * (BM / WM) < tc.nvalid;
 
   f32x16 acc[TW][TX];
 #pragma unroll
@@ -507,38 +347,30 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_dma_kernel(GemmAr
   tile_epilogue<EPI, BM, BN, WN, WM>(g, tc, acc, wn, wm, lane);
 }
 
-template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, int NS>
-hipError_t launch_dma(const GemmArgs& g, hipStream_t s) {
-  const int ncol = EPI == kEpiGateUp ? g.nfeat / (BN / 2) : g.nfeat / BN;
-  static_assert(BM == kTileRoutesContiguous, "a tile is one plan tile of routes");
-  const int64_t nlog = g.max_tiles * ncol;
-  dim3 grid((unsigned)padded_blocks(nlog));
-  hipLaunchKernelGGL((gemm_tile_dma_kernel<EPI, BM, BN, BK, WN, WM, OCC, NS>), grid, dim3(64 * WN * WM), 0, s,
-                     g, ncol, nlog);
-  return hipGetLastError();
-}
-
-// Grid and launch of one tile configuration.
-template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, int ORDER>
+template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, int NS, int ORDER>
 hipError_t launch(const GemmArgs& g, hipStream_t s) {
   const int ncol = EPI == kEpiGateUp ? g.nfeat / (BN / 2) : g.nfeat / BN;
   int64_t nrow;
-  if (g.rows.layout == 0) nrow = g.max_tiles * kTileRoutesContiguous / BM;
-  else nrow = (int64_t)g.E * ((g.rows.max_tokens + BM - 1) / BM);
+  if (g.rows.layout == 0) {
+    if (BM != kTileRoutesContiguous) return hipErrorInvalidValue;   // a tile is one plan tile of routes
+    nrow = g.max_tiles;
+  } else {
+    nrow = (int64_t)g.E * ((g.rows.max_tokens + BM - 1) / BM);
+  }
   const int64_t nlog = nrow * ncol;
   dim3 grid((unsigned)(ORDER == kRouteMajor ? nlog : padded_blocks(nlog)));
-  hipLaunchKernelGGL((gemm_tile_bf16_kernel<EPI, BM, BN, BK, WN, WM, OCC, ORDER>), grid,
-                     dim3(64 * WN * WM), 0, s, g, ncol, nlog);
+  hipLaunchKernelGGL((gemm_tile_bf16_kernel<EPI, BM, BN, BK, WN, WM, OCC, NS, ORDER>), grid, dim3(64 * WN * WM),
+                     0, s, g, ncol, nlog);
   return hipGetLastError();
 }
 
 template <int EPI>
 hipError_t launch_layout(const GemmArgs& g, hipStream_t s) {
-  // contiguous: 256 routes x 256 weight rows, 16 waves of 64x64, 64-wide
-  // slices loaded straight into a 2-slot LDS ring (128 KB, one workgroup
-  // per CU); batched: 128 x 128, 4 waves of 64x64, route-major
-  if (g.rows.layout == 0) return launch_dma<EPI, 256, 256, 64, 4, 4, 4, 2>(g, s);
-  return launch<EPI, 128, 128, 64, 2, 2, 1, kRouteMajor>(g, s);
+  // contiguous: 256 routes x 256 weight rows, 16 waves of 64x64 (128 KB of
+  // LDS, one workgroup per CU); batched: 128 x 128, 4 waves of 64x64 (64 KB,
+  // two per CU), route-major; both with 64-wide slices in a 2-slot ring
+  if (g.rows.layout == 0) return launch<EPI, 256, 256, 64, 4, 4, 4, 2, kWeightMajor>(g, s);
+  return launch<EPI, 128, 128, 64, 2, 2, 2, 2, kRouteMajor>(g, s);
 }
 
 }  // namespace tile
