@@ -142,7 +142,8 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const TileCoord
 #pragma unroll
   for (int j = 0; j < TX; ++j) {
     const int m = wm * (BM / WM) + 32 * j + (lane & 31);
-    if (rm.layout != 0 && m >= tc.nvalid) continue;   // contiguous: padding rows of z are written (zeros)
+    if (rm.layout != 0 && m >= tc.nvalid) continue;   // batched: rows past the count are not written
+    const bool pad = m >= tc.nvalid;                   // contiguous padding: z rows of zeros
     int64_t orow;
     if (EPI == kEpiGateUp || rm.layout != 0) {
       orow = tc.row0 + m;
@@ -161,7 +162,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const TileCoord
           uint32_t v[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            v[r] = f32_to_bf16_rne(silu_f32(acc[i][j][4 * h + r]) * acc[i + TW / 2][j][4 * h + r]);
+            v[r] = pad ? 0u : f32_to_bf16_rne(silu_f32(acc[i][j][4 * h + r]) * acc[i + TW / 2][j][4 * h + r]);
           const int f = tc.col0 / 2 + wn * FW + 32 * i + 8 * h + 4 * (lane >> 5);
           *reinterpret_cast<uint2*>(o + f) = make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
         }
@@ -264,6 +265,15 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmA
 
   const int nk = K / BK;
   // request slice kt (past the end: the last slice again, never read) into slot st
+  // a route block whose rows are all padding is not loaded: its LDS rows keep
+  // stale values, which reach only those rows' own outputs (an MFMA output
+  // column depends on its route row alone), and the epilogue drops them or
+  // writes zeros in their place.  Fewer loads per flop is what this kernel is
+  // bound by (operand delivery from L2 into the CU).
+  bool xload[LX];
+#pragma unroll
+  for (int i = 0; i < LX; ++i)
+    xload[i] = __builtin_amdgcn_readfirstlane((int)((wave + NW * i) * RPB < tc.nvalid)) != 0;
   auto issue = [&](int kt, int st) {
     const int kb = min(kt, nk - 1) * BK * 2;
     uint16_t* slot = smem + st * STAGE;
@@ -272,7 +282,7 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmA
       load_to_lds16(wr, slot + (wave + NW * i) * RPB * BK, ow[i], kb);
 #pragma unroll
     for (int i = 0; i < LX; ++i)
-      load_to_lds16(ar, slot + BN * BK + (wave + NW * i) * RPB * BK, ox[i], kb);
+      if (xload[i]) load_to_lds16(ar, slot + BN * BK + (wave + NW * i) * RPB * BK, ox[i], kb);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
