@@ -89,8 +89,17 @@ __global__ void __launch_bounds__(64 * kMxWaves, 4) gemm_stream_mxfp8_kernel(Gem
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const RowMap& rm = g.rows;
-  const int slot = blockIdx.y;
-  if (slot >= rm.active[g.max_active]) return;
+  // work item (slot, feature block): the hardware deals blocks to the 8 XCDs
+  // round robin (block b on XCD b % 8); each XCD takes a contiguous range of
+  // the items of the active slots, so the feature blocks of one expert share
+  // an XCD and its L2 serves them the expert's staged activation rows
+  const int nfb = g.nfeat / ((EPI == kEpiGateUp ? 64 : 128) * TT);
+  const int64_t items = (int64_t)nfb * rm.active[g.max_active];
+  const int64_t per_xcd = (items + 7) / 8;
+  const int64_t k = blockIdx.x / 8;
+  const int64_t item = (blockIdx.x % 8) * per_xcd + k;
+  if (k >= per_xcd || item >= items) return;
+  const int slot = (int)(item / nfb);
   const int e = rm.active[slot];
   const int cnt = rm.counts[e];
   const int pos0 = rm.offsets[e];
@@ -98,7 +107,7 @@ __global__ void __launch_bounds__(64 * kMxWaves, 4) gemm_stream_mxfp8_kernel(Gem
   const int KB = K / 32;
   const int q = lane >> 4;
   const int l16 = lane & 15;
-  const int f0 = blockIdx.x * (EPI == kEpiGateUp ? 64 : 128) * TT;
+  const int f0 = (int)(item % nfb) * (EPI == kEpiGateUp ? 64 : 128) * TT;
   const int nsteps = K / 128;
   const int nchunks = nsteps / CS;
 
@@ -330,12 +339,14 @@ static hipError_t launch_mxfp8(const GemmArgs& g, hipStream_t s) {
   // steps when the features divide; W2 keeps one tile and chunks of 2 steps:
   // with more, its epilogue's registers no longer fit the 128 that let two
   // workgroups share a CU
+  // one block per (slot, feature block) work item of the largest possible
+  // slot count, rounded up to the 8 XCDs
+  auto blocks = [&](int feats) { return dim3((unsigned)((((int64_t)g.nfeat / feats) * g.max_active + 7) / 8 * 8)); };
   if (EPI == kEpiGateUp && g.nfeat % 128 == 0 && nsteps % 2 == 0) {
-    const dim3 grid(g.nfeat / 128, (unsigned)g.max_active);
-    hipLaunchKernelGGL((gemm_stream_mxfp8_kernel<kEpiGateUp, 2, 2>), grid, dim3(64 * kMxWaves), 0, s, g);
+    hipLaunchKernelGGL((gemm_stream_mxfp8_kernel<kEpiGateUp, 2, 2>), blocks(128), dim3(64 * kMxWaves), 0, s, g);
     return hipGetLastError();
   }
-  const dim3 grid(g.nfeat / (EPI == kEpiGateUp ? 64 : 128), (unsigned)g.max_active);
+  const dim3 grid = blocks(EPI == kEpiGateUp ? 64 : 128);
   if (EPI == kEpiGateUp && nsteps % 4 == 0)
     hipLaunchKernelGGL((gemm_stream_mxfp8_kernel<kEpiGateUp, 4, 1>), grid, dim3(64 * kMxWaves), 0, s, g);
   else if (nsteps % 2 == 0)
