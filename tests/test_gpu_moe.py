@@ -93,6 +93,35 @@ def test_tiny_intermediate_z():
         assert np.abs(z[p] - ref).max() <= 2e-2 * np.abs(ref).max() + 1e-3, p
 
 
+def test_tile_count_edges():
+    """Tile path with per-expert route counts at the edges of its 256-route
+    tiles and of its 8-row load blocks (an expert with none, 1, 7, 8, 9, 129,
+    255, 256, 257, 512), the routes shuffled over the tokens: the output
+    against the oracle, and every padding row of z exactly zero."""
+    counts = [1, 7, 8, 9, 255, 256, 257, 512, 0, 129]
+    E, R, topk = len(counts), sum(counts), 2
+    cfg = mi.config(2).scaled(M=R // topk, K=256, I=128, E=E, topk=topk)
+    c = make_case(cfg)
+    rng = np.random.default_rng(11)
+    keys = np.repeat(np.arange(E, dtype=np.int32), counts)
+    rng.shuffle(keys)
+    ids = keys.reshape(cfg.M, topk)
+    wts = rng.uniform(0.1, 1.0, size=(cfg.M, topk)).astype(np.float32)
+    out, plan, ws13, _ = run_contiguous(c, moe.VARIANT_TILE, ids=torch.from_numpy(ids).cuda(),
+                                        wts=torch.from_numpy(wts).cuda())
+    assert plan.variant == moe.VARIANT_TILE and plan.block_m == 256
+    check_close(out, oracle_contiguous(c, np.arange(cfg.M), ids, wts), BF16_REL, BF16_ABS, "tile_count_edges")
+    got_counts = moe.ws_view(ws13, plan.off_counts, E).cpu().numpy()
+    assert got_counts.tolist() == counts
+    sorted_ids = moe.ws_view(ws13, plan.off_sorted_ids, plan.sorted_capacity).cpu().numpy()
+    npost = int(moe.ws_view(ws13, plan.off_num_post_padded, 1).cpu()[0])
+    assert npost == sum(-(-n // 256) * 256 for n in counts)
+    z = moe.ws_view(ws13, plan.off_z, plan.sorted_capacity * cfg.I, torch.bfloat16).view(-1, cfg.I)[:npost]
+    pad = torch.from_numpy(np.flatnonzero(sorted_ids[:npost] == R)).cuda()
+    assert pad.numel() == npost - R
+    assert torch.all(z[pad].view(torch.int16) == 0)
+
+
 def test_nullity_and_equivariance():
     cfg = mi.config(2).scaled(M=300, K=256, I=256, E=16)
     c = make_case(cfg)
