@@ -49,6 +49,10 @@ __global__ void __launch_bounds__(256) align_hist_kernel(AlignArgs a) {
 
 // Launch 2: each bucket's histogram row scanned over the chunks (in place:
 // each chunk's starting rank), a wave per bucket, then the bucket layout.
+// A wave takes kScanBatch of its buckets at a time and issues their loads
+// together, so it waits for memory once per batch rather than once per
+// bucket.
+constexpr int kScanBatch = 8;
 __global__ void __launch_bounds__(1024) align_scan_kernel(AlignArgs a) {
   __shared__ int s_cnt[kAlignMaxBuckets + 1];
   __shared__ int s_off[kAlignMaxBuckets + 1];
@@ -56,22 +60,36 @@ __global__ void __launch_bounds__(1024) align_scan_kernel(AlignArgs a) {
   const int lane = __lane_id();
   const int wave = threadIdx.x / kWave;
   const int nwaves = blockDim.x / kWave;
-  for (int e = wave; e <= a.nb; e += nwaves) {
-    int32_t* row = a.block_hist + (int64_t)e * a.nblocks;
-    int run = 0;
+  for (int e0 = wave; e0 <= a.nb; e0 += nwaves * kScanBatch) {
+    int run[kScanBatch];
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) run[u] = 0;
     for (int b0 = 0; b0 < a.nblocks; b0 += kWave) {
       const int b = b0 + lane;
-      const int v = b < a.nblocks ? row[b] : 0;
-      int x = v;
+      int v[kScanBatch];
 #pragma unroll
-      for (int d = 1; d < kWave; d <<= 1) {
-        const int y = __shfl_up(x, d);
-        if (lane >= d) x += y;
+      for (int u = 0; u < kScanBatch; ++u) {
+        const int e = e0 + u * nwaves;
+        v[u] = (e <= a.nb && b < a.nblocks) ? a.block_hist[(int64_t)e * a.nblocks + b] : 0;
       }
-      if (b < a.nblocks) row[b] = run + x - v;
-      run += __shfl(x, kWave - 1);
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) {
+        const int e = e0 + u * nwaves;
+        int x = v[u];
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+          const int y = __shfl_up(x, d);
+          if (lane >= d) x += y;
+        }
+        if (e <= a.nb && b < a.nblocks) a.block_hist[(int64_t)e * a.nblocks + b] = run[u] + x - v[u];
+        run[u] += __shfl(x, kWave - 1);
+      }
     }
-    if (lane == 0) s_cnt[e] = run;
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) {
+      const int e = e0 + u * nwaves;
+      if (lane == 0 && e <= a.nb) s_cnt[e] = run[u];
+    }
   }
   __syncthreads();
   if (threadIdx.x == 0) a.status[0] = s_cnt[a.nb];
