@@ -131,28 +131,29 @@ __device__ __forceinline__ bool tile_coord(const GemmArgs& g, int ncol, int64_t 
   return true;
 }
 
-// Epilogue shared by the tile kernels.  acc[i][j][r]: weight row (tile i)
-// 8*(r/4) + 4*(lane/32) + r%4, route wm*(BM/WM) + 32*j + lane%32; registers
-// 4h..4h+3 are 4 consecutive rows.
-template <int EPI, int BM, int BN, int WN, int WM, int TW, int TX>
+// Epilogue.  acc[i][j][r]: weight row (tile i) 8*(r/4) + 4*(lane/32) + r%4,
+// route wm*(BM/WM) + 32*j + lane%32; registers 4h..4h+3 are 4 consecutive
+// rows, i.e. 4 consecutive output features of one route.  The tile's bf16
+// outputs are first laid out row by row in LDS (the staging ring is free by
+// then), 16-byte chunks XOR-swizzled by row so that both the writes from the
+// accumulators (one chunk of 32 rows per instruction) and the row reads
+// spread over the banks; then each row's segment of the output goes out in
+// 16-byte stores, whole segments per group of lanes, instead of 8-byte
+// pieces of 32 rows per store instruction.
+template <int EPI, int BM, int BN, int WN, int WM, int NT, int TW, int TX>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const TileCoord& tc,
-                                              const f32x16 (&acc)[TW][TX], int wn, int wm, int lane) {
+                                              const f32x16 (&acc)[TW][TX], int wn, int wm, int lane,
+                                              uint16_t* stage) {
+  constexpr int OUTF = EPI == kEpiGateUp ? BN / 2 : BN;   // output features per route row
+  constexpr int NCH = OUTF / 8;                            // 16-byte chunks per row
+  static_assert(NCH <= 64 && (NCH & (NCH - 1)) == 0, "row segment: a power of two of at most 64 chunks");
   const RowMap& rm = g.rows;
-  uint16_t* out = static_cast<uint16_t*>(g.out);
+  // element offset of chunk c of row m
+  auto chunk_at = [](int m, int c) { return (m * NCH + (c ^ (m & (NCH - 1)))) * 8; };
 #pragma unroll
   for (int j = 0; j < TX; ++j) {
     const int m = wm * (BM / WM) + 32 * j + (lane & 31);
-    if (rm.layout != 0 && m >= tc.nvalid) continue;   // batched: rows past the count are not written
-    const bool pad = m >= tc.nvalid;                   // contiguous padding: z rows of zeros
-    int64_t orow;
-    if (EPI == kEpiGateUp || rm.layout != 0) {
-      orow = tc.row0 + m;
-    } else {
-      const int sid = rm.sorted_ids[tc.row0 + m];
-      if (sid == rm.sentinel) continue;
-      orow = sid;
-    }
-    uint16_t* o = out + orow * g.out_ld;
+    const bool pad = m >= tc.nvalid;   // contiguous W1: padding rows of z are zeros
     if (EPI == kEpiGateUp) {
       constexpr int FW = BN / 2 / WN;
 #pragma unroll
@@ -163,8 +164,9 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const TileCoord
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             v[r] = pad ? 0u : f32_to_bf16_rne(silu_f32(acc[i][j][4 * h + r]) * acc[i + TW / 2][j][4 * h + r]);
-          const int f = tc.col0 / 2 + wn * FW + 32 * i + 8 * h + 4 * (lane >> 5);
-          *reinterpret_cast<uint2*>(o + f) = make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
+          const int f = wn * FW + 32 * i + 8 * h + 4 * (lane >> 5);
+          *reinterpret_cast<uint2*>(stage + chunk_at(m, f / 8) + (f & 7)) =
+              make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
         }
     } else {
 #pragma unroll
@@ -174,10 +176,28 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const TileCoord
           uint32_t v[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = f32_to_bf16_rne(acc[i][j][4 * h + r]);
-          const int n = tc.col0 + wn * (BN / WN) + 32 * i + 8 * h + 4 * (lane >> 5);
-          *reinterpret_cast<uint2*>(o + n) = make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
+          const int f = wn * (BN / WN) + 32 * i + 8 * h + 4 * (lane >> 5);
+          *reinterpret_cast<uint2*>(stage + chunk_at(m, f / 8) + (f & 7)) =
+              make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
         }
     }
+  }
+  lds_barrier();
+  uint16_t* out = static_cast<uint16_t*>(g.out);
+  const int col = EPI == kEpiGateUp ? tc.col0 / 2 : tc.col0;
+  const int c = threadIdx.x % NCH;
+  for (int m = threadIdx.x / NCH; m < BM; m += NT / NCH) {
+    if (rm.layout != 0 && m >= tc.nvalid) continue;   // batched: rows past the count are not written
+    int64_t orow;
+    if (EPI == kEpiGateUp || rm.layout != 0) {
+      orow = tc.row0 + m;
+    } else {
+      const int sid = rm.sorted_ids[tc.row0 + m];       // W2: the route's (token, slot) row
+      if (sid == rm.sentinel) continue;                 // padding rows are dropped
+      orow = sid;
+    }
+    *reinterpret_cast<i32x4*>(out + orow * g.out_ld + col + 8 * c) =
+        *reinterpret_cast<const i32x4*>(stage + chunk_at(m, c));
   }
 }
 
@@ -352,9 +372,12 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmA
     lds_barrier();
     st = st + 1 == NS ? 0 : st + 1;
   }
-  wait_vmem<0>();   // no load may write LDS after the workgroup has left it
-
-  tile_epilogue<EPI, BM, BN, WN, WM>(g, tc, acc, wn, wm, lane);
+  // every wave's loads have landed and every wave is done with the ring
+  // before the epilogue reuses it (and before the workgroup leaves its LDS)
+  wait_vmem<0>();
+  lds_barrier();
+  static_assert(BM * (EPI == kEpiGateUp ? BN / 2 : BN) <= NS * STAGE, "epilogue tile fits the ring");
+  tile_epilogue<EPI, BM, BN, WN, WM, 64 * WN * WM>(g, tc, acc, wn, wm, lane, smem);
 }
 
 template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, int NS, int ORDER>
