@@ -284,18 +284,19 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmA
   }
 
   const int nk = K / BK;
-  // request slice kt (past the end: the last slice again, never read) into slot st
-  // a route block whose rows are all padding is not loaded: its LDS rows keep
+  // A route block whose rows are all padding is not loaded: its LDS rows keep
   // stale values, which reach only those rows' own outputs (an MFMA output
   // column depends on its route row alone), and the epilogue drops them or
-  // writes zeros in their place.  Fewer loads per flop is what this kernel is
-  // bound by (operand delivery from L2 into the CU).
+  // writes zeros in their place.  Only with a 2-slot ring, whose waits are
+  // for every outstanding load: deeper rings count a fixed LPW loads per
+  // slice in their waits.
   bool xload[LX];
 #pragma unroll
   for (int i = 0; i < LX; ++i)
-    xload[i] = __builtin_amdgcn_readfirstlane((int)((wave + NW * i) * RPB < tc.nvalid)) != 0;
+    xload[i] = NS > 2 || __builtin_amdgcn_readfirstlane((int)((wave + NW * i) * RPB < tc.nvalid)) != 0;
+  // request slice kt into slot st
   auto issue = [&](int kt, int st) {
-    const int kb = min(kt, nk - 1) * BK * 2;
+    const int kb = kt * BK * 2;
     uint16_t* slot = smem + st * STAGE;
 #pragma unroll
     for (int i = 0; i < LW; ++i)
@@ -359,16 +360,23 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmA
 
   // slices 0 .. NS-2 in flight; wait for slice 0
 #pragma unroll
-  for (int p = 0; p < NS - 1; ++p) issue(p, p);
-  wait_vmem<(NS - 2) * LPW>();
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < nk) issue(p, p);
+  if (nk >= NS - 1) wait_vmem<(NS - 2) * LPW>();
+  else wait_vmem<0>();
   lds_barrier();
   int st = 0;   // slot of slice kt
   for (int kt = 0; kt < nk; ++kt) {
-    // slot (kt + NS - 1) % NS was read in iteration kt - 1, before the barrier that ended it
-    issue(kt + NS - 1, st == 0 ? NS - 1 : st - 1);
+    // slot (kt + NS - 1) % NS was read in iteration kt - 1, before the barrier
+    // that ended it.  Past the last slice nothing is requested (a reload
+    // would only add its latency to the tile's end), and the waits that
+    // counted on those loads wait for everything instead.
+    const bool more = kt + NS - 1 < nk;
+    if (more) issue(kt + NS - 1, st == 0 ? NS - 1 : st - 1);
     compute(st);
     // slice kt+1 has landed once at most the NS-2 younger slices' loads remain
-    wait_vmem<(NS - 2) * LPW>();
+    if (more) wait_vmem<(NS - 2) * LPW>();
+    else wait_vmem<0>();
     lds_barrier();
     st = st + 1 == NS ? 0 : st + 1;
   }
