@@ -216,6 +216,33 @@ def test_batched_scaled():
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
 
+def test_batched_count_edges():
+    """Batched tiles with per-expert row counts at the edges of the 128-row
+    tiles and 8-row load blocks (0, 1, 7, 8, 9, 127, 128, 129, 255, 256, 257,
+    max_tokens=512); rows past the counts hold NaN and must never be read."""
+    counts = np.array([0, 1, 7, 8, 9, 127, 128, 129, 255, 256, 257, 512], dtype=np.int32)
+    cfg = mi.config(4).scaled(E=len(counts), max_tokens=512, K=256, I=128, M=64, slot_pool=int(counts.sum()))
+    c = make_case(cfg)
+    rng = np.random.default_rng(7)
+    row_token = rng.integers(0, cfg.M, size=(cfg.E, cfg.max_tokens)).astype(np.int32)
+    row_weight = rng.uniform(0.0, 1.0, size=(cfg.E, cfg.max_tokens)).astype(np.float32)
+    c.inp.expert_num_tokens, c.inp.row_token, c.inp.row_weight = counts, row_token, row_weight
+    c.counts = torch.from_numpy(counts).cuda()
+    c.row_token = torch.from_numpy(row_token).cuda()
+    c.row_weight = torch.from_numpy(row_weight).cuda()
+    junk = torch.arange(cfg.max_tokens, device="cuda")[None, :] >= c.counts[:, None]
+    c.inp.a[junk] = float("nan")
+    y, out, plan = run_batched(c)
+    w1_of, w2_of = oracle_weights(c)
+    a_host = c.inp.a.cpu()
+    ys = oracle.moe_batched_rows(lambda e, r: _host_f64(a_host[e][torch.from_numpy(r)]), counts,
+                                 w1_of, w2_of)
+    for e, (rows, ye) in ys.items():
+        check_close(y[e][torch.from_numpy(rows).cuda()], ye, BF16_REL, BF16_ABS, f"batched edges y e={e}")
+    ref = oracle.naive_batched_reduce(lambda e, r: ys[e][1][r], counts, row_token, row_weight, cfg.M, cfg.K)
+    check_close(out, ref, BF16_REL, BF16_ABS, "batched edges out")
+
+
 # ------------------------------------------------------------- full size --
 
 def test_full_decode():
