@@ -47,6 +47,38 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Buffer loads that write LDS themselves (buffer_load_dword{x4} ... lds):
+// one instruction writes the 64 lanes' 4 or 16 bytes to consecutive LDS at
+// the wave-uniform address dst, lane i at byte 4i or 16i.  A lane whose
+// offset is past the buffer writes zeros.  The compiler does not count these
+// loads in its own waits: the kernels wait for them with wait_vm.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t vo, int so) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, vo, so, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t vo, int so) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, vo, so, 0, 0);
+}
+
+// Keeps every instruction on its side: explicit vmcnt waits count loads in
+// program order, so neither the compiler's IR passes (memory clobber) nor
+// its scheduler may move a load across one of these.
+__device__ __forceinline__ void issue_order() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding: vmcnt
+// in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8); the memory clobbers keep
+// loads from moving across it.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xf00);
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 __device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + expf(-v)); }

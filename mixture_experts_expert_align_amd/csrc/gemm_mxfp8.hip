@@ -50,31 +50,6 @@ constexpr int kMxWaves = 8;
 constexpr int kMxStepA = kMxTok * 128;           // token code bytes per step
 constexpr int kMxStepAS = kMxTok * 4;            // token scale bytes per step (one wave's slot)
 
-typedef __attribute__((address_space(3))) void lds_void;
-__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint8_t* dst, uint32_t vo, int so) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, vo, so, 0, 0);
-}
-__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, uint8_t* dst, uint32_t vo, int so) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, vo, so, 0, 0);
-}
-// Keeps every instruction on its side: the explicit vmcnt waits below count
-// loads in program order, so neither the compiler's IR passes (memory
-// clobber) nor its scheduler may move a load across one of these.
-__device__ __forceinline__ void issue_order() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding: vmcnt
-// in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xf00);
-  asm volatile("" ::: "memory");
-}
-
 // CS: steps per chunk (4, 2 or 1, dividing the contraction's step count);
 // the weights stream CS steps ahead.  TT: 16-row weight tiles per wave (2
 // for W1: each staged activation fragment then feeds two MFMAs, and the

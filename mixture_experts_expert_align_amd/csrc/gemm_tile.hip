@@ -201,24 +201,6 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const TileCoord
   }
 }
 
-// Loads that write LDS directly (see the top of the file).
-typedef __attribute__((address_space(3))) void lds_void;
-__device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, uint16_t* dst, uint32_t vo, int so) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, vo, so, 0, 0);
-}
-
-// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt in bits
-// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).  The compiler does not count the
-// LDS-writing loads, so the waits that cover them are explicit; the memory
-// clobbers keep loads from moving across them.
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xf00);
-  asm volatile("" ::: "memory");
-}
-
 template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, int NS, int ORDER>
 __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmArgs g, int ncol,
                                                                           int64_t nlog) {
@@ -300,12 +282,11 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmA
     uint16_t* slot = smem + st * STAGE;
 #pragma unroll
     for (int i = 0; i < LW; ++i)
-      load_to_lds16(wr, slot + (wave + NW * i) * RPB * BK, ow[i], kb);
+      lds_load16(wr, slot + (wave + NW * i) * RPB * BK, ow[i], kb);
 #pragma unroll
     for (int i = 0; i < LX; ++i)
-      if (xload[i]) load_to_lds16(ar, slot + BN * BK + (wave + NW * i) * RPB * BK, ox[i], kb);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
+      if (xload[i]) lds_load16(ar, slot + BN * BK + (wave + NW * i) * RPB * BK, ox[i], kb);
+    issue_order();
   };
 
   int wrow_l[TW];
@@ -362,8 +343,8 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmA
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p)
     if (p < nk) issue(p, p);
-  if (nk >= NS - 1) wait_vmem<(NS - 2) * LPW>();
-  else wait_vmem<0>();
+  if (nk >= NS - 1) wait_vm<(NS - 2) * LPW>();
+  else wait_vm<0>();
   lds_barrier();
   int st = 0;   // slot of slice kt
   for (int kt = 0; kt < nk; ++kt) {
@@ -375,14 +356,14 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmA
     if (more) issue(kt + NS - 1, st == 0 ? NS - 1 : st - 1);
     compute(st);
     // slice kt+1 has landed once at most the NS-2 younger slices' loads remain
-    if (more) wait_vmem<(NS - 2) * LPW>();
-    else wait_vmem<0>();
+    if (more) wait_vm<(NS - 2) * LPW>();
+    else wait_vm<0>();
     lds_barrier();
     st = st + 1 == NS ? 0 : st + 1;
   }
   // every wave's loads have landed and every wave is done with the ring
   // before the epilogue reuses it (and before the workgroup leaves its LDS)
-  wait_vmem<0>();
+  wait_vm<0>();
   lds_barrier();
   static_assert(BM * (EPI == kEpiGateUp ? BN / 2 : BN) <= NS * STAGE, "epilogue tile fits the ring");
   tile_epilogue<EPI, BM, BN, WN, WM, 64 * WN * WM>(g, tc, acc, wn, wm, lane, smem);
