@@ -1,4 +1,4 @@
-"""HIP graph capture of the library's calls.
+"""HIP graph capture of the library's calls, and calls on two streams at once.
 
 The boundary documents that a call only enqueues kernels on the caller's
 stream (no host synchronisation, no allocation, grid sizes from the plan
@@ -107,3 +107,30 @@ def test_graph_batched():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(bits(gb[3]), ref), f"batched: replay {i} differs from the eager call"
+
+
+def test_two_streams():
+    """Reentrancy: two problems with workspaces of their own, issued
+    interleaved on two streams, give their single-stream outputs bit for bit."""
+    cases = [(mi.config(2).scaled(M=700, K=512, I=384, E=24), moe.VARIANT_AUTO),
+             (mi.config(1).scaled(K=512, I=1024), moe.VARIANT_STREAM)]
+    runs = []
+    for cfg, variant in cases:
+        c = make_case(cfg)
+        plan = moe.moe_plan_init(problem(cfg, variant))
+        ws13, ws2 = moe.allocate_workspaces(plan)
+        out = torch.empty((cfg.M, cfg.K), dtype=torch.bfloat16, device="cuda")
+        moe.moe_apply_contiguous(plan, c.inp.x, c.ids, c.wts, c.w1, c.w2, out, ws13, ws2)
+        torch.cuda.synchronize()
+        runs.append((c, plan, ws13, ws2, out, bits(out)))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for i in range(REPLAYS):
+        for (c, plan, ws13, ws2, out, _), s in zip(runs, streams):
+            with torch.cuda.stream(s):
+                out.fill_(float("nan"))
+                moe.moe_apply_contiguous(plan, c.inp.x, c.ids, c.wts, c.w1, c.w2, out, ws13, ws2)
+    torch.cuda.synchronize()
+    for (c, plan, _, _, out, ref) in runs:
+        assert torch.equal(bits(out), ref), f"{c.cfg.name}: two-stream output differs"
