@@ -342,8 +342,12 @@ __global__ void __launch_bounds__(RowsTile::NT, 4) train_rows_kernel(TrainArgs t
 __global__ void __launch_bounds__(WgradTile::NT, 2) train_wgrad_kernel(TrainArgs t) {
   using T = WgradTile;
   constexpr int BI = T::BI, BJ = T::BJ;
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][T::BI * T::BC];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][T::BJ * T::BC];
+  // the two operand buffers, then (after the contraction) the fp32 C tile
+  constexpr int kRing = 2 * (T::BI + T::BJ) * T::BC;   // uint16 elements
+  static_assert(kRing * 2 >= BI * BJ * 4, "the C tile fits the operand buffers");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kRing];
+  auto sA = reinterpret_cast<uint16_t(*)[T::BI * T::BC]>(smem);
+  auto sB = reinterpret_cast<uint16_t(*)[T::BJ * T::BC]>(smem + 2 * T::BI * T::BC);
   // blocks (n tile, k tile) with k fastest, per group: dealt round robin,
   // XCD x sees the k tiles congruent to x mod 8 for every n tile, so those x
   // slices stay in its L2 (runs of 8 consecutive k tiles per XCD measured
@@ -373,26 +377,51 @@ __global__ void __launch_bounds__(WgradTile::NT, 2) train_wgrad_kernel(TrainArgs
   B.nc = m;
   f32x16 acc[2][2];
   tile_mma<T, true, true>(A, B, n0, k0, m, sA, sB, acc);
-  float* out = static_cast<float*>(t.out) + (int64_t)e * t.N * t.K;
+  // Epilogue through LDS (tile_mma's last barrier freed it): the C tile is
+  // laid out row by row (16-byte chunks of 4 k, XOR-swizzled by row so the
+  // writes from the accumulators — one chunk of 32 rows per instruction —
+  // and the row reads spread over the banks); then each row's 512-byte
+  // segment is read from main_grad, added and written back by 32 lanes,
+  // every thread's loads of the previous values issued together.
+  constexpr int NCH = BJ / 4;                  // 16-byte chunks per C row
+  float* stage = reinterpret_cast<float*>(smem);
+  auto chunk_at = [](int r, int c) { return (r * NCH + (c ^ (r & (NCH - 1)))) * 4; };
 #pragma unroll
   for (int tx = 0; tx < 2; ++tx) {
-    const int n = n0 + 64 * wm + 32 * tx + (lane & 31);
-    float* o = out + (int64_t)n * t.K;
+    const int r = 64 * wm + 32 * tx + (lane & 31);
 #pragma unroll
     for (int tw = 0; tw < 2; ++tw)
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        const int k = k0 + 64 * wn + 32 * tw + 8 * h + 4 * (lane >> 5);
-        if (k >= t.K) continue;   // a partial last column tile
-        f32x4 v = {acc[tw][tx][4 * h], acc[tw][tx][4 * h + 1], acc[tw][tx][4 * h + 2], acc[tw][tx][4 * h + 3]};
-        f32x4* dst = reinterpret_cast<f32x4*>(o + k);
-        if (t.accumulate) {
-          const f32x4 prev = *dst;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = prev[q] + v[q];
-        }
-        *dst = v;
+        const int c = (64 * wn + 32 * tw + 8 * h + 4 * (lane >> 5)) / 4;
+        *reinterpret_cast<f32x4*>(stage + chunk_at(r, c)) =
+            (f32x4){acc[tw][tx][4 * h], acc[tw][tx][4 * h + 1], acc[tw][tx][4 * h + 2], acc[tw][tx][4 * h + 3]};
       }
+  }
+  lds_barrier();
+  float* out = static_cast<float*>(t.out) + (int64_t)e * t.N * t.K;
+  constexpr int RPP = T::NT / NCH;             // rows per pass of the workgroup
+  constexpr int NP = BI / RPP;                 // passes
+  const int c = threadIdx.x % NCH;
+  const int k = k0 + 4 * c;
+  f32x4 prev[NP];
+  if (t.accumulate) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int r = threadIdx.x / NCH + RPP * p;
+      if (k < t.K) prev[p] = *reinterpret_cast<const f32x4*>(out + (int64_t)(n0 + r) * t.K + k);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int r = threadIdx.x / NCH + RPP * p;
+    if (k >= t.K) continue;   // a partial last column tile
+    f32x4 v = *reinterpret_cast<const f32x4*>(stage + chunk_at(r, c));
+    if (t.accumulate) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = prev[p][q] + v[q];
+    }
+    *reinterpret_cast<f32x4*>(out + (int64_t)(n0 + r) * t.K + k) = v;
   }
 }
 
