@@ -190,7 +190,11 @@ typedef struct moe_plan {
  * follow-up: a prebuilt library whose argument list no longer matches). */
 int moe_abi_version(void);
 
-/* Static string for a status code. */
+/* Static string for a status code, the readable companion of the plan's
+ * reason field (page "Cake deterministic MoE grouped GEMM", section 1 and
+ * its closing lessons: the plan records why a path was not taken, in a
+ * diagnostic field meant for callers and tests).  Never NULL; unknown codes
+ * give "unknown status".  The string is owned by the library. */
 const char* moe_status_string(int status);
 
 /* sizeof(moe_problem), sizeof(moe_plan) and sizeof(moe_weights) as compiled
@@ -198,7 +202,11 @@ const char* moe_status_string(int status);
  * Each pointer may be NULL. */
 void moe_struct_sizes(int64_t* problem, int64_t* plan, int64_t* weights);
 
-/* Validate `prob` (host) and fill `plan` (host).  Chooses the kernel variant
+/* Validate `prob` (host) and fill `plan` (host): the workspace sizes of page
+ * "Fused MoE Modular Kernel", section "workspace_shapes()" (the caller
+ * allocates ws13 and ws2 of the sizes the plan states, once, at the largest
+ * size it needs), and the reduce kind of section
+ * "finalize_weight_and_reduce_impl()".  Chooses the kernel variant
  * (STREAM when at most 64 rows can reach one expert, else TILE), the align
  * tile size, the workspace sizes and the reduce kind (NOOP for contiguous,
  * NAIVE_BATCHED for batched).  Errors: MOE_EINVAL for null pointers,
@@ -210,7 +218,11 @@ void moe_struct_sizes(int64_t* problem, int64_t* plan, int64_t* weights);
  * and MXFP8 kernels K % 128 == 0 and I % 128 == 0. */
 int moe_plan_init(moe_plan* plan, const moe_problem* prob);
 
-/* plan->reason. */
+/* plan->reason: why moe_plan_init chose this kernel family, or why it
+ * refused the problem (page "Cake deterministic MoE grouped GEMM", section 1:
+ * the plan's accumulate_reason says why the fused route was not taken; the
+ * closing lessons: such a field serves both callers and tests).  `plan` is
+ * host memory; returns "" for NULL.  The string lives inside the plan. */
 const char* moe_plan_reason(const moe_plan* plan);
 
 /* Permute (page "Fused MoE Modular Kernel", apply() step 1): group the flat
@@ -263,7 +275,11 @@ int moe_down_unpermute(const moe_plan* plan, const moe_weights* w, void* ws13, v
 int moe_apply_batched(const moe_plan* plan, const void* a, const int32_t* expert_num_tokens,
                       const moe_weights* w, void* y, void* ws13, void* stream);
 
-/* TopKWeightAndReduceContiguous on its own.  y: device bf16 [M*topk, K], row
+/* TopKWeightAndReduceContiguous on its own (page "Fused MoE Modular
+ * Kernel", section "TopKWeightAndReduce": the contiguous policy weights each
+ * (token, slot) row and sums the slots of a token; page "Cake MegaMoE EP16
+ * backend for BF16 activations and MXFP8 weights", section 3: the ordered
+ * Top-K reduce over the per-(token, slot) buffer).  y: device bf16 [M*topk, K], row
  * t*topk+j is slot (t, j); out: device bf16 [M, K]; expert_map as for
  * moe_align_permute; same arithmetic as the reduce inside
  * moe_apply_contiguous. */

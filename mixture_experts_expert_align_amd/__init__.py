@@ -22,7 +22,8 @@ __all__ = [
     "moe_plan_reason", "moe_align_permute", "moe_apply_contiguous", "moe_apply_batched",
     "moe_gate_up_act", "moe_down_unpermute",
     "moe_topk_reduce_contiguous", "moe_naive_batched_ws_bytes", "moe_topk_reduce_naive_batched",
-    "moe_quantize_mxfp8", "make_problem", "allocate_workspaces", "ws_view",
+    "moe_quantize_mxfp8", "make_problem", "allocate_workspaces", "ws_view", "status_words",
+    "check_status",
     "MoeGroupedProblem", "moe_grouped_forward", "moe_grouped_dgrad", "moe_grouped_wgrad",
 ]
 
@@ -144,6 +145,27 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr()
 
 
+def _arg(t: Optional[torch.Tensor], name: str, dtypes, numel: int) -> Optional[int]:
+    """Device pointer of ``t`` after checking its dtype and that it holds at
+    least ``numel`` elements (the kernels read or write that many)."""
+    if t is None:
+        return None
+    if not isinstance(dtypes, tuple):
+        dtypes = (dtypes,)
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
+    if t.numel() < numel:
+        raise ValueError(f"{name}: {t.numel()} elements, the call needs {numel}")
+    return _ptr(t)
+
+
+def _ws(t: torch.Tensor, name: str, nbytes: int) -> int:
+    """A workspace: any dtype, at least ``nbytes`` bytes."""
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name}: {t.numel() * t.element_size()} bytes, the plan needs {nbytes}")
+    return _ptr(t)
+
+
 def _stream(stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -190,52 +212,102 @@ def ws_view(ws: torch.Tensor, offset: int, count: int, dtype=torch.int32) -> tor
     return ws[offset: offset + nbytes].view(dtype)
 
 
+def _ids_arg(plan: MoePlan, topk_ids: torch.Tensor, name="topk_ids") -> int:
+    p = plan.prob
+    if topk_ids.dtype != torch.int32:
+        raise ValueError(f"{name}: dtype {topk_ids.dtype}, expected torch.int32 (e.g. topk ids .int())")
+    if topk_ids.numel() != p.M * p.topk:
+        raise ValueError(f"{name}: {topk_ids.numel()} elements, expected M*topk = {p.M * p.topk}")
+    return _ptr(topk_ids)
+
+
+def _map_arg(plan: MoePlan, expert_map: Optional[torch.Tensor]) -> Optional[int]:
+    return _arg(expert_map, "expert_map", torch.int32, plan.prob.global_experts)
+
+
+def status_words(plan: MoePlan, ws13: torch.Tensor):
+    """(ids outside {-1} U [0,E) seen by the last align, waits of the
+    single-launch variant that timed out, summed over calls) from the status
+    words in ws13.  Synchronises with the device (a copy to the host)."""
+    w = ws_view(ws13, plan.off_status, 2).cpu()
+    return int(w[0]), int(w[1])
+
+
+def check_status(plan: MoePlan, ws13: torch.Tensor):
+    """Raise MoeError when a single-launch call on this ws13 gave up a bounded
+    wait (its outputs are then undefined).  The count stays until ws13 is
+    cleared, so every later check fails too."""
+    _, timeouts = status_words(plan, ws13)
+    if timeouts:
+        raise MoeError("moe_apply_contiguous", MOE_EHIP,
+                       f"{timeouts} bounded waits of the single-launch kernel timed out; outputs undefined")
+
+
 def moe_align_permute(plan: MoePlan, topk_ids: torch.Tensor, ws13: torch.Tensor, stream=None,
                       expert_map: Optional[torch.Tensor] = None):
-    st = load_library().moe_align_permute(ctypes.byref(plan), _ptr(topk_ids), _ptr(expert_map),
-                                          _ptr(ws13), _stream(stream))
+    st = load_library().moe_align_permute(ctypes.byref(plan), _ids_arg(plan, topk_ids),
+                                          _map_arg(plan, expert_map), _ws(ws13, "ws13", plan.ws13_bytes),
+                                          _stream(stream))
     _check("moe_align_permute", st)
 
 
-def _weights(w1, w2, w1_scale=None, w2_scale=None, expert_map=None) -> MoeWeights:
-    return MoeWeights(_ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale), _ptr(expert_map))
+def _weights(plan: MoePlan, w1, w2, w1_scale=None, w2_scale=None, expert_map=None) -> MoeWeights:
+    p = plan.prob
+    mx = p.w_dtype == W_MXFP8
+    wt = torch.uint8 if mx else torch.bfloat16
+    n1, n2 = p.E * 2 * p.I * p.K, p.E * p.K * p.I
+    if mx and (w1_scale is None or w2_scale is None):
+        raise ValueError("MXFP8 weights need w1_scale and w2_scale")
+    return MoeWeights(_arg(w1, "w1", wt, n1), _arg(w1_scale, "w1_scale", torch.uint8, n1 // 32 if mx else 0),
+                      _arg(w2, "w2", wt, n2), _arg(w2_scale, "w2_scale", torch.uint8, n2 // 32 if mx else 0),
+                      _map_arg(plan, expert_map))
 
 
 def moe_apply_contiguous(plan: MoePlan, a, topk_ids, topk_weights, w1, w2, out, ws13, ws2,
                          w1_scale=None, w2_scale=None, stream=None, expert_map=None):
-    w = _weights(w1, w2, w1_scale, w2_scale, expert_map)
+    w = _weights(plan, w1, w2, w1_scale, w2_scale, expert_map)
+    p = plan.prob
     st = load_library().moe_apply_contiguous(
-        ctypes.byref(plan), _ptr(a), _ptr(topk_ids), _ptr(topk_weights), ctypes.byref(w), _ptr(out),
-        _ptr(ws13), _ptr(ws2), _stream(stream))
+        ctypes.byref(plan), _arg(a, "a", torch.bfloat16, p.M * p.K), _ids_arg(plan, topk_ids),
+        _arg(topk_weights, "topk_weights", torch.float32, p.M * p.topk), ctypes.byref(w),
+        _arg(out, "out", torch.bfloat16, p.M * p.K), _ws(ws13, "ws13", plan.ws13_bytes),
+        _ws(ws2, "ws2", plan.ws2_bytes), _stream(stream))
     _check("moe_apply_contiguous", st)
 
 
 def moe_gate_up_act(plan: MoePlan, a, w1, w2, ws13, w1_scale=None, w2_scale=None, stream=None):
-    w = _weights(w1, w2, w1_scale, w2_scale)
-    st = load_library().moe_gate_up_act(ctypes.byref(plan), _ptr(a), ctypes.byref(w), _ptr(ws13),
-                                        _stream(stream))
+    w = _weights(plan, w1, w2, w1_scale, w2_scale)
+    st = load_library().moe_gate_up_act(ctypes.byref(plan), _arg(a, "a", torch.bfloat16, plan.prob.M * plan.prob.K),
+                                        ctypes.byref(w), _ws(ws13, "ws13", plan.ws13_bytes), _stream(stream))
     _check("moe_gate_up_act", st)
 
 
 def moe_down_unpermute(plan: MoePlan, w1, w2, ws13, ws2, w1_scale=None, w2_scale=None, stream=None):
-    w = _weights(w1, w2, w1_scale, w2_scale)
-    st = load_library().moe_down_unpermute(ctypes.byref(plan), ctypes.byref(w), _ptr(ws13),
-                                           _ptr(ws2), _stream(stream))
+    w = _weights(plan, w1, w2, w1_scale, w2_scale)
+    st = load_library().moe_down_unpermute(ctypes.byref(plan), ctypes.byref(w), _ws(ws13, "ws13", plan.ws13_bytes),
+                                           _ws(ws2, "ws2", plan.ws2_bytes), _stream(stream))
     _check("moe_down_unpermute", st)
 
 
 def moe_apply_batched(plan: MoePlan, a, expert_num_tokens, w1, w2, y, ws13, stream=None):
-    w = _weights(w1, w2)
-    st = load_library().moe_apply_batched(ctypes.byref(plan), _ptr(a), _ptr(expert_num_tokens),
-                                          ctypes.byref(w), _ptr(y), _ptr(ws13), _stream(stream))
+    w = _weights(plan, w1, w2)
+    p = plan.prob
+    slab = p.E * p.max_tokens * p.K
+    st = load_library().moe_apply_batched(ctypes.byref(plan), _arg(a, "a", torch.bfloat16, slab),
+                                          _arg(expert_num_tokens, "expert_num_tokens", torch.int32, p.E),
+                                          ctypes.byref(w), _arg(y, "y", torch.bfloat16, slab),
+                                          _ws(ws13, "ws13", plan.ws13_bytes), _stream(stream))
     _check("moe_apply_batched", st)
 
 
 def moe_topk_reduce_contiguous(plan: MoePlan, y, topk_ids, topk_weights, out, stream=None,
                                expert_map: Optional[torch.Tensor] = None):
-    st = load_library().moe_topk_reduce_contiguous(ctypes.byref(plan), _ptr(y), _ptr(topk_ids),
-                                                   _ptr(topk_weights), _ptr(expert_map), _ptr(out),
-                                                   _stream(stream))
+    p = plan.prob
+    st = load_library().moe_topk_reduce_contiguous(ctypes.byref(plan), _arg(y, "y", torch.bfloat16, p.M * p.topk * p.K),
+                                                   _ids_arg(plan, topk_ids),
+                                                   _arg(topk_weights, "topk_weights", torch.float32, p.M * p.topk),
+                                                   _map_arg(plan, expert_map),
+                                                   _arg(out, "out", torch.bfloat16, p.M * p.K), _stream(stream))
     _check("moe_topk_reduce_contiguous", st)
 
 
@@ -248,9 +320,14 @@ def moe_naive_batched_ws_bytes(plan: MoePlan, n_out: int) -> int:
 
 def moe_topk_reduce_naive_batched(plan: MoePlan, y, expert_num_tokens, row_token, row_weight,
                                   n_out: int, out, ws, stream=None):
+    p = plan.prob
+    rows = p.E * p.max_tokens
     st = load_library().moe_topk_reduce_naive_batched(
-        ctypes.byref(plan), _ptr(y), _ptr(expert_num_tokens), _ptr(row_token), _ptr(row_weight),
-        n_out, _ptr(out), _ptr(ws), _stream(stream))
+        ctypes.byref(plan), _arg(y, "y", torch.bfloat16, rows * p.K),
+        _arg(expert_num_tokens, "expert_num_tokens", torch.int32, p.E),
+        _arg(row_token, "row_token", torch.int32, rows), _arg(row_weight, "row_weight", torch.float32, rows),
+        n_out, _arg(out, "out", torch.bfloat16, n_out * p.K),
+        _ws(ws, "ws", moe_naive_batched_ws_bytes(plan, n_out)), _stream(stream))
     _check("moe_topk_reduce_naive_batched", st)
 
 
@@ -259,7 +336,9 @@ def moe_quantize_mxfp8(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tenso
         raise ValueError("x must be float32 or bfloat16")
     rows = x.numel() // x.shape[-1]
     st = load_library().moe_quantize_mxfp8(_ptr(x), 0 if x.dtype == torch.float32 else 1, rows,
-                                           x.shape[-1], _ptr(codes), _ptr(scales), _stream(stream))
+                                           x.shape[-1], _arg(codes, "codes", torch.uint8, x.numel()),
+                                           _arg(scales, "scales", torch.uint8, x.numel() // 32),
+                                           _stream(stream))
     _check("moe_quantize_mxfp8", st)
 
 
@@ -272,16 +351,20 @@ def _grouped(R, N, K, E) -> MoeGroupedProblem:
 def moe_grouped_forward(x, w, group_offsets, y, stream=None):
     """y[r] = W[e] x[r] over the rows of each group (x [R,K], w [E,N,K], y [R,N] bf16)."""
     p = _grouped(x.shape[0], w.shape[1], w.shape[2], w.shape[0])
-    st = load_library().moe_grouped_forward(ctypes.byref(p), _ptr(x), _ptr(w), _ptr(group_offsets),
-                                            _ptr(y), _stream(stream))
+    st = load_library().moe_grouped_forward(ctypes.byref(p), _arg(x, "x", torch.bfloat16, p.R * p.K),
+                                            _arg(w, "w", torch.bfloat16, p.E * p.N * p.K),
+                                            _arg(group_offsets, "group_offsets", torch.int32, p.E + 1),
+                                            _arg(y, "y", torch.bfloat16, p.R * p.N), _stream(stream))
     _check("moe_grouped_forward", st)
 
 
 def moe_grouped_dgrad(dy, w, group_offsets, dx, stream=None):
     """dx[r] = W[e]^T dy[r] (dy [R,N], w [E,N,K], dx [R,K] bf16)."""
     p = _grouped(dy.shape[0], w.shape[1], w.shape[2], w.shape[0])
-    st = load_library().moe_grouped_dgrad(ctypes.byref(p), _ptr(dy), _ptr(w), _ptr(group_offsets),
-                                          _ptr(dx), _stream(stream))
+    st = load_library().moe_grouped_dgrad(ctypes.byref(p), _arg(dy, "dy", torch.bfloat16, p.R * p.N),
+                                          _arg(w, "w", torch.bfloat16, p.E * p.N * p.K),
+                                          _arg(group_offsets, "group_offsets", torch.int32, p.E + 1),
+                                          _arg(dx, "dx", torch.bfloat16, p.R * p.K), _stream(stream))
     _check("moe_grouped_dgrad", st)
 
 
@@ -289,7 +372,10 @@ def moe_grouped_wgrad(dy, x, group_offsets, dw, accumulate: bool = False, stream
     """dW[e] = sum over group e's rows of dy[r] x[r]^T into dw [E,N,K] float32
     (written, or added when ``accumulate``)."""
     p = _grouped(dy.shape[0], dw.shape[1], dw.shape[2], dw.shape[0])
-    st = load_library().moe_grouped_wgrad(ctypes.byref(p), _ptr(dy), _ptr(x), _ptr(group_offsets),
-                                          _ptr(dw), 1 if accumulate else 0, _stream(stream))
+    st = load_library().moe_grouped_wgrad(ctypes.byref(p), _arg(dy, "dy", torch.bfloat16, p.R * p.N),
+                                          _arg(x, "x", torch.bfloat16, p.R * p.K),
+                                          _arg(group_offsets, "group_offsets", torch.int32, p.E + 1),
+                                          _arg(dw, "dw", torch.float32, p.E * p.N * p.K),
+                                          1 if accumulate else 0, _stream(stream))
     _check("moe_grouped_wgrad", st)
 

@@ -213,6 +213,16 @@ int moe_plan_init(moe_plan* plan, const moe_problem* prob) {
   }
   if (plan->max_tiles > 65535 || plan->max_active > 65535)
     return fail(plan, MOE_EUNSUPPORTED, "grid too large");
+  if (contiguous && variant != MOE_VARIANT_TILE) {
+    // the streaming and MXFP8 kernels read z (and for MXFP8 the gathered
+    // activation codes) through one buffer resource with 32-bit offsets,
+    // whose range check stops at 2^31 - 1 bytes: rows past it would read 0
+    const int64_t zbytes = plan->sorted_capacity * P.I * (P.w_dtype == MOE_W_MXFP8 ? 1 : 2);
+    const int64_t xqbytes = P.w_dtype == MOE_W_MXFP8 ? plan->sorted_capacity * P.K : 0;
+    if (zbytes >= (1ll << 31) - 1 || xqbytes >= (1ll << 31) - 1)
+      return fail(plan, MOE_EUNSUPPORTED,
+                  "streaming/MXFP8 kernels address z and the gathered activations with 32-bit offsets");
+  }
 
   AlignLayout L = layout_align(0, P.E, plan->sorted_capacity, plan->max_tiles, plan->max_active,
                                plan->align_blocks);

@@ -175,3 +175,66 @@ def test_grouped_validation(R, N, K, E, acc, misalign, code):
     if acc == 0:
         assert lib.moe_grouped_dgrad(ctypes.byref(p), fake, fake, fake, out, None) == code
         assert lib.moe_grouped_forward(ctypes.byref(p), fake, fake, fake, out, None) == code
+
+
+@pytest.mark.parametrize("kw", [
+    # MXFP8: gathered activation codes sorted_capacity * K = 2.2 GB
+    dict(M=45000, K=6144, I=2048, E=32, topk=8, w_dtype=moe.W_MXFP8, w1_order=moe.W1_INTERLEAVE16),
+    # forced streaming bf16: z = sorted_capacity * I * 2 = 2.15 GB
+    dict(M=65536, K=4096, I=2048, E=64, topk=8, variant=moe.VARIANT_STREAM),
+    # MXFP8 z = sorted_capacity * I bytes past 2^31 with a small K
+    dict(M=40000, K=128, I=8192, E=8, topk=8, w_dtype=moe.W_MXFP8),
+])
+def test_plan_refuses_32bit_offset_overflow(kw):
+    """The streaming and MXFP8 kernels address z and the gathered activation
+    codes through one buffer each with 32-bit offsets: plans whose buffers
+    reach 2^31 bytes are refused instead of reading zeros past that point."""
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_plan_init(moe.make_problem(**kw))
+    assert ei.value.status == moe.MOE_EUNSUPPORTED
+    assert "32-bit" in str(ei.value)
+
+
+def test_plan_accepts_largest_streaming_buffers_below_2g():
+    """Just below the limit the same shapes plan (MXFP8 share, 30000 tokens:
+    sorted_capacity * K = 1.48 GB)."""
+    p = moe.moe_plan_init(moe.make_problem(30000, 6144, 2048, 32, topk=8, w_dtype=moe.W_MXFP8,
+                                           w1_order=moe.W1_INTERLEAVE16))
+    assert p.sorted_capacity * 6144 < (1 << 31) - 1
+
+
+def test_binding_checks_dtypes_and_sizes(monkeypatch):
+    """The wrappers refuse tensors of the wrong dtype or size before any call:
+    int64 ids (torch.topk's dtype) would be read as int32 pairs, a bf16 dw
+    would be written past its end as fp32, a short workspace overrun.  (Host
+    tensors stand in for device ones: the device check is switched off, and
+    every case fails a check before the library is called.)"""
+    import torch
+    monkeypatch.setattr(moe, "_ptr", lambda t: None if t is None else t.data_ptr())
+    cfg = mi.config(0)
+    plan = plan_for(cfg)
+    ids64 = torch.zeros((cfg.M, cfg.topk), dtype=torch.int64)
+    with pytest.raises(ValueError, match="int32"):
+        moe.moe_align_permute(plan, ids64, torch.zeros(plan.ws13_bytes, dtype=torch.uint8))
+    ids = torch.zeros((cfg.M, cfg.topk + 1), dtype=torch.int32)
+    with pytest.raises(ValueError, match="M\\*topk"):
+        moe.moe_align_permute(plan, ids, torch.zeros(plan.ws13_bytes, dtype=torch.uint8))
+    ids = torch.zeros((cfg.M, cfg.topk), dtype=torch.int32)
+    with pytest.raises(ValueError, match="ws13"):
+        moe.moe_align_permute(plan, ids, torch.zeros(plan.ws13_bytes - 1, dtype=torch.uint8))
+    x = torch.zeros((cfg.M, cfg.K), dtype=torch.float32)
+    w1 = torch.zeros((cfg.E, 2 * cfg.I, cfg.K), dtype=torch.bfloat16)
+    w2 = torch.zeros((cfg.E, cfg.K, cfg.I), dtype=torch.bfloat16)
+    out = torch.zeros((cfg.M, cfg.K), dtype=torch.bfloat16)
+    wts = torch.zeros((cfg.M, cfg.topk), dtype=torch.float32)
+    ws13 = torch.zeros(plan.ws13_bytes, dtype=torch.uint8)
+    ws2 = torch.zeros(plan.ws2_bytes, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="a: dtype"):
+        moe.moe_apply_contiguous(plan, x, ids, wts, w1, w2, out, ws13, ws2)
+    with pytest.raises(ValueError, match="w2"):
+        moe.moe_apply_contiguous(plan, x.bfloat16(), ids, wts, w1, w2[:1], out, ws13, ws2)
+    dy = torch.zeros((256, 128), dtype=torch.bfloat16)
+    xx = torch.zeros((256, 128), dtype=torch.bfloat16)
+    off = torch.tensor([0, 256], dtype=torch.int32)
+    with pytest.raises(ValueError, match="dw"):
+        moe.moe_grouped_wgrad(dy, xx, off, torch.zeros((1, 128, 128), dtype=torch.bfloat16))

@@ -224,6 +224,67 @@ def pin_batched():
     assert all(np.array_equal(ys[e][1], ys2[e][1]) for e in ys)
 
 
+def pin_batched_reduce_worked_example():
+    """TopKWeightAndReduceNaiveBatched ("Fused MoE Modular Kernel",
+    TopKWeightAndReduce) by hand: E=2 slabs of 3 rows, K=2, 3 output tokens.
+    Expert 0 has 2 valid rows, expert 1 has 1; the junk rows carry a valid
+    looking token id and a large weight, so reading them changes the result.
+      Y[0,0] = [1, 2]  -> token 1, weight 0.5
+      Y[0,1] = [3, 4]  -> token 0, weight 2
+      Y[0,2] = [5, 5]  (junk: token 2, weight 99)
+      Y[1,0] = [8, -4] -> token 1, weight 0.25
+      Y[1,1], Y[1,2]   (junk: token 0 / 2, weight 7)
+    out[0] = 2*[3,4] = [6, 8]; out[1] = 0.5*[1,2] + 0.25*[8,-4] = [2.5, 0];
+    out[2] = [+0, +0] (no valid row maps to token 2)."""
+    Y = np.array([[[1, 2], [3, 4], [5, 5]], [[8, -4], [9, 9], [6, 6]]], np.float64)
+    counts = np.array([2, 1], np.int32)
+    tok = np.array([[1, 0, 2], [1, 0, 2]], np.int32)
+    wt = np.array([[0.5, 2.0, 99.0], [0.25, 7.0, 7.0]], np.float32)
+    out = oracle.naive_batched_reduce(lambda e, r: Y[e, r], counts, tok, wt, 3, 2)
+    assert np.array_equal(out, np.array([[6, 8], [2.5, 0], [0, 0]], np.float64))
+    assert not np.any(np.signbit(out))
+    part = oracle.naive_batched_reduce(lambda e, r: Y[e, r], counts, tok, wt, 3, 2, tokens=np.array([1]))
+    assert np.array_equal(part, np.array([[2.5, 0]]))
+
+
+def pin_batched_equals_contiguous():
+    """The two activation formats ("Fused MoE Modular Kernel", introduction)
+    differ only in how routes are laid out: dispatching a contiguous problem
+    into per-expert slabs (row r of expert e = a copy of its token's x, the
+    map holding the token and its top-k weight) and running the batched
+    format's rows + naive-batched reduce gives the contiguous result.  Slots
+    with id -1 are not dispatched; a token may hit one expert twice."""
+    rng = np.random.default_rng(29)
+    M, K, I, E, topk = 9, 16, 8, 4, 3
+    x = rng.standard_normal((M, K))
+    w1 = rng.standard_normal((E, 2 * I, K)) / 4
+    w2 = rng.standard_normal((E, K, I)) / 4
+    ids = rng.integers(0, E, (M, topk)).astype(np.int32)
+    ids[2, 1] = -1
+    ids[4] = -1                                   # token 4: no valid slot
+    ids[6] = [3, 3, 1]                            # expert 3 twice
+    wts = rng.random((M, topk)).astype(np.float32)
+    ref = oracle.moe_contiguous(x, np.arange(M), ids, wts, E, lambda e: w1[e], lambda e: w2[e])
+    T = M * topk
+    a = np.full((E, T, K), np.nan)                # rows past the counts stay NaN: never read
+    tok = np.full((E, T), -1, np.int32)
+    wt = np.zeros((E, T), np.float32)
+    counts = np.zeros(E, np.int32)
+    for t in range(M):
+        for j in range(topk):
+            e = ids[t, j]
+            if e < 0:
+                continue
+            r = counts[e]
+            a[e, r], tok[e, r], wt[e, r] = x[t], t, wts[t, j]
+            counts[e] += 1
+    ys = oracle.moe_batched_rows(lambda e, r: a[e][r], counts, lambda e: w1[e], lambda e: w2[e])
+    pos = {e: {int(r): i for i, r in enumerate(ys[e][0])} for e in ys}
+    out = oracle.naive_batched_reduce(lambda e, r: ys[e][1][pos[e][r]], counts, tok, wt, M, K)
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-13)
+    assert np.all(out[4] == 0) and not np.any(np.signbit(out[4]))
+
+
 def pin_mxfp8_weights_layer():
     # A layer whose weights went through the codec stays within the format's
     # relative error of the unquantised layer (sanity of the dequantised path).
@@ -281,7 +342,8 @@ def pin_expert_map_worked_example():
 
 PINS = [pin_silu_library, pin_closed_form_selection, pin_dense_swiglu_library,
         pin_dense_mixing_bruteforce, pin_equivariance, pin_nullity_linearity, pin_reduce_contiguous,
-        pin_interleave_layout, pin_batched, pin_mxfp8_weights_layer, pin_expert_map_partition,
+        pin_interleave_layout, pin_batched, pin_batched_reduce_worked_example,
+        pin_batched_equals_contiguous, pin_mxfp8_weights_layer, pin_expert_map_partition,
         pin_expert_map_worked_example]
 
 

@@ -20,6 +20,7 @@ _orig = {n: getattr(oracle, n) for n in ("split_gate_up", "silu", "expert_ffn", 
                                          "mx_scale_exponent", "e4m3fn_encode",
                                          "topk_reduce_contiguous", "moe_contiguous",
                                          "map_expert_ids", "grouped_forward", "grouped_dgrad",
+                                         "naive_batched_reduce", "moe_batched_rows",
                                          "grouped_wgrad", "grouped_wgrad_accumulate")}
 
 
@@ -143,6 +144,39 @@ def m_accumulate_ignores_out(out, dy, x, off):
     return _orig["grouped_wgrad"](dy, x, off)
 
 
+def m_batched_reduce_ignores_counts(y_of, counts, row_token, row_weight, n_out, K, tokens=None):
+    full = np.full_like(np.asarray(counts), row_token.shape[1])
+    return _orig["naive_batched_reduce"](y_of, full, row_token, row_weight, n_out, K, tokens)
+
+
+def m_batched_reduce_transposed_map(y_of, counts, row_token, row_weight, n_out, K, tokens=None):
+    tokens = np.arange(n_out) if tokens is None else np.asarray(tokens)
+    pos = {int(t): i for i, t in enumerate(tokens)}
+    out = np.zeros((len(tokens), K))
+    for e in range(len(counts)):
+        for r in range(int(counts[e])):
+            t = int(row_token[r, e])                 # indices swapped
+            if t in pos:
+                out[pos[t]] += float(row_weight[e, r]) * y_of(e, r)
+    return out
+
+
+def m_batched_reduce_unweighted(y_of, counts, row_token, row_weight, n_out, K, tokens=None):
+    return _orig["naive_batched_reduce"](y_of, counts, row_token, np.ones_like(row_weight), n_out, K, tokens)
+
+
+def m_batched_rows_one_past(a_rows_of, counts, w1_of, w2_of, order="halves", rows_of=None):
+    cap = lambda e: range(int(counts[e]) + 1)
+    return _orig["moe_batched_rows"](a_rows_of, np.asarray(counts) + 1, w1_of, w2_of, order,
+                                     rows_of or cap)
+
+
+def m_batched_rows_wrong_expert(a_rows_of, counts, w1_of, w2_of, order="halves", rows_of=None):
+    n = len(counts)
+    return _orig["moe_batched_rows"](a_rows_of, counts, lambda e: w1_of((e + 1) % n),
+                                     lambda e: w2_of((e + 1) % n), order, rows_of)
+
+
 MUTATIONS = [
     ("grouped_forward", m_forward_w_layout), ("grouped_dgrad", m_dgrad_wrong_expert),
     ("grouped_dgrad", m_dgrad_w_layout), ("grouped_wgrad", m_wgrad_drops_last_row),
@@ -154,6 +188,10 @@ MUTATIONS = [
     ("topk_reduce_contiguous", m_reduce_reads_skipped), ("moe_contiguous", m_moe_ignores_weights),
     ("map_expert_ids", m_map_ignored), ("map_expert_ids", m_map_remote_invalid),
     ("map_expert_ids", m_map_out_of_range_kept),
+    ("naive_batched_reduce", m_batched_reduce_ignores_counts),
+    ("naive_batched_reduce", m_batched_reduce_transposed_map),
+    ("naive_batched_reduce", m_batched_reduce_unweighted),
+    ("moe_batched_rows", m_batched_rows_one_past), ("moe_batched_rows", m_batched_rows_wrong_expert),
 ]
 
 
