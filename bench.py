@@ -275,7 +275,7 @@ def main():
                                               wsr, stream)
             ev[2].record(stream)
 
-    elapsed, stage_ms, step_ev, cold_ev = time_steps(step, stages, args, dev)
+    elapsed, stage_ms, step_ev, cold_ev, aa_ev = time_steps(step, stages, args, dev)
     ms_per_step = elapsed * 1e3 / args.steps
     tokens = cfg.M
     value = tokens * args.steps / elapsed
@@ -286,9 +286,13 @@ def main():
     if cfg.w_dtype == "mxfp8":
         wbytes = 1.0 + 1.0 / 32
         dtype_name = "bf16 activations, MXFP8 weights"
+        # both GEMMs multiply E4M3 codes with UE8M0 block scales (activations
+        # and z quantised on the device), fp32 accumulate
+        dtype = "mxfp8"
     else:
         wbytes = 2.0
         dtype_name = "bf16"
+        dtype = "bf16"
     if contiguous and "apply" in stage_ms:
         # the whole layer in one stage: both weight sets, x rows read once,
         # out written once (intermediates are the implementation's overhead)
@@ -332,8 +336,12 @@ def main():
     rec = {
         "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
         "data": "synthetic (seeded counter-based generator; random-init expert weights)",
+        "value_basis": "wall clock over the K steps, issued back to back (L2 and Infinity Cache as "
+                       "the previous step left them); value_cache_flushed: tokens / p50 of K steps "
+                       "each after a 512 MiB cache flush",
+        "value_cache_flushed": round(tokens / (float(np.percentile(cold_ev, 50)) * 1e-3), 2),
         "config": {"workload": cfg.name, "M": cfg.M, "K": K, "I": I, "E": cfg.E, "topk": cfg.topk,
                    "max_tokens": cfg.max_tokens, "weights": dtype_name, "routes": n_routes,
                    "active_experts": n_act, "variant": plan.reason.decode(),
@@ -341,12 +349,40 @@ def main():
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "step_event_ms": pct(step_ev),
         "step_event_ms_cache_flushed": pct(cold_ev),
+        "noise": noise(step_ev, aa_ev),
         "step_weight_GBps": round(step_gbs, 1),
         "step_TFLOPs": round(6.0 * n_routes * K * I / (ms_per_step * 1e-3) / 1e12, 3),
         "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def noise(step_ev, aa_ev):
+    """Noise floor of the per-step event times: the 95% confidence interval
+    of the mean step (normal approximation over the K steps) and an A/A
+    rerun of the same K steps right after, as the measurement method of the
+    deterministic grouped GEMM page does (A/A noise as the smallest
+    detectable effect, 95% CI)."""
+    import numpy as np
+    a = np.asarray(step_ev, dtype=np.float64)
+    b = np.asarray(aa_ev, dtype=np.float64)
+    half = 1.96 * a.std(ddof=1) / np.sqrt(a.size) if a.size > 1 else 0.0
+    return {"mean_ms": round(float(a.mean()), 4),
+            "ci95_ms": [round(float(a.mean() - half), 4), round(float(a.mean() + half), 4)],
+            "aa_mean_ms": round(float(b.mean()), 4),
+            "aa_diff_pct": round(float(100.0 * (b.mean() - a.mean()) / a.mean()), 3)}
 
 
 def pct(v):
@@ -357,10 +393,11 @@ def pct(v):
 def time_steps(step, stages, args, dev):
     """W untimed steps, then exactly K timed ones between two synchronisations
     (wall clock), with HIP events between the stages on the launch stream;
-    then K more, each after a 512 MiB fill that flushes L2 and the Infinity
-    Cache (outside each step's events and outside the wall-clock steps).
-    Returns (seconds for the K steps, mean ms per stage, per-step event ms,
-    per-step event ms of the flushed steps)."""
+    then K more the same way (the A/A rerun); then K more, each after a
+    512 MiB fill that flushes L2 and the Infinity Cache (outside each step's
+    events and outside the wall-clock steps).  Returns (seconds for the K
+    steps, mean ms per stage, per-step event ms, per-step event ms of the
+    flushed steps, per-step event ms of the rerun)."""
     import numpy as np
     import torch
     nev = len(stages) + 1
@@ -378,6 +415,11 @@ def time_steps(step, stages, args, dev):
     stage_ms = {s: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in events]))
                 for i, s in enumerate(stages)}
     step_ev = [ev[0].elapsed_time(ev[-1]) for ev in events]
+    aa = [mk() for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(aa[k])
+    torch.cuda.synchronize()
+    aa_ev = [ev[0].elapsed_time(ev[-1]) for ev in aa]
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     cold = [mk() for _ in range(args.steps)]
     for k in range(args.steps):
@@ -386,7 +428,7 @@ def time_steps(step, stages, args, dev):
     torch.cuda.synchronize()
     cold_ev = [ev[0].elapsed_time(ev[-1]) for ev in cold]
     del flush
-    return elapsed, stage_ms, step_ev, cold_ev
+    return elapsed, stage_ms, step_ev, cold_ev, aa_ev
 
 
 TRAIN_METRIC = "training grouped GEMM rows/s (forward + dgrad + fp32 wgrad accumulate); TFLOP/s vs MFMA peak"
@@ -424,7 +466,7 @@ def main_train(args):
         moe.moe_grouped_wgrad(ti.dy, ti.x, off, main_grad, accumulate=True, stream=stream)
         ev[3].record(stream)
 
-    elapsed, stage_ms, step_ev, cold_ev = time_steps(step, stages, args, dev)
+    elapsed, stage_ms, step_ev, cold_ev, aa_ev = time_steps(step, stages, args, dev)
     ms_per_step = elapsed * 1e3 / args.steps
     flops = 2.0 * R * cfg.N * cfg.K           # per GEMM
     tf = {s: round(flops / (stage_ms[s] * 1e-3) / 1e12, 1) for s in stages}
@@ -456,6 +498,7 @@ def main_train(args):
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "stage_TFLOPs": tf,
         "step_event_ms": pct(step_ev), "step_event_ms_cache_flushed": pct(cold_ev),
+        "noise": noise(step_ev, aa_ev),
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
@@ -491,7 +534,7 @@ def cpu_baseline_train(cfg, ti, min_seconds):
     dt = time.perf_counter() - t0
     return {"value": round((b - a) * reps / dt, 4), "unit": "rows/s", "cores": int(blas_threads),
             "kind": "oracle", "sample": f"group {e} ({b - a} rows, N={cfg.N}, K={cfg.K}), {reps} passes",
-            "seconds": round(dt, 2), "host_cpus": os.cpu_count()}
+            "seconds": round(dt, 2), "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 def cpu_baseline(cfg, inp, w1, w2, w_f32, sample, min_seconds):
@@ -517,8 +560,12 @@ def cpu_baseline(cfg, inp, w1, w2, w_f32, sample, min_seconds):
         experts = sorted({int(e) for e in ids[tokens][valid[tokens]]})
         # stage host copies of the inputs (not timed): raw bf16 bits or float32
         if w_f32 is not None:
-            host = {e: (w_f32[0][e].cpu().numpy(), w_f32[1][e].cpu().numpy()) for e in experts}
-            dec = lambda a: oracle.mxfp8_dequantize(*oracle.mxfp8_quantize(a))
+            # the oracle's own codec encodes the float32 weights once, before
+            # the timed loop (the GPU path too gets its weights encoded); the
+            # timed oracle decodes them, as it decodes bf16 weights
+            host = {e: (oracle.mxfp8_quantize(w_f32[0][e].cpu().numpy()),
+                        oracle.mxfp8_quantize(w_f32[1][e].cpu().numpy())) for e in experts}
+            dec = lambda cs: oracle.mxfp8_dequantize(*cs)
         else:
             host = {e: (mi.bf16_bits(inp.w1[e]), mi.bf16_bits(inp.w2[e])) for e in experts}
             dec = oracle.bf16_to_f64
@@ -556,7 +603,7 @@ def cpu_baseline(cfg, inp, w1, w2, w_f32, sample, min_seconds):
         units = rows * cfg.M / max(1, int(counts.sum()))
     return {"value": round(units / dt, 4), "unit": "tokens/s", "cores": int(blas_threads),
             "kind": "oracle", "sample": what, "seconds": round(dt, 2),
-            "host_cpus": os.cpu_count()}
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 if __name__ == "__main__":

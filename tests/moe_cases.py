@@ -82,13 +82,27 @@ def make_case(cfg: mi.MoEConfig, device="cuda") -> DeviceCase:
     return c
 
 
+def poison_workspaces(plan, ws13: torch.Tensor, ws2: torch.Tensor):
+    """Fill z (in ws13) and the per-(token, slot) rows y (ws2) with 0xFF bytes
+    (bf16 NaN, E4M3 NaN): a row the kernels should have written but did not
+    then turns the output it feeds into NaN instead of a stale zero."""
+    end = plan.off_xq if plan.off_xq > 0 else plan.ws13_bytes
+    if plan.off_sync > 0:
+        end = min(end, plan.off_sync)
+    ws13[plan.off_z:end].fill_(0xFF)
+    ws2.fill_(0xFF)
+
+
 def run_contiguous(c: DeviceCase, variant=moe.VARIANT_AUTO, ids=None, wts=None, x=None,
-                   expert_map: Optional[np.ndarray] = None):
+                   expert_map: Optional[np.ndarray] = None, poison: bool = False):
     """One moe_apply_contiguous call; with ``expert_map`` (host int32 [G]) the
-    ids are global and the plan's global_experts is G."""
+    ids are global and the plan's global_experts is G.  ``poison``: the
+    intermediate buffers start as NaN patterns (see poison_workspaces)."""
     G = 0 if expert_map is None else len(expert_map)
     plan = moe.moe_plan_init(problem(c.cfg, variant, global_experts=G))
     ws13, ws2 = moe.allocate_workspaces(plan)
+    if poison:
+        poison_workspaces(plan, ws13, ws2)
     out = torch.empty((c.cfg.M, c.cfg.K), dtype=torch.bfloat16, device="cuda")
     emap = None if expert_map is None else torch.from_numpy(np.asarray(expert_map, np.int32)).cuda()
     moe.moe_apply_contiguous(plan, c.inp.x if x is None else x, c.ids if ids is None else ids,
@@ -157,6 +171,43 @@ def check_close(gpu: torch.Tensor, ref: np.ndarray, rel: float, abs_: float, wha
     i = np.unravel_index(np.argmax(err), err.shape)
     say(f"[parity] {what}: max|err| {err.max():.3e} bound {bound:.3e} max|ref| {np.abs(ref).max():.3e}")
     assert err.max() <= bound, f"{what}: max err {err.max()} at {i} > {bound} (gpu {g[i]}, ref {ref[i]})"
+
+
+def tokens_covering_experts(ids: np.ndarray, E: int, experts=None, per_expert: int = 2) -> np.ndarray:
+    """Tokens that together reach every listed expert (default: all E): for
+    each expert its first and last routed token in flat order (and, with
+    per_expert > 2, evenly spaced ones between), so each expert's run is
+    checked at its start and its end."""
+    flat_tok = np.repeat(np.arange(ids.shape[0]), ids.shape[1])
+    flat = ids.reshape(-1)
+    pick = set()
+    for e in (range(E) if experts is None else experts):
+        toks = flat_tok[flat == e]
+        if toks.size == 0:
+            continue
+        idx = np.unique(np.linspace(0, toks.size - 1, per_expert).round().astype(int))
+        pick.update(int(t) for t in toks[idx])
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+def heavy_tail_rows(x: torch.Tensor, seed: int, every: int = 3):
+    """Put large values into the activations, in place: in every ``every``-th
+    row, one element of each 32-column block becomes +-(4 .. 8) (4 to 8 sigma
+    of the N(0,1) rows; the seeded generator's own values stay within 3.46
+    sigma), and one block of row 0 holds a single 64.  The block maximum then
+    sets the MXFP8 scale, so the other elements of the block lose precision
+    the way normal tails make them."""
+    M, K = x.shape
+    rng = np.random.default_rng(seed)
+    rows = np.arange(0, M, every)
+    nb = K // 32
+    col = (np.arange(nb)[None, :] * 32 + rng.integers(0, 32, (rows.size, nb))).reshape(-1)
+    row = np.repeat(rows, nb)
+    val = rng.uniform(4.0, 8.0, row.size) * np.where(rng.random(row.size) < 0.5, -1.0, 1.0)
+    xr = torch.from_numpy(row).to(x.device)
+    xc = torch.from_numpy(col).to(x.device)
+    x[xr, xc] = torch.from_numpy(val).to(x.device, torch.float32).to(x.dtype)
+    x[0, 5] = 64.0
 
 
 def sample_tokens(M: int, n: int, seed: int = 0) -> np.ndarray:
