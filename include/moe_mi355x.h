@@ -250,6 +250,30 @@ int moe_apply_contiguous(const moe_plan* plan, const void* a, const int32_t* top
                          const float* topk_weights, const moe_weights* w, void* out,
                          void* ws13, void* ws2, void* stream);
 
+/* Bytes of the library's own workspace array used by
+ * moe_apply_contiguous_static (one per GPU). */
+#define MOE_STATIC_SCRATCH_BYTES (64ll << 20)
+
+/* moe_apply_contiguous for callers that cannot allocate: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, kernels and results (bit for bit) as moe_apply_contiguous, but
+ * ws13 and ws2 live in an array inside the library: MOE_STATIC_SCRATCH_BYTES
+ * of device memory per GPU, held from the library's load until the process
+ * ends.  The call allocates and frees nothing.  Limit: the plan's ws13
+ * (rounded up to 256 bytes) plus ws2 must fit in MOE_STATIC_SCRATCH_BYTES,
+ * else MOE_EUNSUPPORTED and nothing is enqueued (e.g. the decode batch
+ * M=4 K=4096 I=8192 E=64 top-8 needs about 8.7 MB; a prefill batch of 8192
+ * tokens does not fit).  Every call on one GPU uses that GPU's one array:
+ * calls that overlap in time on one GPU (two streams, two host threads)
+ * race and give undefined results; calls ordered on one stream are safe.
+ * The status words of ws13 (invalid ids, time-outs) are cleared at the start
+ * of each call and are not visible to the caller.  Errors as for
+ * moe_apply_contiguous, plus MOE_EHIP when the array's device address
+ * cannot be obtained. */
+int moe_apply_contiguous_static(const moe_plan* plan, const void* a, const int32_t* topk_ids,
+                                const float* topk_weights, const moe_weights* w, void* out,
+                                void* stream);
+
 /* The two matmul stages of moe_apply_contiguous on their own, for callers
  * that time or overlap them (contiguous plans; moe_align_permute must have
  * filled ws13 first, on the same stream).

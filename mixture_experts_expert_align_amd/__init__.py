@@ -19,6 +19,7 @@ __all__ = [
     "W1_INTERLEAVE16", "VARIANT_AUTO", "VARIANT_TILE", "VARIANT_STREAM", "VARIANT_FUSED", "REDUCE_NOOP",
     "REDUCE_CONTIGUOUS", "REDUCE_NAIVE_BATCHED", "MoeError", "MoeProblem", "MoePlan", "MoeWeights",
     "load_library", "library_path", "moe_abi_version", "moe_status_string", "moe_plan_init",
+    "moe_apply_contiguous_static", "STATIC_SCRATCH_BYTES",
     "moe_plan_reason", "moe_align_permute", "moe_apply_contiguous", "moe_apply_batched",
     "moe_gate_up_act", "moe_down_unpermute",
     "moe_topk_reduce_contiguous", "moe_naive_batched_ws_bytes", "moe_topk_reduce_naive_batched",
@@ -28,6 +29,7 @@ __all__ = [
 ]
 
 ABI_VERSION = 4
+STATIC_SCRATCH_BYTES = 64 << 20     # MOE_STATIC_SCRATCH_BYTES
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, 1, 2, 3
 LAYOUT_CONTIGUOUS, LAYOUT_BATCHED = 0, 1
 W_BF16, W_MXFP8 = 0, 1
@@ -98,6 +100,7 @@ def load_library() -> ctypes.CDLL:
         "moe_plan_reason": (ctypes.c_char_p, [_vp]),
         "moe_align_permute": (_i32, [_vp] * 5),
         "moe_apply_contiguous": (_i32, [_vp] * 9),
+        "moe_apply_contiguous_static": (_i32, [_vp] * 7),
         "moe_apply_batched": (_i32, [_vp] * 7),
         "moe_gate_up_act": (_i32, [_vp] * 5),
         "moe_down_unpermute": (_i32, [_vp] * 5),
@@ -273,6 +276,21 @@ def moe_apply_contiguous(plan: MoePlan, a, topk_ids, topk_weights, w1, w2, out, 
         _arg(out, "out", torch.bfloat16, p.M * p.K), _ws(ws13, "ws13", plan.ws13_bytes),
         _ws(ws2, "ws2", plan.ws2_bytes), _stream(stream))
     _check("moe_apply_contiguous", st)
+
+
+def moe_apply_contiguous_static(plan: MoePlan, a, topk_ids, topk_weights, w1, w2, out, w1_scale=None,
+                                w2_scale=None, stream=None, expert_map=None):
+    """moe_apply_contiguous with the workspaces inside the library's own
+    per-GPU array (no allocation by anyone; calls that overlap on one GPU
+    race).  Raises MoeError(MOE_EUNSUPPORTED) when the plan's workspaces do
+    not fit in STATIC_SCRATCH_BYTES."""
+    w = _weights(plan, w1, w2, w1_scale, w2_scale, expert_map)
+    p = plan.prob
+    st = load_library().moe_apply_contiguous_static(
+        ctypes.byref(plan), _arg(a, "a", torch.bfloat16, p.M * p.K), _ids_arg(plan, topk_ids),
+        _arg(topk_weights, "topk_weights", torch.float32, p.M * p.topk), ctypes.byref(w),
+        _arg(out, "out", torch.bfloat16, p.M * p.K), _stream(stream))
+    _check("moe_apply_contiguous_static", st)
 
 
 def moe_gate_up_act(plan: MoePlan, a, w1, w2, ws13, w1_scale=None, w2_scale=None, stream=None):

@@ -176,6 +176,9 @@ hipError_t launch_reduce_csr(const uint16_t* y, const float* w, const int32_t* o
                              const int32_t* rows, uint16_t* out, int64_t n_out, int64_t K,
                              hipStream_t s);
 
+// p[i * stride] = 0 for i < n (a fill kernel, capturable in a graph).
+hipError_t launch_zero_words(int32_t* p, int64_t n, int64_t stride, hipStream_t s);
+
 // ---------------------------------------------------------------- codec ----
 hipError_t launch_quantize_mxfp8(const void* x, int x_dtype, int64_t rows, int64_t cols,
                                  uint8_t* codes, uint8_t* scales, hipStream_t s);

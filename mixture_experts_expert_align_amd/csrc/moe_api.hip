@@ -1,8 +1,11 @@
 // The C ABI declared in include/moe_mi355x.h: validation, planning,
-// workspace layout and the launch sequences.  Host code only; it enqueues
+// workspace layout and the launch sequences.  Host code, plus the one device
+// array that moe_apply_contiguous_static uses as its workspace; it enqueues
 // kernels on the caller's stream and never allocates or synchronises.
 #include <stdio.h>
 #include <string.h>
+
+#include <mutex>
 
 #include "../../include/moe_mi355x.h"
 #include "kernels.h"
@@ -74,6 +77,33 @@ AlignArgs align_args(const moe_plan* p, const int32_t* keys, const int32_t* expe
   return a;
 }
 
+}  // namespace
+
+// ------------------------------------------------ the allocation-free call ----
+// The workspaces of moe_apply_contiguous_static: one array per GPU, held from
+// the library's load until the process ends.  Host code never uses the
+// array's name as an address (in host code it names a host-side stand-in);
+// it takes the device address hipGetSymbolAddress returns for the current
+// device, once per device.
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device, or nullptr.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
 }  // namespace
 
 extern "C" {
@@ -391,15 +421,11 @@ int moe_down_unpermute(const moe_plan* plan, const moe_weights* w, void* ws13, v
   return down_unpermute(plan, w, ws13, ws2, (hipStream_t)stream);
 }
 
-int moe_apply_contiguous(const moe_plan* plan, const void* a, const int32_t* topk_ids,
-                         const float* topk_weights, const moe_weights* w, void* out, void* ws13,
-                         void* ws2, void* stream) {
-  if (!contiguous_args_ok(plan, w) || !map_ok(plan, w->expert_map)) return MOE_EINVAL;
+// The launches of moe_apply_contiguous (arguments already validated).
+static int apply_contiguous(const moe_plan* plan, const void* a, const int32_t* topk_ids,
+                            const float* topk_weights, const moe_weights* w, void* out, void* ws13,
+                            void* ws2, hipStream_t s) {
   const moe_problem& P = plan->prob;
-  if (!aligned16(a) || !aligned4(topk_ids) || !aligned4(topk_weights) || !aligned16(out) ||
-      !aligned16(ws13) || !aligned16(ws2))
-    return MOE_EINVAL;
-  hipStream_t s = (hipStream_t)stream;
   AlignArgs al = align_args(plan, topk_ids, w->expert_map, ws13);
   if (plan->variant == MOE_VARIANT_FUSED) {
     FusedArgs f{};
@@ -427,6 +453,45 @@ int moe_apply_contiguous(const moe_plan* plan, const void* a, const int32_t* top
                                           fused ? at<int32_t>(ws13, plan->off_sync) : nullptr,
                                           fused ? sync_counter_lines(plan->max_active) : 0, s);
   return e == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+static bool apply_args_ok(const moe_plan* plan, const void* a, const int32_t* topk_ids,
+                          const float* topk_weights, const moe_weights* w, const void* out) {
+  return contiguous_args_ok(plan, w) && map_ok(plan, w->expert_map) && aligned16(a) &&
+         aligned4(topk_ids) && aligned4(topk_weights) && aligned16(out);
+}
+
+int moe_apply_contiguous(const moe_plan* plan, const void* a, const int32_t* topk_ids,
+                         const float* topk_weights, const moe_weights* w, void* out, void* ws13,
+                         void* ws2, void* stream) {
+  if (!apply_args_ok(plan, a, topk_ids, topk_weights, w, out) || !aligned16(ws13) || !aligned16(ws2))
+    return MOE_EINVAL;
+  return apply_contiguous(plan, a, topk_ids, topk_weights, w, out, ws13, ws2, (hipStream_t)stream);
+}
+
+int moe_apply_contiguous_static(const moe_plan* plan, const void* a, const int32_t* topk_ids,
+                                const float* topk_weights, const moe_weights* w, void* out,
+                                void* stream) {
+  if (!apply_args_ok(plan, a, topk_ids, topk_weights, w, out)) return MOE_EINVAL;
+  const int64_t ws2_off = up(plan->ws13_bytes, kAlign);
+  if (plan->ws13_bytes <= 0 || ws2_off + plan->ws2_bytes > (int64_t)MOE_STATIC_SCRATCH_BYTES)
+    return MOE_EUNSUPPORTED;
+  uint8_t* base = static_cast<uint8_t*>(scratch_on_current_device());
+  if (!base) return MOE_EHIP;
+  hipStream_t s = (hipStream_t)stream;
+  void* ws13 = base;
+  void* ws2 = base + ws2_off;
+  // The array keeps whatever the previous call (of any plan) left in it.
+  // Every buffer the kernels read is written earlier in the same call,
+  // except the single-launch variant's work-queue counters and the status
+  // words it counts into: clear those first, with a kernel rather than a
+  // memset node, so the call stays capturable.
+  if (launch_zero_words(at<int32_t>(ws13, plan->off_status), 4, 1, s) != hipSuccess) return MOE_EHIP;
+  if (plan->variant == MOE_VARIANT_FUSED &&
+      launch_zero_words(at<int32_t>(ws13, plan->off_sync), sync_counter_lines(plan->max_active), kSyncLine,
+                        s) != hipSuccess)
+    return MOE_EHIP;
+  return apply_contiguous(plan, a, topk_ids, topk_weights, w, out, ws13, ws2, s);
 }
 
 int moe_apply_batched(const moe_plan* plan, const void* a, const int32_t* expert_num_tokens,

@@ -221,6 +221,14 @@ __global__ void __launch_bounds__(NT) quantize_gather_kernel(
   quantize_block(v, codes + p * K + b * 32, scales + p * nb + b);
 }
 
+// p[i * stride] = 0 for i < n: clears counters where a caller cannot rely on
+// the previous call having left them zero (and where hipMemsetAsync would
+// put a memset node into a captured graph).
+__global__ void __launch_bounds__(NT) zero_words_kernel(int32_t* __restrict__ p, int64_t n, int64_t stride) {
+  const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;
+  if (i < n) p[i * stride] = 0;
+}
+
 inline unsigned nblocks(int64_t n) { return (unsigned)((n + NT - 1) / NT); }
 
 // Chunks per thread of the reduces: as many (up to kChunks) as keep about
@@ -252,6 +260,12 @@ hipError_t launch_reduce_csr(const uint16_t* y, const float* w, const int32_t* o
   const int cpt = reduce_cpt(n_out, K / 8);
   const dim3 grid((unsigned)n_out, (unsigned)((K / 8 + NT * cpt - 1) / (NT * cpt)));
   hipLaunchKernelGGL(reduce_csr_kernel, grid, dim3(NT), 0, s, y, w, offsets, rows, out, n_out, K, cpt);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_words(int32_t* p, int64_t n, int64_t stride, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_words_kernel, dim3(nblocks(n)), dim3(NT), 0, s, p, n, stride);
   return hipGetLastError();
 }
 
