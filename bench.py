@@ -254,7 +254,7 @@ def main():
             ev[2].record(stream)
             moe.moe_down_unpermute(plan, w1, w2, ws13, ws2, w1_scale, w2_scale, stream)
             ev[3].record(stream)
-            moe.moe_topk_reduce_contiguous(plan, ws2, ids, wts, out, stream, expert_map=emap)
+            moe.moe_topk_reduce_contiguous(plan, ws2.view(torch.bfloat16), ids, wts, out, stream, expert_map=emap)
             ev[4].record(stream)
     else:
         counts = torch.from_numpy(inp.expert_num_tokens).to(dev)
