@@ -151,7 +151,7 @@ COPY_LAUNCHES = 3
 FUSED_KERNELS = ["fused_stream_bf16_kernel", "reduce_contiguous_kernel"]
 FUSED_FILES = ["fused.hip", "stream_bf16.h", "align_device.h", "reduce_codec.hip"]
 DOMINANT_KERNEL = {"tiny": FUSED_KERNELS, "decode": ["gemm_stream_bf16_kernel<0,"],
-                   "prefill": ["gemm_tile_bf16_kernel<0,"],
+                   "prefill": ["gemm_tile_split_bf16_kernel<0,"],
                    "mxfp8": ["quantize_gather_kernel", "gemm_stream_mxfp8_kernel<0,"],
                    "batched": ["gemm_tile_bf16_kernel<0,", "gemm_tile_bf16_kernel<1,"],
                    "decode_fused": FUSED_KERNELS, "tiny_fused": FUSED_KERNELS,

@@ -40,6 +40,8 @@
 //    order: workgroups in flight read different weight tiles of one expert
 //    while sharing its route tile, and when the weight-tile count is a
 //    multiple of 8 the route tiles of one weight tile land on the same XCD.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -201,6 +203,72 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const TileCoord
   }
 }
 
+// Per-lane byte offsets of the slice loads.  Block b of a slot (b = wave +
+// NW * i) holds rows RPB*b .. RPB*b + RPB-1 of its region; lane l lands on
+// row RPB*b + l/CH, physical chunk l%CH, which holds logical chunk
+// (l%CH) ^ x(row).  W1 tiles hold BN/2 gate rows then the BN/2 matching up
+// rows; route rows are gathered through the route list (token = flat slot /
+// topk) for W1, read in position order for W2, or taken from the expert's
+// slab for the batched format; a padding route (or a batched row past its
+// expert's count) gets an offset past the buffer, which loads zeros.
+template <int EPI, int BM, int BN, int BK, int NW>
+__device__ __forceinline__ void load_offsets(const GemmArgs& g, const TileCoord& tc, int wave, int lane,
+                                             uint32_t (&ow)[BN / (512 / BK) / NW],
+                                             uint32_t (&ox)[BM / (512 / BK) / NW]) {
+  constexpr int CH = BK / 8;
+  constexpr int RPB = 64 / CH;
+  constexpr int RPW = 256 / (BK * 2) > 0 ? 256 / (BK * 2) : 1;
+  constexpr int LW = BN / RPB / NW;
+  constexpr int LX = BM / RPB / NW;
+  const RowMap& rm = g.rows;
+  const int K = g.kdim;
+#pragma unroll
+  for (int i = 0; i < LW; ++i) {
+    const int n = (wave + NW * i) * RPB + lane / CH;
+    const int c = (lane % CH) ^ ((n / RPW) & (CH - 1));
+    int wrow;
+    if (EPI == kEpiGateUp) {
+      const int f = tc.col0 / 2 + (n % (BN / 2));
+      wrow = w1_row(f, n >= BN / 2, g.I, g.w1_order);
+    } else {
+      wrow = tc.col0 + n;
+    }
+    ow[i] = (uint32_t)((wrow * K + c * 8) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < LX; ++i) {
+    const int m = (wave + NW * i) * RPB + lane / CH;
+    const int c = (lane % CH) ^ ((m / RPW) & (CH - 1));
+    int64_t row = -1;
+    if (rm.layout != 0) {
+      if (m < tc.nvalid) row = tc.row0 + m;   // rows past the expert's count are never read
+    } else if (EPI == kEpiGateUp) {
+      const int sid = rm.sorted_ids[tc.row0 + m];
+      if (sid != rm.sentinel) row = sid / rm.topk;
+    } else {
+      row = tc.row0 + m;
+    }
+    ox[i] = row >= 0 ? (uint32_t)((row * g.act_ld + c * 8) * 2) : 0x80000000u;
+  }
+}
+
+// LDS rows of a wave's fragments: weight row of tile i (W1: gate tiles, then
+// the matching up tiles) and the first route row of its route tiles.
+template <int EPI, int BM, int BN, int WN, int WM>
+__device__ __forceinline__ void frag_rows(int wn, int wm, int lane, int (&wrow_l)[BN / WN / 32], int& xrow_l) {
+  constexpr int TW = BN / WN / 32;
+#pragma unroll
+  for (int i = 0; i < TW; ++i) {
+    if (EPI == kEpiGateUp) {
+      constexpr int FW = BN / 2 / WN;
+      wrow_l[i] = (i < TW / 2 ? 0 : BN / 2) + wn * FW + 32 * (i % (TW / 2)) + (lane & 31);
+    } else {
+      wrow_l[i] = wn * (BN / WN) + 32 * i + (lane & 31);
+    }
+  }
+  xrow_l = wm * (BM / WM) + (lane & 31);
+}
+
 template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, int NS, int ORDER>
 __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmArgs g, int ncol,
                                                                           int64_t nlog) {
@@ -231,39 +299,8 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmA
   const uint16_t* wexp = static_cast<const uint16_t*>(g.w) + (int64_t)tc.expert * g.w_expert_stride;
   const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(wexp, g.w_expert_stride * 2);
   const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(g.act, g.act_bytes);
-  // block b of a slot (b = wave + NW * i) holds rows RPB*b .. RPB*b + RPB-1 of
-  // its region; lane l lands on row RPB*b + l/CH, physical chunk l%CH, which
-  // holds logical chunk (l%CH) ^ x(row)
   uint32_t ow[LW], ox[LX];
-#pragma unroll
-  for (int i = 0; i < LW; ++i) {
-    const int n = (wave + NW * i) * RPB + lane / CH;
-    const int c = (lane % CH) ^ ((n / RPW) & (CH - 1));
-    int wrow;
-    if (EPI == kEpiGateUp) {
-      const int f = tc.col0 / 2 + (n % (BN / 2));
-      const bool up = n >= BN / 2;
-      wrow = g.w1_order == 0 ? (up ? g.I + f : f) : (32 * (f >> 4) + (f & 15) + (up ? 16 : 0));
-    } else {
-      wrow = tc.col0 + n;
-    }
-    ow[i] = (uint32_t)((wrow * K + c * 8) * 2);
-  }
-#pragma unroll
-  for (int i = 0; i < LX; ++i) {
-    const int m = (wave + NW * i) * RPB + lane / CH;
-    const int c = (lane % CH) ^ ((m / RPW) & (CH - 1));
-    int64_t row = -1;
-    if (rm.layout != 0) {
-      if (m < tc.nvalid) row = tc.row0 + m;   // rows past the expert's count are never read
-    } else if (EPI == kEpiGateUp) {
-      const int sid = rm.sorted_ids[tc.row0 + m];
-      if (sid != rm.sentinel) row = sid / rm.topk;
-    } else {
-      row = tc.row0 + m;
-    }
-    ox[i] = row >= 0 ? (uint32_t)((row * g.act_ld + c * 8) * 2) : 0x80000000u;
-  }
+  load_offsets<EPI, BM, BN, BK, NW>(g, tc, wave, lane, ow, ox);
 
   const int nk = K / BK;
   // A route block whose rows are all padding is not loaded: its LDS rows keep
@@ -289,17 +326,8 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmA
     issue_order();
   };
 
-  int wrow_l[TW];
-#pragma unroll
-  for (int i = 0; i < TW; ++i) {
-    if (EPI == kEpiGateUp) {
-      constexpr int FW = BN / 2 / WN;
-      wrow_l[i] = (i < TW / 2 ? 0 : BN / 2) + wn * FW + 32 * (i % (TW / 2)) + (lane & 31);
-    } else {
-      wrow_l[i] = wn * (BN / WN) + 32 * i + (lane & 31);
-    }
-  }
-  const int xrow_l = wm * (BM / WM) + (lane & 31);
+  int wrow_l[TW], xrow_l;
+  frag_rows<EPI, BM, BN, WN, WM>(wn, wm, lane, wrow_l, xrow_l);
   // a wave whose route rows all lie past the tile's valid rows holds only
   // padding: it skips its fragment reads and MFMAs (its accumulators stay 0,
   // what zero-filled padding rows would give) but still issues its share of
@@ -369,6 +397,178 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmA
   tile_epilogue<EPI, BM, BN, WN, WM, 64 * WN * WM>(g, tc, acc, wn, wm, lane, smem);
 }
 
+
+// The contiguous format's tiles (prefill: 256 routes x 256 weight rows,
+// K = 4096 for W1): the same tile and wave grid as above, with the ring
+// split by operand and the slice hand-off moved into the last k step.
+//  * Weights are requested two slices ahead (3 slots), routes one ahead
+//    (2 slots): 3 x 32 KB + 2 x 32 KB = 160 KB, all of the LDS.  Weight rows
+//    come from HBM (each weight tile serves only the few route tiles of its
+//    expert) and have the longer way; route rows mostly hit L2.
+//  * Slice kt's last k step begins with the wait for slice kt+1 and the
+//    barrier; right after it the freed slots are refilled (routes of slice
+//    kt+2, weights of slice kt+3) and the first fragments of slice kt+1 are
+//    read while the MFMAs of that last step run, so the MFMA pipe has work
+//    across the barrier instead of waiting for the first reads of a slice.
+//  * Fragment reads and MFMAs of a step are interleaved one to one
+//    (scheduling groups), so the next step's reads overlap this step's
+//    MFMAs instead of being issued after them into the same registers.
+//  * Waits count only weight loads as younger than the loads they wait for:
+//    a wave skips its route blocks made only of padding, so its route loads
+//    per slice are not a fixed number.
+//  * A wave whose route rows are all padding runs the same loop without
+//    fragment reads and MFMAs (its own copy of the loop, so the live copy
+//    has no branches around its MFMAs).
+template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC>
+__global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_split_bf16_kernel(GemmArgs g, int ncol,
+                                                                                int64_t nlog) {
+  constexpr int NW = WN * WM;
+  constexpr int CH = BK / 8;
+  constexpr int RPB = 64 / CH;
+  constexpr int LW = BN / RPB / NW;          // weight loads per wave per slice
+  constexpr int LX = BM / RPB / NW;          // route loads per wave per slice
+  static_assert(LW * NW * RPB == BN && LX * NW * RPB == BM, "blocks / waves mismatch");
+  static_assert(2 * LW < 64, "wait counts");
+  constexpr int WS = 3, RS = 2;              // weight / route slots
+  constexpr int WSLOT = BN * BK, RSLOT = BM * BK;
+  constexpr int TW = BN / WN / 32;
+  constexpr int TX = BM / WM / 32;
+  constexpr int NSTEP = BK / 16;
+  static_assert(EPI != kEpiGateUp || TW % 2 == 0, "gate/up pairs need an even tile count");
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[WS * WSLOT + RS * RSLOT];
+  uint16_t* const wbase = smem;
+  uint16_t* const rbase = smem + WS * WSLOT;
+
+  TileCoord tc;
+  if (!tile_coord<BM, BN, kWeightMajor>(g, ncol, nlog, tc)) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave / WM;
+  const int wm = wave % WM;
+  const uint16_t* wexp = static_cast<const uint16_t*>(g.w) + (int64_t)tc.expert * g.w_expert_stride;
+  const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(wexp, g.w_expert_stride * 2);
+  const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(g.act, g.act_bytes);
+  uint32_t ow[LW], ox[LX];
+  load_offsets<EPI, BM, BN, BK, NW>(g, tc, wave, lane, ow, ox);
+  const int nk = g.kdim / BK;
+  // route blocks made only of padding are not loaded (see the ring kernel)
+  bool xload[LX];
+#pragma unroll
+  for (int i = 0; i < LX; ++i)
+    xload[i] = __builtin_amdgcn_readfirstlane((int)((wave + NW * i) * RPB < tc.nvalid)) != 0;
+  auto issue_w = [&](int kt) {
+    uint16_t* slot = wbase + (kt % WS) * WSLOT;
+#pragma unroll
+    for (int i = 0; i < LW; ++i) lds_load16(wr, slot + (wave + NW * i) * RPB * BK, ow[i], kt * BK * 2);
+    issue_order();
+  };
+  auto issue_r = [&](int kt) {
+    uint16_t* slot = rbase + (kt & 1) * RSLOT;
+#pragma unroll
+    for (int i = 0; i < LX; ++i)
+      if (xload[i]) lds_load16(ar, slot + (wave + NW * i) * RPB * BK, ox[i], kt * BK * 2);
+    issue_order();
+  };
+  int wrow_l[TW], xrow_l;
+  frag_rows<EPI, BM, BN, WN, WM>(wn, wm, lane, wrow_l, xrow_l);
+  f32x16 acc[TW][TX];
+#pragma unroll
+  for (int i = 0; i < TW; ++i)
+#pragma unroll
+    for (int j = 0; j < TX; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  bf16x8 fw[2][TW], fx[2][TX];
+  // fragments of k step s of slice kt into buffer fb
+  auto fload = [&](int fb, int kt, int s) {
+    const uint16_t* ws = wbase + (kt % WS) * WSLOT;
+    const uint16_t* rs = rbase + (kt & 1) * RSLOT;
+    const int c = 2 * s + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < TW; ++i)
+      fw[fb][i] = as_bf16x8(*reinterpret_cast<const i32x4*>(&ws[lds_off<BK>(wrow_l[i], c)]));
+#pragma unroll
+    for (int j = 0; j < TX; ++j)
+      fx[fb][j] = as_bf16x8(*reinterpret_cast<const i32x4*>(&rs[lds_off<BK>(xrow_l + 32 * j, c)]));
+  };
+  auto mma = [&](int fb) {
+#pragma unroll
+    for (int i = 0; i < TW; ++i)
+#pragma unroll
+      for (int j = 0; j < TX; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[fb][i], fx[fb][j], acc[i][j], 0, 0, 0);
+  };
+  // one fragment read, one MFMA, and so on; the MFMAs past the reads last
+  auto interleave = [&]() {
+#pragma unroll
+    for (int q = 0; q < TW + TX; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    }
+    if (TW * TX > TW + TX) __builtin_amdgcn_sched_group_barrier(0x008, TW * TX - TW - TX, 0);
+  };
+
+  // prologue: weights 0, routes 0 and 1, weights 1 and 2; wait for slice 0
+  issue_w(0);
+  issue_r(0);
+  if (nk > 1) { issue_r(1); issue_w(1); }
+  if (nk > 2) issue_w(2);
+  if (nk > 2) wait_vm<2 * LW>();
+  else if (nk > 1) wait_vm<LW>();
+  else wait_vm<0>();
+  lds_barrier();
+
+  // Slice kt.  MODE 2: slices kt+2 and kt+3 exist (routes of kt+2 and
+  // weights of kt+3 are requested); 1: only kt+2; 0: only kt+1; -1: kt is
+  // the last slice.  LIVE: the wave computes.
+  auto slice = [&](int kt, auto mode, auto live) {
+    constexpr int MODE = decltype(mode)::value;
+    constexpr bool LIVE = decltype(live)::value;
+    if (LIVE) {
+#pragma unroll
+      for (int s = 0; s + 1 < NSTEP; ++s) {
+        fload((s + 1) & 1, kt, s + 1);
+        mma(s & 1);
+        interleave();
+      }
+    }
+    if (MODE >= 0) {
+      // slice kt+1 has landed once only the weights of slice kt+2 (issued
+      // after its routes) may still be in flight
+      if (MODE >= 1) wait_vm<LW>();
+      else wait_vm<0>();
+      lds_barrier();   // every wave's slice kt+1 is in; nobody reads slice kt's slots any more
+      if (MODE >= 1) issue_r(kt + 2);
+      if (MODE >= 2) issue_w(kt + 3);
+      if (LIVE) {
+        fload(0, kt + 1, 0);
+        mma((NSTEP - 1) & 1);
+        interleave();
+      }
+    } else if (LIVE) {
+      mma((NSTEP - 1) & 1);
+    }
+  };
+  auto run = [&](auto live) {
+    if (decltype(live)::value) fload(0, 0, 0);
+    int kt = 0;
+    for (; kt + 3 < nk; ++kt) slice(kt, std::integral_constant<int, 2>(), live);
+    if (kt + 2 < nk) slice(kt++, std::integral_constant<int, 1>(), live);
+    if (kt + 1 < nk) slice(kt++, std::integral_constant<int, 0>(), live);
+    slice(kt, std::integral_constant<int, -1>(), live);
+  };
+  // a wave whose route rows all lie past the tile's valid rows holds only
+  // padding: it loads and meets the barriers but computes nothing (its
+  // accumulators stay 0, what zero-filled padding rows would give)
+  if (wm * (BM / WM) < tc.nvalid) run(std::true_type());
+  else run(std::false_type());
+
+  wait_vm<0>();
+  lds_barrier();
+  static_assert(BM * (EPI == kEpiGateUp ? BN / 2 : BN) <= WS * WSLOT + RS * RSLOT, "epilogue tile fits the LDS");
+  tile_epilogue<EPI, BM, BN, WN, WM, 64 * WN * WM>(g, tc, acc, wn, wm, lane, smem);
+}
+
 template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, int NS, int ORDER>
 hipError_t launch(const GemmArgs& g, hipStream_t s) {
   const int ncol = EPI == kEpiGateUp ? g.nfeat / (BN / 2) : g.nfeat / BN;
@@ -386,12 +586,23 @@ hipError_t launch(const GemmArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC>
+hipError_t launch_split(const GemmArgs& g, hipStream_t s) {
+  if (BM != kTileRoutesContiguous || g.rows.layout != 0) return hipErrorInvalidValue;
+  const int ncol = EPI == kEpiGateUp ? g.nfeat / (BN / 2) : g.nfeat / BN;
+  const int64_t nlog = g.max_tiles * ncol;
+  hipLaunchKernelGGL((gemm_tile_split_bf16_kernel<EPI, BM, BN, BK, WN, WM, OCC>), dim3((unsigned)padded_blocks(nlog)),
+                     dim3(64 * WN * WM), 0, s, g, ncol, nlog);
+  return hipGetLastError();
+}
+
 template <int EPI>
 hipError_t launch_layout(const GemmArgs& g, hipStream_t s) {
-  // contiguous: 256 routes x 256 weight rows, 16 waves of 64x64 (128 KB of
-  // LDS, one workgroup per CU); batched: 128 x 128, 4 waves of 64x64 (64 KB,
-  // two per CU), route-major; both with 64-wide slices in a 2-slot ring
-  if (g.rows.layout == 0) return launch<EPI, 256, 256, 64, 4, 4, 4, 2, kWeightMajor>(g, s);
+  // contiguous: 256 routes x 256 weight rows, 16 waves of 64x64, the split
+  // ring (160 KB of LDS, one workgroup per CU); batched: 128 x 128, 4 waves
+  // of 64x64, 64-wide slices in a 2-slot ring (64 KB, two per CU),
+  // route-major
+  if (g.rows.layout == 0) return launch_split<EPI, 256, 256, 64, 4, 4, 4>(g, s);
   return launch<EPI, 128, 128, 64, 2, 2, 2, 2, kRouteMajor>(g, s);
 }
 
