@@ -152,13 +152,16 @@ FUSED_KERNELS = ["fused_stream_bf16_kernel", "reduce_contiguous_kernel"]
 FUSED_FILES = ["fused.hip", "stream_bf16.h", "align_device.h", "reduce_codec.hip"]
 DOMINANT_KERNEL = {"tiny": FUSED_KERNELS, "decode": ["gemm_stream_bf16_kernel<0,"],
                    "prefill": ["gemm_tile_split_bf16_kernel<0,"],
-                   "mxfp8": ["quantize_gather_kernel", "gemm_stream_mxfp8_kernel<0,"],
+                   "mxfp8": ["quantize_gather_kernel", "gemm_tile_mxfp8_kernel<0"],
+                   "mxfp8_stream": ["quantize_gather_kernel", "gemm_stream_mxfp8_kernel<0,"],
                    "batched": ["gemm_tile_bf16_kernel<0,", "gemm_tile_bf16_kernel<1,"],
                    "decode_fused": FUSED_KERNELS, "tiny_fused": FUSED_KERNELS,
                    "train_gu": ["train_wgrad_kernel"], "train_dn": ["train_wgrad_kernel"]}
 KERNEL_FILES = {"tiny": FUSED_FILES, "decode": ["gemm_stream.hip", "stream_bf16.h"],
-                "prefill": ["gemm_tile.hip"], "mxfp8": ["reduce_codec.hip", "gemm_mxfp8.hip"],
-                "batched": ["gemm_tile.hip"], "decode_fused": FUSED_FILES, "tiny_fused": FUSED_FILES,
+                "prefill": ["gemm_tile.hip", "tile_common.h"],
+                "mxfp8": ["reduce_codec.hip", "gemm_mxfp8_tile.hip", "tile_common.h"],
+                "mxfp8_stream": ["reduce_codec.hip", "gemm_mxfp8.hip"],
+                "batched": ["gemm_tile.hip", "tile_common.h"], "decode_fused": FUSED_FILES, "tiny_fused": FUSED_FILES,
                 "train_gu": ["train.hip"], "train_dn": ["train.hip"]}
 
 

@@ -4,19 +4,15 @@
 //
 // A workgroup computes BN weight rows x BM route rows of one expert, stepping
 // through the contraction in BK-wide slices.  The slices reach LDS by buffer
-// loads that write LDS themselves (no registers, no LDS store instructions)
-// into a ring of NS slice buffers: slice kt+NS-1 is requested as the
-// multiplication of slice kt starts, so every load has NS-1 slices of MFMA
-// work to land, and each slice costs one wait and one barrier.  In LDS the
-// 16-byte chunks of a row are XOR-swizzled so the 32-row fragment reads of an
-// MFMA hit distinct banks; one such load writes the 64 lanes' 16 bytes to
-// 1 KB of LDS at a wave-uniform address, lane i at byte 16 i, so each lane
-// fetches the chunk that the swizzle places at its position.  The waves form
-// a WN x WM grid; each owns (BN/WN) weight rows x (BM/WM) routes as tiles of
-// v_mfma_f32_32x32x16_bf16 with the weight rows in the MFMA row operand, so a
-// lane's accumulators hold 4 consecutive output features of one route and
-// the epilogue writes 8-byte runs.  Inside a slice the fragments of the next
-// 16-wide k step are read from LDS while the MFMAs of the current one run.
+// loads that write LDS themselves (no registers, no LDS store instructions).
+// In LDS the 16-byte chunks of a row are XOR-swizzled so the 32-row fragment
+// reads of an MFMA hit distinct banks; one such load writes the 64 lanes' 16
+// bytes to 1 KB of LDS at a wave-uniform address, lane i at byte 16 i, so
+// each lane fetches the chunk that the swizzle places at its position.  The
+// waves form a WN x WM grid; each owns (BN/WN) weight rows x (BM/WM) routes
+// as tiles of v_mfma_f32_32x32x16_bf16 with the weight rows in the MFMA row
+// operand, so a lane's accumulators hold 4 consecutive output features of
+// one route and the epilogue writes 8-byte runs.
 //
 // W1 (kGateUp): the BN weight rows are BN/2 gate rows and the BN/2 matching up
 // rows; each wave holds gate and up values of the same (feature, route) in
@@ -44,94 +40,10 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "tile_common.h"
 
 namespace moe {
 namespace tile {
-
-constexpr int NXCD = 8;
-constexpr int kXcdChunk = 32;
-enum Order { kWeightMajor = 0, kRouteMajor = 1 };
-
-template <int BK>
-__device__ __forceinline__ int lds_off(int row, int c) {
-  constexpr int CH = BK / 8;  // 16-byte chunks per row
-  // chunk c of row r lives at chunk c ^ f(r); f spreads 8 consecutive rows
-  // over the 128-byte bank period for the reads of 8 lanes
-  constexpr int RPW = 256 / (BK * 2) > 0 ? 256 / (BK * 2) : 1;   // rows per 256-byte bank window
-  const int x = (row / RPW) & (CH - 1);
-  return row * BK + ((c ^ x) << 3);
-}
-
-// Workgroup -> (expert, first weight row, first route row).
-struct TileCoord {
-  int expert, col0;
-  int64_t row0;   // contiguous: sorted position; batched: slab row e*max_tokens + r0
-  int nvalid;     // route rows of the tile that exist (the rest are padding)
-};
-
-__host__ __device__ inline int64_t padded_blocks(int64_t nlog) {
-  const int64_t unit = (int64_t)NXCD * kXcdChunk;
-  return (nlog + unit - 1) / unit * unit;
-}
-
-template <int BM, int BN, int ORDER>
-__device__ __forceinline__ bool tile_coord(const GemmArgs& g, int ncol, int64_t nlog, TileCoord& tc) {
-  const RowMap& rm = g.rows;
-  // block b runs on XCD b % 8 as that XCD's (b / 8)-th block
-  const int64_t b = blockIdx.x;
-  const int64_t k = b / NXCD;
-  int64_t L = b;
-  if (rm.layout == 0) {
-    const int64_t total = (int64_t)rm.num_post[0] / BM * ncol;
-    if (ORDER == kWeightMajor) {
-      // full rounds of 8 chunks; the tiles left after them are split evenly
-      // over the 8 XCDs so that none idles through the last round
-      const int64_t full = total / (NXCD * kXcdChunk);
-      const int64_t x = b % NXCD;
-      if (k < full * kXcdChunk) {
-        L = ((k / kXcdChunk) * NXCD + x) * kXcdChunk + (k % kXcdChunk);
-      } else {
-        const int64_t c2 = (total - full * NXCD * kXcdChunk + NXCD - 1) / NXCD;
-        const int64_t kk = k - full * kXcdChunk;
-        if (kk >= c2) return false;
-        L = full * NXCD * kXcdChunk + x * c2 + kk;
-      }
-    }
-    if (L >= total) return false;
-    // expert e owns logical tiles [offsets[e]/BM*ncol, offsets[e+1]/BM*ncol)
-    int lo = 0, hi = g.E - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if ((int64_t)rm.offsets[mid] / BM * ncol <= L) lo = mid; else hi = mid - 1;
-    }
-    const int64_t t0 = rm.offsets[lo] / BM;
-    const int64_t ne = rm.offsets[lo + 1] / BM - t0;
-    const int64_t local = L - t0 * ncol;
-    tc.expert = lo;
-    if (ORDER == kRouteMajor) {
-      tc.col0 = (int)(local % ncol) * BN;
-      tc.row0 = (t0 + local / ncol) * BM;
-    } else {
-      tc.col0 = (int)(local / ne) * BN;
-      tc.row0 = (t0 + local % ne) * BM;
-    }
-    // the expert's run holds counts[lo] routes, then padding to a tile
-    tc.nvalid = (int)max<int64_t>(0, min<int64_t>(BM, rm.counts[lo] - (tc.row0 - rm.offsets[lo])));
-    return true;
-  }
-  if (L >= nlog) return false;
-  const int tpe = (rm.max_tokens + BM - 1) / BM;
-  const int e = (int)(L / ((int64_t)ncol * tpe));
-  const int local = (int)(L - (int64_t)e * ncol * tpe);
-  const int r0 = (ORDER == kRouteMajor ? local / ncol : local % tpe) * BM;
-  const int cnt = min(rm.counts[e], rm.max_tokens);
-  if (r0 >= cnt) return false;
-  tc.expert = e;
-  tc.col0 = (ORDER == kRouteMajor ? local % ncol : local / tpe) * BN;
-  tc.row0 = (int64_t)e * rm.max_tokens + r0;
-  tc.nvalid = min(BM, cnt - r0);
-  return true;
-}
 
 // Epilogue.  acc[i][j][r]: weight row (tile i) 8*(r/4) + 4*(lane/32) + r%4,
 // route wm*(BM/WM) + 32*j + lane%32; registers 4h..4h+3 are 4 consecutive
@@ -269,140 +181,12 @@ __device__ __forceinline__ void frag_rows(int wn, int wm, int lane, int (&wrow_l
   xrow_l = wm * (BM / WM) + (lane & 31);
 }
 
-template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, int NS, int ORDER>
-__global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmArgs g, int ncol,
-                                                                          int64_t nlog) {
-  constexpr int NW = WN * WM;
-  constexpr int CH = BK / 8;                 // 16-byte chunks per row
-  constexpr int RPB = 64 / CH;               // rows per 1 KB block (one load instruction)
-  constexpr int RPW = 256 / (BK * 2) > 0 ? 256 / (BK * 2) : 1;   // as in lds_off
-  constexpr int LW = BN / RPB / NW;          // weight blocks per wave per slice
-  constexpr int LX = BM / RPB / NW;          // route blocks per wave per slice
-  static_assert(LW * NW * RPB == BN && LX * NW * RPB == BM, "blocks / waves mismatch");
-  constexpr int LPW = LW + LX;               // loads per wave per slice
-  static_assert((NS - 2) * LPW < 64 && NS >= 2, "ring depth");
-  constexpr int STAGE = (BN + BM) * BK;      // elements per ring slot: weight rows, then routes
-  constexpr int TW = BN / WN / 32;
-  constexpr int TX = BM / WM / 32;
-  static_assert(EPI != kEpiGateUp || TW % 2 == 0, "gate/up pairs need an even tile count");
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * STAGE];
-
-  TileCoord tc;
-  if (!tile_coord<BM, BN, ORDER>(g, ncol, nlog, tc)) return;
-  const RowMap& rm = g.rows;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wn = wave / WM;
-  const int wm = wave % WM;
-  const int K = g.kdim;
-
-  const uint16_t* wexp = static_cast<const uint16_t*>(g.w) + (int64_t)tc.expert * g.w_expert_stride;
-  const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(wexp, g.w_expert_stride * 2);
-  const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(g.act, g.act_bytes);
-  uint32_t ow[LW], ox[LX];
-  load_offsets<EPI, BM, BN, BK, NW>(g, tc, wave, lane, ow, ox);
-
-  const int nk = K / BK;
-  // A route block whose rows are all padding is not loaded: its LDS rows keep
-  // stale values, which reach only those rows' own outputs (an MFMA output
-  // column depends on its route row alone), and the epilogue drops them or
-  // writes zeros in their place.  Only with a 2-slot ring, whose waits are
-  // for every outstanding load: deeper rings count a fixed LPW loads per
-  // slice in their waits.
-  bool xload[LX];
-#pragma unroll
-  for (int i = 0; i < LX; ++i)
-    xload[i] = NS > 2 || __builtin_amdgcn_readfirstlane((int)((wave + NW * i) * RPB < tc.nvalid)) != 0;
-  // request slice kt into slot st
-  auto issue = [&](int kt, int st) {
-    const int kb = kt * BK * 2;
-    uint16_t* slot = smem + st * STAGE;
-#pragma unroll
-    for (int i = 0; i < LW; ++i)
-      lds_load16(wr, slot + (wave + NW * i) * RPB * BK, ow[i], kb);
-#pragma unroll
-    for (int i = 0; i < LX; ++i)
-      if (xload[i]) lds_load16(ar, slot + BN * BK + (wave + NW * i) * RPB * BK, ox[i], kb);
-    issue_order();
-  };
-
-  int wrow_l[TW], xrow_l;
-  frag_rows<EPI, BM, BN, WN, WM>(wn, wm, lane, wrow_l, xrow_l);
-  // a wave whose route rows all lie past the tile's valid rows holds only
-  // padding: it skips its fragment reads and MFMAs (its accumulators stay 0,
-  // what zero-filled padding rows would give) but still issues its share of
-  // the loads and meets the barriers; a wave-uniform branch
-  const bool wlive = wm * (BM / WM) < tc.nvalid;
-
-  f32x16 acc[TW][TX];
-#pragma unroll
-  for (int i = 0; i < TW; ++i)
-#pragma unroll
-    for (int j = 0; j < TX; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  bf16x8 fw[2][TW], fx[2][TX];
-  auto fload = [&](int fb, const uint16_t* slot, int s) {
-    const int c = 2 * s + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < TW; ++i)
-      fw[fb][i] = as_bf16x8(*reinterpret_cast<const i32x4*>(&slot[lds_off<BK>(wrow_l[i], c)]));
-#pragma unroll
-    for (int j = 0; j < TX; ++j)
-      fx[fb][j] = as_bf16x8(*reinterpret_cast<const i32x4*>(&slot[BN * BK + lds_off<BK>(xrow_l + 32 * j, c)]));
-  };
-  auto compute = [&](int st) {
-    if (!wlive) return;
-    const uint16_t* slot = smem + st * STAGE;
-    fload(0, slot, 0);
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      if (s + 1 < BK / 16) fload((s + 1) & 1, slot, s + 1);
-#pragma unroll
-      for (int i = 0; i < TW; ++i)
-#pragma unroll
-        for (int j = 0; j < TX; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[s & 1][i], fx[s & 1][j], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  // slices 0 .. NS-2 in flight; wait for slice 0
-#pragma unroll
-  for (int p = 0; p < NS - 1; ++p)
-    if (p < nk) issue(p, p);
-  if (nk >= NS - 1) wait_vm<(NS - 2) * LPW>();
-  else wait_vm<0>();
-  lds_barrier();
-  int st = 0;   // slot of slice kt
-  for (int kt = 0; kt < nk; ++kt) {
-    // slot (kt + NS - 1) % NS was read in iteration kt - 1, before the barrier
-    // that ended it.  Past the last slice nothing is requested (a reload
-    // would only add its latency to the tile's end), and the waits that
-    // counted on those loads wait for everything instead.
-    const bool more = kt + NS - 1 < nk;
-    if (more) issue(kt + NS - 1, st == 0 ? NS - 1 : st - 1);
-    compute(st);
-    // slice kt+1 has landed once at most the NS-2 younger slices' loads remain
-    if (more) wait_vm<(NS - 2) * LPW>();
-    else wait_vm<0>();
-    lds_barrier();
-    st = st + 1 == NS ? 0 : st + 1;
-  }
-  // every wave's loads have landed and every wave is done with the ring
-  // before the epilogue reuses it (and before the workgroup leaves its LDS)
-  wait_vm<0>();
-  lds_barrier();
-  static_assert(BM * (EPI == kEpiGateUp ? BN / 2 : BN) <= NS * STAGE, "epilogue tile fits the ring");
-  tile_epilogue<EPI, BM, BN, WN, WM, 64 * WN * WM>(g, tc, acc, wn, wm, lane, smem);
-}
-
-
-// The contiguous format's tiles (prefill: 256 routes x 256 weight rows,
-// K = 4096 for W1): the same tile and wave grid as above, with the ring
-// split by operand and the slice hand-off moved into the last k step.
+// The kernel.  Its ring of slice buffers is split by operand and the slice
+// hand-off sits in the last k step (prefill: 256 routes x 256 weight rows,
+// K = 4096 for W1; batched: 128 x 128):
 //  * Weights are requested two slices ahead (3 slots), routes one ahead
-//    (2 slots): 3 x 32 KB + 2 x 32 KB = 160 KB, all of the LDS.  Weight rows
+//    (2 slots): for 256 x 256 tiles 3 x 32 KB + 2 x 32 KB = 160 KB, all of
+//    the LDS; for 128 x 128 tiles 80 KB, two workgroups per CU.  Weight rows
 //    come from HBM (each weight tile serves only the few route tiles of its
 //    expert) and have the longer way; route rows mostly hit L2.
 //  * Slice kt's last k step begins with the wait for slice kt+1 and the
@@ -419,7 +203,7 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_bf16_kernel(GemmA
 //  * A wave whose route rows are all padding runs the same loop without
 //    fragment reads and MFMAs (its own copy of the loop, so the live copy
 //    has no branches around its MFMAs).
-template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC>
+template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, int ORDER>
 __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_split_bf16_kernel(GemmArgs g, int ncol,
                                                                                 int64_t nlog) {
   constexpr int NW = WN * WM;
@@ -440,7 +224,7 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_split_bf16_kernel
   uint16_t* const rbase = smem + WS * WSLOT;
 
   TileCoord tc;
-  if (!tile_coord<BM, BN, kWeightMajor>(g, ncol, nlog, tc)) return;
+  if (!tile_coord<BM, BN, ORDER>(g, ncol, nlog, tc)) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave / WM;
@@ -451,7 +235,10 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_split_bf16_kernel
   uint32_t ow[LW], ox[LX];
   load_offsets<EPI, BM, BN, BK, NW>(g, tc, wave, lane, ow, ox);
   const int nk = g.kdim / BK;
-  // route blocks made only of padding are not loaded (see the ring kernel)
+  // A route block whose rows are all padding is not loaded: its LDS rows keep
+  // stale values, which reach only those rows' own outputs (an MFMA output
+  // column depends on its route row alone), and the epilogue drops them or
+  // writes zeros in their place.
   bool xload[LX];
 #pragma unroll
   for (int i = 0; i < LX; ++i)
@@ -569,41 +356,30 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_split_bf16_kernel
   tile_epilogue<EPI, BM, BN, WN, WM, 64 * WN * WM>(g, tc, acc, wn, wm, lane, smem);
 }
 
-template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, int NS, int ORDER>
-hipError_t launch(const GemmArgs& g, hipStream_t s) {
+template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, int ORDER>
+hipError_t launch_split(const GemmArgs& g, hipStream_t s) {
   const int ncol = EPI == kEpiGateUp ? g.nfeat / (BN / 2) : g.nfeat / BN;
-  int64_t nrow;
+  int64_t nlog;
   if (g.rows.layout == 0) {
     if (BM != kTileRoutesContiguous) return hipErrorInvalidValue;   // a tile is one plan tile of routes
-    nrow = g.max_tiles;
+    nlog = g.max_tiles * ncol;
   } else {
-    nrow = (int64_t)g.E * ((g.rows.max_tokens + BM - 1) / BM);
+    nlog = (int64_t)g.E * ((g.rows.max_tokens + BM - 1) / BM) * ncol;
   }
-  const int64_t nlog = nrow * ncol;
-  dim3 grid((unsigned)(ORDER == kRouteMajor ? nlog : padded_blocks(nlog)));
-  hipLaunchKernelGGL((gemm_tile_bf16_kernel<EPI, BM, BN, BK, WN, WM, OCC, NS, ORDER>), grid, dim3(64 * WN * WM),
-                     0, s, g, ncol, nlog);
-  return hipGetLastError();
-}
-
-template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC>
-hipError_t launch_split(const GemmArgs& g, hipStream_t s) {
-  if (BM != kTileRoutesContiguous || g.rows.layout != 0) return hipErrorInvalidValue;
-  const int ncol = EPI == kEpiGateUp ? g.nfeat / (BN / 2) : g.nfeat / BN;
-  const int64_t nlog = g.max_tiles * ncol;
-  hipLaunchKernelGGL((gemm_tile_split_bf16_kernel<EPI, BM, BN, BK, WN, WM, OCC>), dim3((unsigned)padded_blocks(nlog)),
+  const int64_t grid = ORDER == kRouteMajor ? nlog : padded_blocks(nlog);
+  hipLaunchKernelGGL((gemm_tile_split_bf16_kernel<EPI, BM, BN, BK, WN, WM, OCC, ORDER>), dim3((unsigned)grid),
                      dim3(64 * WN * WM), 0, s, g, ncol, nlog);
   return hipGetLastError();
 }
 
 template <int EPI>
 hipError_t launch_layout(const GemmArgs& g, hipStream_t s) {
-  // contiguous: 256 routes x 256 weight rows, 16 waves of 64x64, the split
-  // ring (160 KB of LDS, one workgroup per CU); batched: 128 x 128, 4 waves
-  // of 64x64, 64-wide slices in a 2-slot ring (64 KB, two per CU),
+  // both formats on the split ring: contiguous 256 routes x 256 weight rows,
+  // 16 waves of 64x64 (160 KB of LDS, one workgroup per CU), weight-major
+  // in XCD chunks; batched 128 x 128, 4 waves of 64x64 (80 KB, two per CU),
   // route-major
-  if (g.rows.layout == 0) return launch_split<EPI, 256, 256, 64, 4, 4, 4>(g, s);
-  return launch<EPI, 128, 128, 64, 2, 2, 2, 2, kRouteMajor>(g, s);
+  if (g.rows.layout == 0) return launch_split<EPI, 256, 256, 64, 4, 4, 4, kWeightMajor>(g, s);
+  return launch_split<EPI, 128, 128, 64, 2, 2, 2, kRouteMajor>(g, s);
 }
 
 }  // namespace tile

@@ -106,10 +106,14 @@ struct GemmArgs {
 // the route count of one contiguous tile; the batched tiles hold 128 rows.
 constexpr int kTileRoutesContiguous = 256;
 constexpr int kTileRowsBatched = 128;
+// The MXFP8 tiles hold 64 routes (the align pads each expert's run to 64)
+// and 256 weight rows.
+constexpr int kTileRoutesMxfp8 = 64;
 
 hipError_t launch_gemm_tile_bf16(const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_stream_bf16(const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_stream_mxfp8(const GemmArgs& g, hipStream_t s);
+hipError_t launch_gemm_tile_mxfp8(const GemmArgs& g, hipStream_t s);
 
 // -------------------------------------------------------- single launch ----
 // Align, W1 + SiLU-and-mul and W2 + unpermute of the bf16 streaming path in

@@ -167,15 +167,24 @@ int moe_plan_init(moe_plan* plan, const moe_problem* prob) {
   if (P.w_dtype == MOE_W_MXFP8) {
     if (!contiguous)
       return fail(plan, MOE_EUNSUPPORTED, "MXFP8 weights are built for the contiguous format only");
-    if (variant == MOE_VARIANT_TILE || variant == MOE_VARIANT_FUSED)
-      return fail(plan, MOE_EUNSUPPORTED, "MXFP8 weights have only the two-launch streaming kernels");
+    if (variant == MOE_VARIANT_FUSED)
+      return fail(plan, MOE_EUNSUPPORTED, "MXFP8 weights have no single-launch kernel");
     if (P.K % 128 || P.I % 128)
       return fail(plan, MOE_EUNSUPPORTED, "MXFP8 kernels need K % 128 == 0 and I % 128 == 0");
     if (2 * P.I * P.K >= (1ll << 31))
       return fail(plan, MOE_EUNSUPPORTED, "MXFP8 kernels address one expert with 32-bit offsets");
-    variant = MOE_VARIANT_STREAM;
-    snprintf(plan->reason, sizeof(plan->reason),
-             "stream (MXFP8): weight rows streamed into scaled MFMA, 64 tokens per pass");
+    // the tiles (256 weight rows: W2 needs K % 256) unless the streaming
+    // kernels are asked for
+    if (variant == MOE_VARIANT_AUTO) variant = P.K % 256 == 0 ? MOE_VARIANT_TILE : MOE_VARIANT_STREAM;
+    if (variant == MOE_VARIANT_TILE) {
+      if (P.K % 256)
+        return fail(plan, MOE_EUNSUPPORTED, "MXFP8 tiles need K % 256 == 0");
+      snprintf(plan->reason, sizeof(plan->reason),
+               "tile (MXFP8): 128 weight rows x 64 routes per workgroup, both operands staged in LDS");
+    } else {
+      snprintf(plan->reason, sizeof(plan->reason),
+               "stream (MXFP8): weight rows streamed into scaled MFMA, 64 tokens per pass");
+    }
   } else {
     if (variant == MOE_VARIANT_AUTO) {
       // small layers (all weights within 1 GiB, at most 32 rows per expert
@@ -226,7 +235,10 @@ int moe_plan_init(moe_plan* plan, const moe_problem* prob) {
     }
   }
   plan->variant = variant;
-  plan->block_m = variant != MOE_VARIANT_TILE ? 16 : contiguous ? kTileRoutesContiguous : kTileRowsBatched;
+  plan->block_m = variant != MOE_VARIANT_TILE   ? 16
+                  : !contiguous                  ? kTileRowsBatched
+                  : P.w_dtype == MOE_W_MXFP8     ? kTileRoutesMxfp8
+                                                 : kTileRoutesContiguous;
   plan->reduce_kind = contiguous ? MOE_REDUCE_NOOP : MOE_REDUCE_NAIVE_BATCHED;
   plan->routes = R;
   const int64_t B = plan->block_m;
@@ -243,7 +255,7 @@ int moe_plan_init(moe_plan* plan, const moe_problem* prob) {
   }
   if (plan->max_tiles > 65535 || plan->max_active > 65535)
     return fail(plan, MOE_EUNSUPPORTED, "grid too large");
-  if (contiguous && variant != MOE_VARIANT_TILE) {
+  if (contiguous && (variant != MOE_VARIANT_TILE || P.w_dtype == MOE_W_MXFP8)) {
     // the streaming and MXFP8 kernels read z (and for MXFP8 the gathered
     // activation codes) through one buffer resource with 32-bit offsets,
     // whose range check stops at 2^31 - 1 bytes: rows past it would read 0
@@ -383,7 +395,8 @@ static int gate_up_act(const moe_plan* plan, const void* a, const moe_weights* w
     g.act_ld = P.K;
     g.act_bytes = plan->sorted_capacity * P.K;
     g.out_scale = at<uint8_t>(ws13, plan->off_z_scale);
-    return launch_gemm_stream_mxfp8(g, s) == hipSuccess ? MOE_OK : MOE_EHIP;
+    const hipError_t e = plan->variant == MOE_VARIANT_TILE ? launch_gemm_tile_mxfp8(g, s) : launch_gemm_stream_mxfp8(g, s);
+    return e == hipSuccess ? MOE_OK : MOE_EHIP;
   }
   g.act = a;
   g.act_ld = P.K;
@@ -401,7 +414,7 @@ static int down_unpermute(const moe_plan* plan, const moe_weights* w, void* ws13
   if (P.w_dtype == MOE_W_MXFP8) {
     g.act_scale = at<uint8_t>(ws13, plan->off_z_scale);
     g.act_bytes = plan->sorted_capacity * P.I;
-    e = launch_gemm_stream_mxfp8(g, s);
+    e = plan->variant == MOE_VARIANT_TILE ? launch_gemm_tile_mxfp8(g, s) : launch_gemm_stream_mxfp8(g, s);
   } else {
     e = plan->variant != MOE_VARIANT_TILE ? launch_gemm_stream_bf16(g, s)
                                             : launch_gemm_tile_bf16(g, s);

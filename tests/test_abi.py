@@ -62,7 +62,7 @@ def test_plans_of_the_five_workloads(idx):
     else:
         assert p.reduce_kind == moe.REDUCE_NAIVE_BATCHED and p.variant == moe.VARIANT_TILE
     expected_variant = {0: moe.VARIANT_FUSED, 1: moe.VARIANT_STREAM, 2: moe.VARIANT_TILE,
-                        3: moe.VARIANT_STREAM, 4: moe.VARIANT_TILE}[idx]
+                        3: moe.VARIANT_TILE, 4: moe.VARIANT_TILE}[idx]
     assert p.variant == expected_variant, p.reason
     # sub-buffers are in order, 256-byte aligned, and inside ws13
     offs = [p.off_counts, p.off_offsets, p.off_sorted_ids, p.off_block_expert,
@@ -73,6 +73,8 @@ def test_plans_of_the_five_workloads(idx):
     assert offs[-1] < p.ws13_bytes
     if idx == 2:
         assert p.sorted_capacity == 98048            # floor((65536 + 128 * 255) / 256) * 256
+    if idx == 3:
+        assert p.block_m == 64                       # MXFP8 tiles: 64 routes
     if idx == 4:
         assert moe.moe_naive_batched_ws_bytes(p, 512) > 0
 
@@ -85,7 +87,7 @@ def test_plans_of_the_five_workloads(idx):
     (dict(layout=1, max_tokens=0), moe.MOE_EINVAL),
     (dict(layout=1, max_tokens=64, variant=moe.VARIANT_STREAM), moe.MOE_EUNSUPPORTED),
     (dict(layout=1, max_tokens=64, w_dtype=moe.W_MXFP8), moe.MOE_EUNSUPPORTED),
-    (dict(w_dtype=moe.W_MXFP8, variant=moe.VARIANT_TILE), moe.MOE_EUNSUPPORTED),
+    (dict(w_dtype=moe.W_MXFP8, variant=moe.VARIANT_TILE, K=128), moe.MOE_EUNSUPPORTED),   # MXFP8 tiles: K % 256
     (dict(K=128, variant=moe.VARIANT_TILE), moe.MOE_EUNSUPPORTED),   # contiguous tiles need K % 256
     (dict(global_experts=4), moe.MOE_EINVAL),             # fewer global than local experts
     (dict(global_experts=1 << 31), moe.MOE_EINVAL),

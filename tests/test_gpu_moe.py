@@ -156,6 +156,22 @@ def test_mxfp8_intermediates():
     assert err <= bound
 
 
+@pytest.mark.parametrize("cfg", [mi.config(3).scaled(M=4160, K=512, I=256),
+                                 mi.config(3).scaled(M=12000, K=256, I=128)],
+                         ids=["m4160", "m12000_375_routes_per_expert"])
+def test_mxfp8_tile_equals_stream(cfg):
+    """The MXFP8 tile kernels (both operands staged in LDS, weights read once
+    per expert however many 64-route tiles it has) and the streaming kernels
+    accumulate the same scaled MFMA over the same k steps in the same order:
+    the outputs agree bit for bit, and with the oracle."""
+    c = make_case(cfg)
+    tile, ptile, *_ = run_contiguous(c, moe.VARIANT_TILE, poison=True)
+    stream, pstream, *_ = run_contiguous(c, moe.VARIANT_STREAM, poison=True)
+    assert ptile.variant == moe.VARIANT_TILE and pstream.variant == moe.VARIANT_STREAM
+    assert torch.equal(tile.view(torch.int16), stream.view(torch.int16)), "MXFP8 tile and stream outputs differ"
+    check_close(tile, oracle_contiguous(c, np.arange(cfg.M)), MX_REL, 0.0, f"{cfg.name} tile")
+
+
 def test_tiny_intermediate_z():
     """z = silu(x W1g^T) * (x W1u^T) at each sorted position (tile path)."""
     cfg = mi.config(0)
