@@ -154,7 +154,7 @@ DOMINANT_KERNEL = {"tiny": FUSED_KERNELS, "decode": ["gemm_stream_bf16_kernel<0,
                    "prefill": ["gemm_tile_split_bf16_kernel<0,"],
                    "mxfp8": ["quantize_gather_kernel", "gemm_tile_mxfp8_kernel<0"],
                    "mxfp8_stream": ["quantize_gather_kernel", "gemm_stream_mxfp8_kernel<0,"],
-                   "batched": ["gemm_tile_bf16_kernel<0,", "gemm_tile_bf16_kernel<1,"],
+                   "batched": ["gemm_tile_split_bf16_kernel<0,", "gemm_tile_split_bf16_kernel<1,"],
                    "decode_fused": FUSED_KERNELS, "tiny_fused": FUSED_KERNELS,
                    "train_gu": ["train_wgrad_kernel"], "train_dn": ["train_wgrad_kernel"]}
 KERNEL_FILES = {"tiny": FUSED_FILES, "decode": ["gemm_stream.hip", "stream_bf16.h"],
