@@ -173,12 +173,10 @@ int moe_plan_init(moe_plan* plan, const moe_problem* prob) {
       return fail(plan, MOE_EUNSUPPORTED, "MXFP8 kernels need K % 128 == 0 and I % 128 == 0");
     if (2 * P.I * P.K >= (1ll << 31))
       return fail(plan, MOE_EUNSUPPORTED, "MXFP8 kernels address one expert with 32-bit offsets");
-    // the tiles (256 weight rows: W2 needs K % 256) unless the streaming
-    // kernels are asked for
-    if (variant == MOE_VARIANT_AUTO) variant = P.K % 256 == 0 ? MOE_VARIANT_TILE : MOE_VARIANT_STREAM;
+    // the tiles (128 weight rows: 64 W1 features, 128 W2 rows, covered by
+    // the checks above) unless the streaming kernels are asked for
+    if (variant == MOE_VARIANT_AUTO) variant = MOE_VARIANT_TILE;
     if (variant == MOE_VARIANT_TILE) {
-      if (P.K % 256)
-        return fail(plan, MOE_EUNSUPPORTED, "MXFP8 tiles need K % 256 == 0");
       snprintf(plan->reason, sizeof(plan->reason),
                "tile (MXFP8): 128 weight rows x 64 routes per workgroup, both operands staged in LDS");
     } else {

@@ -87,7 +87,6 @@ def test_plans_of_the_five_workloads(idx):
     (dict(layout=1, max_tokens=0), moe.MOE_EINVAL),
     (dict(layout=1, max_tokens=64, variant=moe.VARIANT_STREAM), moe.MOE_EUNSUPPORTED),
     (dict(layout=1, max_tokens=64, w_dtype=moe.W_MXFP8), moe.MOE_EUNSUPPORTED),
-    (dict(w_dtype=moe.W_MXFP8, variant=moe.VARIANT_TILE, K=128), moe.MOE_EUNSUPPORTED),   # MXFP8 tiles: K % 256
     (dict(K=128, variant=moe.VARIANT_TILE), moe.MOE_EUNSUPPORTED),   # contiguous tiles need K % 256
     (dict(global_experts=4), moe.MOE_EINVAL),             # fewer global than local experts
     (dict(global_experts=1 << 31), moe.MOE_EINVAL),
@@ -115,6 +114,18 @@ def test_global_experts_topk_range():
     assert p.prob.global_experts == 512
     with pytest.raises(moe.MoeError):
         moe.moe_plan_init(moe.make_problem(64, 256, 512, 2, topk=8))
+
+
+def test_mxfp8_tile_shapes():
+    """The MXFP8 tiles (128 weight rows: 64 W1 features, 128 W2 rows) take
+    every shape the MXFP8 kernels take (K and I multiples of 128); the
+    streaming kernels only when asked for."""
+    for K, I in [(128, 128), (384, 256), (6144, 2048)]:
+        p = moe.moe_plan_init(moe.make_problem(512, K, I, 32, topk=8, w_dtype=moe.W_MXFP8))
+        assert p.variant == moe.VARIANT_TILE and p.block_m == 64
+    p = moe.moe_plan_init(moe.make_problem(512, 384, 256, 32, topk=8, w_dtype=moe.W_MXFP8,
+                                           variant=moe.VARIANT_STREAM))
+    assert p.variant == moe.VARIANT_STREAM and p.block_m == 16
 
 
 def test_batched_tile_shapes():

@@ -24,7 +24,8 @@ CONTIGUOUS = [
     ("tiny_tile", mi.config(0), moe.VARIANT_TILE),
     ("decode_stream", mi.config(1).scaled(K=512, I=1024), moe.VARIANT_STREAM),
     ("prefill_tile", mi.config(2).scaled(M=700, K=512, I=384, E=24), moe.VARIANT_AUTO),
-    ("mxfp8_stream", mi.config(3).scaled(M=512, K=512, I=256), moe.VARIANT_AUTO),
+    ("mxfp8_tile", mi.config(3).scaled(M=512, K=512, I=256), moe.VARIANT_AUTO),
+    ("mxfp8_stream", mi.config(3).scaled(M=512, K=512, I=256), moe.VARIANT_STREAM),
 ]
 
 

@@ -49,10 +49,19 @@ SCALED = [
     ("mxfp8_m512", mi.config(3).scaled(M=512, K=512, I=256), moe.VARIANT_AUTO),
     ("mxfp8_m4160", mi.config(3).scaled(M=4160, K=512, I=256), moe.VARIANT_AUTO),
     ("mxfp8_m12000", mi.config(3).scaled(M=12000, K=256, I=128), moe.VARIANT_AUTO),
-    # W1 weights 8 steps ahead: one trip of two chunks (8 steps), and a full
-    # trip before the last (16 steps) with two 64-token passes per expert
     ("mxfp8_k1024", mi.config(3).scaled(M=512, K=1024, I=256), moe.VARIANT_AUTO),
     ("mxfp8_m4160_k2048", mi.config(3).scaled(M=4160, K=2048, I=128), moe.VARIANT_AUTO),
+    # tiles with an odd number of 128-wide steps (K = 384: 3 W1 steps) and a
+    # single step (K = 128), W2 over I = 384 (3 steps)
+    ("mxfp8_k384", mi.config(3).scaled(M=700, K=384, I=256), moe.VARIANT_AUTO),
+    ("mxfp8_k128_i384", mi.config(3).scaled(M=300, K=128, I=384), moe.VARIANT_AUTO),
+    # streaming kernels, W1 weights 8 steps ahead: one trip of two chunks
+    # (8 steps), and a full trip before the last (16 steps) with two
+    # 64-token passes per expert
+    ("mxfp8_k512_stream", mi.config(3).scaled(M=512, K=512, I=256), moe.VARIANT_STREAM),
+    ("mxfp8_k1024_stream", mi.config(3).scaled(M=512, K=1024, I=256), moe.VARIANT_STREAM),
+    ("mxfp8_m4160_k2048_stream", mi.config(3).scaled(M=4160, K=2048, I=128), moe.VARIANT_STREAM),
+    ("mxfp8_k384_stream", mi.config(3).scaled(M=700, K=384, I=256), moe.VARIANT_STREAM),
 ]
 
 
