@@ -206,16 +206,18 @@ void moe_struct_sizes(int64_t* problem, int64_t* plan, int64_t* weights);
  * "Fused MoE Modular Kernel", section "workspace_shapes()" (the caller
  * allocates ws13 and ws2 of the sizes the plan states, once, at the largest
  * size it needs), and the reduce kind of section
- * "finalize_weight_and_reduce_impl()".  Chooses the kernel variant
- * (STREAM when at most 64 rows can reach one expert, else TILE), the align
+ * "finalize_weight_and_reduce_impl()".  Chooses the kernel variant when
+ * prob->variant is AUTO (bf16 contiguous: FUSED for small layers — all
+ * weights within 1 GiB, at most 32 routes per expert slot, R <= 8192,
+ * E <= 2048, K and I multiples of 128 — else STREAM for M <= 16, else TILE; batched and MXFP8: TILE), the align
  * tile size, the workspace sizes and the reduce kind (NOOP for contiguous,
  * NAIVE_BATCHED for batched).  Errors: MOE_EINVAL for null pointers,
  * non-positive sizes, topk > E, global_experts neither 0 nor in [E, 2^31),
  * bad enum values or index ranges past 2^31;
  * MOE_EUNSUPPORTED (with plan->reason set) for shapes no kernel is built
- * for: the tiled kernels need K % 256 == 0 and I % 128 == 0 (contiguous
- * format) or K % 128 == 0 and I % 64 == 0 (batched format), the streaming
- * and MXFP8 kernels K % 128 == 0 and I % 128 == 0. */
+ * for: the bf16 tiled kernels need K % 256 == 0 and I % 128 == 0
+ * (contiguous format) or K % 128 == 0 and I % 64 == 0 (batched format), the
+ * streaming kernels and both MXFP8 families K % 128 == 0 and I % 128 == 0. */
 int moe_plan_init(moe_plan* plan, const moe_problem* prob);
 
 /* plan->reason: why moe_plan_init chose this kernel family, or why it
