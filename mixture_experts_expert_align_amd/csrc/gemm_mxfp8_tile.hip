@@ -72,13 +72,84 @@ static_assert(kBM == 64, "route scale words fill one 256-byte block");
 // byte offset of logical 16-byte chunk c of a 128-byte row
 __device__ __forceinline__ int chunk_off(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
 
+// The tile's end.  acc[t][c][r]: weight row 32 wave + 16 t + 4 q + r, route
+// 16 c + l16.  The operand slots are free (the caller has waited for every
+// load and met a barrier), so W1 stages z there.
+template <int EPI, int NW, int SMEM>
+__device__ __forceinline__ void mx_epilogue(const GemmArgs& g, const TileCoord& tc, const f32x4 (&acc)[2][4],
+                                            uint8_t* smem) {
+  constexpr int kBN = 32 * NW;
+  const RowMap& rm = g.rows;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l16 = lane & 15;
+  const int q = lane >> 4;
+  if (EPI == kEpiGateUp) {
+    // z[route][feature] (fp32, rows of 132 floats so the float4 reads of
+    // consecutive routes fall on different banks)
+    constexpr int kZs = 132;
+    static_assert(kBM * kZs * 4 <= SMEM && kBN / 2 <= kZs - 4, "z fits the LDS");
+    float* zs = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        zs[(16 * c + l16) * kZs + 16 * wave + 4 * q + r] = silu_f32(acc[0][c][r]) * acc[1][c][r];
+    lds_barrier();
+    // thread: route m, 32-feature block b of the tile's BN/2 features
+    const int m = threadIdx.x & (kBM - 1);
+    const int b = threadIdx.x / kBM;
+    if (b < kBN / 64 && m < tc.nvalid) {
+      float z[32];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float4 v = *reinterpret_cast<const float4*>(zs + m * kZs + 32 * b + 4 * i);
+        z[4 * i] = v.x; z[4 * i + 1] = v.y; z[4 * i + 2] = v.z; z[4 * i + 3] = v.w;
+      }
+      float bm = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) bm = fmaxf(bm, fabsf(z[i]));
+      const uint32_t sc = mx_scale_code(bm);
+      const float inv = mx_inv_scale(sc);
+      uint32_t w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        w[i] = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[i] |= e4m3_encode(z[4 * i + j] * inv) << (8 * j);
+      }
+      const int64_t pos = tc.row0 + m;
+      const int f = tc.col0 / 2 + 32 * b;   // first feature of the block
+      uint8_t* o = static_cast<uint8_t*>(g.out) + pos * g.out_ld + f;
+      *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4*>(o + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+      g.out_scale[pos * (g.out_ld / 32) + f / 32] = (uint8_t)sc;
+    }
+  } else {
+    uint16_t* out = static_cast<uint16_t*>(g.out);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int m = 16 * c + l16;
+      if (m >= tc.nvalid) continue;
+      const int64_t orow = rm.sorted_ids[tc.row0 + m];   // the route's (token, slot) row
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        uint32_t h[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(acc[t][c][r]);
+        *reinterpret_cast<uint2*>(out + orow * g.out_ld + tc.col0 + 32 * wave + 16 * t + 4 * q) =
+            make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      }
+    }
+  }
+}
+
 template <int EPI, int NW>
 __device__ __forceinline__ void mxfp8_tile(const GemmArgs& g, const TileCoord& tc, uint8_t* smem) {
   using T = MxTile<NW>;
   constexpr int kNW = NW;
   constexpr int kBN = T::BN;
   constexpr int kWCode = T::WCode, kXCode = T::XCode, kWScale = T::WScale, kXScale = T::XScale, kSlot = T::Slot;
-  const RowMap& rm = g.rows;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15;
@@ -210,65 +281,7 @@ __device__ __forceinline__ void mxfp8_tile(const GemmArgs& g, const TileCoord& t
   wait_vm<0>();
   lds_barrier();
 
-  // acc[t][c][r]: weight row 32 wave + 16 t + 4 q + r, route 16 c + l16
-  if (EPI == kEpiGateUp) {
-    // z[route][feature] (fp32, rows of 132 floats so the float4 reads of
-    // consecutive routes fall on different banks)
-    constexpr int kZs = 132;
-    static_assert(kBM * kZs * 4 <= kSlots * kSlot, "z fits the LDS");
-    float* zs = reinterpret_cast<float*>(smem);
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        zs[(16 * c + l16) * kZs + 16 * wave + 4 * q + r] = silu_f32(acc[0][c][r]) * acc[1][c][r];
-    lds_barrier();
-    // thread: route m, 32-feature block b of the tile's BN/2 features
-    const int m = threadIdx.x & (kBM - 1);
-    const int b = threadIdx.x / kBM;
-    if (b < kBN / 64 && m < tc.nvalid) {
-      float z[32];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float4 v = *reinterpret_cast<const float4*>(zs + m * kZs + 32 * b + 4 * i);
-        z[4 * i] = v.x; z[4 * i + 1] = v.y; z[4 * i + 2] = v.z; z[4 * i + 3] = v.w;
-      }
-      float bm = 0.f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) bm = fmaxf(bm, fabsf(z[i]));
-      const uint32_t sc = mx_scale_code(bm);
-      const float inv = mx_inv_scale(sc);
-      uint32_t w[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        w[i] = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w[i] |= e4m3_encode(z[4 * i + j] * inv) << (8 * j);
-      }
-      const int64_t pos = tc.row0 + m;
-      const int f = tc.col0 / 2 + 32 * b;   // first feature of the block
-      uint8_t* o = static_cast<uint8_t*>(g.out) + pos * g.out_ld + f;
-      *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2], w[3]);
-      *reinterpret_cast<uint4*>(o + 16) = make_uint4(w[4], w[5], w[6], w[7]);
-      g.out_scale[pos * (g.out_ld / 32) + f / 32] = (uint8_t)sc;
-    }
-  } else {
-    uint16_t* out = static_cast<uint16_t*>(g.out);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int m = 16 * c + l16;
-      if (m >= tc.nvalid) continue;
-      const int64_t orow = rm.sorted_ids[tc.row0 + m];   // the route's (token, slot) row
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        uint32_t h[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(acc[t][c][r]);
-        *reinterpret_cast<uint2*>(out + orow * g.out_ld + tc.col0 + 32 * wave + 16 * t + 4 * q) =
-            make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-      }
-    }
-  }
+  mx_epilogue<EPI, NW, kSlots * kSlot>(g, tc, acc, smem);
 }
 
 // WPC workgroups per CU (each ring takes 3 slots of LDS) walk the tiles in

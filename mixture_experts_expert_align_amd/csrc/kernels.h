@@ -107,7 +107,7 @@ struct GemmArgs {
 constexpr int kTileRoutesContiguous = 256;
 constexpr int kTileRowsBatched = 128;
 // The MXFP8 tiles hold 64 routes (the align pads each expert's run to 64)
-// and 256 weight rows.
+// and 128 weight rows.
 constexpr int kTileRoutesMxfp8 = 64;
 
 hipError_t launch_gemm_tile_bf16(const GemmArgs& g, hipStream_t s);
