@@ -162,7 +162,8 @@ KERNEL_FILES = {"tiny": FUSED_FILES, "decode": ["gemm_stream.hip", "stream_bf16.
                 "mxfp8": ["reduce_codec.hip", "gemm_mxfp8_tile.hip", "tile_common.h"],
                 "mxfp8_stream": ["reduce_codec.hip", "gemm_mxfp8.hip"],
                 "batched": ["gemm_tile.hip", "tile_common.h"], "decode_fused": FUSED_FILES, "tiny_fused": FUSED_FILES,
-                "train_gu": ["train.hip"], "train_dn": ["train.hip"]}
+                "train_gu": ["train.hip", "gemm_tile.hip", "tile_common.h"],
+                "train_dn": ["train.hip", "gemm_tile.hip", "tile_common.h"]}
 
 
 def main():

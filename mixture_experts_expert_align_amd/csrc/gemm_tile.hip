@@ -101,7 +101,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const TileCoord
   const int col = EPI == kEpiGateUp ? tc.col0 / 2 : tc.col0;
   const int c = threadIdx.x % NCH;
   for (int m = threadIdx.x / NCH; m < BM; m += NT / NCH) {
-    if (rm.layout != 0 && m >= tc.nvalid) continue;   // batched: rows past the count are not written
+    if (rm.layout != 0 && (m < tc.mlo || m >= tc.nvalid)) continue;   // batched / rows: only the tile's own rows
     int64_t orow;
     if (EPI == kEpiGateUp || rm.layout != 0) {
       orow = tc.row0 + m;
@@ -153,7 +153,7 @@ __device__ __forceinline__ void load_offsets(const GemmArgs& g, const TileCoord&
     const int c = (lane % CH) ^ ((m / RPW) & (CH - 1));
     int64_t row = -1;
     if (rm.layout != 0) {
-      if (m < tc.nvalid) row = tc.row0 + m;   // rows past the expert's count are never read
+      if (m >= tc.mlo && m < tc.nvalid) row = tc.row0 + m;   // rows outside the tile's own are never read
     } else if (EPI == kEpiGateUp) {
       const int sid = rm.sorted_ids[tc.row0 + m];
       if (sid != rm.sentinel) row = sid / rm.topk;
@@ -203,9 +203,18 @@ __device__ __forceinline__ void frag_rows(int wn, int wm, int lane, int (&wrow_l
 //  * A wave whose route rows are all padding runs the same loop without
 //    fragment reads and MFMAs (its own copy of the loop, so the live copy
 //    has no branches around its MFMAs).
-template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, int ORDER>
-__global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_split_bf16_kernel(GemmArgs g, int ncol,
-                                                                                int64_t nlog) {
+template <int BM, int BN, int BK>
+struct SplitRing {
+  static constexpr int WS = 3, RS = 2;              // weight / route slots
+  static constexpr int WSLOT = BN * BK, RSLOT = BM * BK;
+  static constexpr int Elems = WS * WSLOT + RS * RSLOT;   // uint16 elements of LDS
+};
+
+// One tile: BN weight rows from tc.col0 times the route rows [mlo, nvalid)
+// of the BM from tc.row0, through the epilogue.  smem: SplitRing::Elems
+// elements; the caller meets a barrier before it reuses them.
+template <int EPI, int BM, int BN, int BK, int WN, int WM>
+__device__ __forceinline__ void split_tile(const GemmArgs& g, const TileCoord& tc, uint16_t* smem) {
   constexpr int NW = WN * WM;
   constexpr int CH = BK / 8;
   constexpr int RPB = 64 / CH;
@@ -213,18 +222,16 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_split_bf16_kernel
   constexpr int LX = BM / RPB / NW;          // route loads per wave per slice
   static_assert(LW * NW * RPB == BN && LX * NW * RPB == BM, "blocks / waves mismatch");
   static_assert(2 * LW < 64, "wait counts");
-  constexpr int WS = 3, RS = 2;              // weight / route slots
-  constexpr int WSLOT = BN * BK, RSLOT = BM * BK;
+  using Ring = SplitRing<BM, BN, BK>;
+  constexpr int WS = Ring::WS, RS = Ring::RS;
+  constexpr int WSLOT = Ring::WSLOT, RSLOT = Ring::RSLOT;
   constexpr int TW = BN / WN / 32;
   constexpr int TX = BM / WM / 32;
   constexpr int NSTEP = BK / 16;
   static_assert(EPI != kEpiGateUp || TW % 2 == 0, "gate/up pairs need an even tile count");
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[WS * WSLOT + RS * RSLOT];
   uint16_t* const wbase = smem;
   uint16_t* const rbase = smem + WS * WSLOT;
 
-  TileCoord tc;
-  if (!tile_coord<BM, BN, ORDER>(g, ncol, nlog, tc)) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave / WM;
@@ -242,7 +249,8 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_split_bf16_kernel
   bool xload[LX];
 #pragma unroll
   for (int i = 0; i < LX; ++i)
-    xload[i] = __builtin_amdgcn_readfirstlane((int)((wave + NW * i) * RPB < tc.nvalid)) != 0;
+    xload[i] = __builtin_amdgcn_readfirstlane(
+                   (int)((wave + NW * i) * RPB < tc.nvalid && (wave + NW * i + 1) * RPB > tc.mlo)) != 0;
   auto issue_w = [&](int kt) {
     uint16_t* slot = wbase + (kt % WS) * WSLOT;
 #pragma unroll
@@ -250,7 +258,7 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_split_bf16_kernel
     issue_order();
   };
   auto issue_r = [&](int kt) {
-    uint16_t* slot = rbase + (kt & 1) * RSLOT;
+    uint16_t* slot = rbase + (kt % RS) * RSLOT;
 #pragma unroll
     for (int i = 0; i < LX; ++i)
       if (xload[i]) lds_load16(ar, slot + (wave + NW * i) * RPB * BK, ox[i], kt * BK * 2);
@@ -269,7 +277,7 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_split_bf16_kernel
   // fragments of k step s of slice kt into buffer fb
   auto fload = [&](int fb, int kt, int s) {
     const uint16_t* ws = wbase + (kt % WS) * WSLOT;
-    const uint16_t* rs = rbase + (kt & 1) * RSLOT;
+    const uint16_t* rs = rbase + (kt % RS) * RSLOT;
     const int c = 2 * s + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < TW; ++i)
@@ -344,16 +352,82 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_split_bf16_kernel
     if (kt + 1 < nk) slice(kt++, std::integral_constant<int, 0>(), live);
     slice(kt, std::integral_constant<int, -1>(), live);
   };
-  // a wave whose route rows all lie past the tile's valid rows holds only
+  // a wave whose route rows all lie outside the tile's valid rows holds only
   // padding: it loads and meets the barriers but computes nothing (its
   // accumulators stay 0, what zero-filled padding rows would give)
-  if (wm * (BM / WM) < tc.nvalid) run(std::true_type());
+  if (wm * (BM / WM) < tc.nvalid && (wm + 1) * (BM / WM) > tc.mlo) run(std::true_type());
   else run(std::false_type());
 
   wait_vm<0>();
   lds_barrier();
-  static_assert(BM * (EPI == kEpiGateUp ? BN / 2 : BN) <= WS * WSLOT + RS * RSLOT, "epilogue tile fits the LDS");
+  static_assert(BM * (EPI == kEpiGateUp ? BN / 2 : BN) <= Ring::Elems, "epilogue tile fits the LDS");
   tile_epilogue<EPI, BM, BN, WN, WM, 64 * WN * WM>(g, tc, acc, wn, wm, lane, smem);
+}
+
+template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, int ORDER>
+__global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_split_bf16_kernel(GemmArgs g, int ncol,
+                                                                                int64_t nlog) {
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[SplitRing<BM, BN, BK>::Elems];
+  TileCoord tc;
+  if (!tile_coord<BM, BN, ORDER>(g, ncol, nlog, tc)) return;
+  split_tile<EPI, BM, BN, BK, WN, WM>(g, tc, smem);
+}
+
+// Training forward (page "Cake deterministic MoE grouped GEMM",
+// introduction): y[r] = W[e] x[r] for the rows r of group e, rows grouped by
+// expert in x (layout 2: the route rows of a tile are rows of x, and the
+// outputs go to the same rows of y).  A logical tile is BM rows of x from r0
+// times BN features of y; it runs the contraction once per group its rows
+// meet, each time with only that group's rows live (rows of other groups
+// load nothing and are not written), so every output element comes from one
+// pass with a fixed contraction order.  The (row tile, column tile) grid is
+// cut into blocks of kRowBlock row tiles x kColBlock column tiles, one block
+// per XCD chunk, row-block major: the 32 tiles an XCD runs together share
+// kRowBlock row tiles of x and kColBlock weight tiles in its L2 (x and W
+// are each far larger than the Infinity Cache, so an order that streams one
+// of them per column or row tile would read it from HBM again each time).
+constexpr int kRowBlock = 4, kColBlock = 8;
+static_assert(kRowBlock * kColBlock == kXcdChunk, "a block fills one XCD chunk");
+
+template <int BM, int BN, int BK, int WN, int WM, int OCC>
+__global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_rows_kernel(GemmArgs g, const int32_t* offsets,
+                                                                          int E, int64_t R, int64_t nrt,
+                                                                          int64_t nct) {
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[SplitRing<BM, BN, BK>::Elems];
+  // block b runs on XCD b % 8 as that XCD's (b / 8)-th block: chunk
+  // (k / 32) * 8 + b % 8, tile k % 32 of it
+  const int64_t b = blockIdx.x;
+  const int64_t k = b / NXCD;
+  const int64_t chunk = (k / kXcdChunk) * NXCD + b % NXCD;
+  const int t = (int)(k % kXcdChunk);
+  const int64_t ncb = (nct + kColBlock - 1) / kColBlock;
+  const int64_t rt = (chunk / ncb) * kRowBlock + t / kColBlock;
+  const int64_t ct = (chunk % ncb) * kColBlock + t % kColBlock;
+  if (rt >= nrt || ct >= nct) return;
+  const int64_t r0 = rt * BM;
+  auto off = [&](int e) { return min<int64_t>(max<int64_t>(offsets[e], 0), R); };
+  // first group with rows past r0
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (off(mid + 1) > r0) hi = mid; else lo = mid + 1;
+  }
+  TileCoord tc;
+  tc.col0 = (int)ct * BN;
+  tc.row0 = r0;
+  bool first = true;
+  for (int e = lo; e < E; ++e) {
+    const int64_t a = off(e), z = max(off(e + 1), a);
+    if (a >= r0 + BM) break;
+    const int64_t s0 = max(a, r0), s1 = min(z, r0 + BM);
+    if (s1 <= s0) continue;
+    if (!first) lds_barrier();   // the previous pass's epilogue has read its LDS
+    first = false;
+    tc.expert = e;
+    tc.mlo = (int)(s0 - r0);
+    tc.nvalid = (int)(s1 - r0);
+    split_tile<kEpiDown, BM, BN, BK, WN, WM>(g, tc, smem);
+  }
 }
 
 template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, int ORDER>
@@ -383,6 +457,20 @@ hipError_t launch_layout(const GemmArgs& g, hipStream_t s) {
 }
 
 }  // namespace tile
+
+// 256 rows x 256 features, the contiguous tile shape
+hipError_t launch_tile_rows_bf16(const GemmArgs& g, const int32_t* offsets, int64_t R, hipStream_t s) {
+  using namespace tile;
+  constexpr int BM = 256, BN = 256;
+  if (g.rows.layout != 2 || g.epi != kEpiDown || g.nfeat % BN || g.kdim % 64) return hipErrorInvalidValue;
+  if (R <= 0) return hipSuccess;
+  const int64_t nrt = (R + BM - 1) / BM, nct = g.nfeat / BN;
+  const int64_t nchunk = (nrt + kRowBlock - 1) / kRowBlock * ((nct + kColBlock - 1) / kColBlock);
+  const int64_t grid = (nchunk + NXCD - 1) / NXCD * NXCD * kXcdChunk;
+  hipLaunchKernelGGL((gemm_tile_rows_kernel<BM, BN, 64, 4, 4, 4>), dim3((unsigned)grid), dim3(1024), 0, s, g, offsets,
+                     g.E, R, nrt, nct);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_tile_bf16(const GemmArgs& g, hipStream_t s) {
   if (g.epi == kEpiGateUp) return tile::launch_layout<kEpiGateUp>(g, s);

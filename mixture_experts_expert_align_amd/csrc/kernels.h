@@ -63,7 +63,8 @@ enum Epilogue { kEpiGateUp = 0, kEpiDown = 1 };
 // the contiguous format, or rows r < count[e] of each expert's slab for the
 // batched format.
 struct RowMap {
-  int32_t layout;              // 0 contiguous, 1 batched
+  int32_t layout;              // 0 contiguous, 1 batched, 2 rows (grouped rows of the
+                               // activation matrix, outputs to the same rows)
   const int32_t* sorted_ids;   // contiguous
   const int32_t* block_expert; // contiguous (tile path)
   const int32_t* num_post;     // contiguous
@@ -111,6 +112,9 @@ constexpr int kTileRowsBatched = 128;
 constexpr int kTileRoutesMxfp8 = 64;
 
 hipError_t launch_gemm_tile_bf16(const GemmArgs& g, hipStream_t s);
+// rows layout (2): y rows = W[e] x rows for the groups offsets[e] ..
+// offsets[e+1] of R rows; 256 x 256 tiles (nfeat % 256 == 0, kdim % 64 == 0)
+hipError_t launch_tile_rows_bf16(const GemmArgs& g, const int32_t* offsets, int64_t R, hipStream_t s);
 hipError_t launch_gemm_stream_bf16(const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_stream_mxfp8(const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_tile_mxfp8(const GemmArgs& g, hipStream_t s);

@@ -26,8 +26,10 @@ __device__ __forceinline__ int lds_off(int row, int c) {
 // Workgroup -> (expert, first weight row, first route row).
 struct TileCoord {
   int expert, col0;
-  int64_t row0;   // contiguous: sorted position; batched: slab row e*max_tokens + r0
-  int nvalid;     // route rows of the tile that exist (the rest are padding)
+  int64_t row0;   // contiguous: sorted position; batched: slab row e*max_tokens + r0;
+                  // rows: first row of the tile
+  int mlo;        // route rows [mlo, nvalid) of the tile exist (the rest are padding)
+  int nvalid;
 };
 
 __host__ __device__ inline int64_t padded_blocks(int64_t nlog) {
@@ -80,6 +82,7 @@ __device__ __forceinline__ bool tile_coord(const GemmArgs& g, int ncol, int64_t 
       tc.row0 = (t0 + local % ne) * BM;
     }
     // the expert's run holds counts[lo] routes, then padding to a tile
+    tc.mlo = 0;
     tc.nvalid = (int)max<int64_t>(0, min<int64_t>(BM, rm.counts[lo] - (tc.row0 - rm.offsets[lo])));
     return true;
   }
@@ -93,6 +96,7 @@ __device__ __forceinline__ bool tile_coord(const GemmArgs& g, int ncol, int64_t 
   tc.expert = e;
   tc.col0 = (ORDER == kRouteMajor ? local % ncol : local / tpe) * BN;
   tc.row0 = (int64_t)e * rm.max_tokens + r0;
+  tc.mlo = 0;
   tc.nvalid = min(BM, cnt - r0);
   return true;
 }

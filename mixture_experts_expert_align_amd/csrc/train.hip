@@ -427,8 +427,31 @@ __global__ void __launch_bounds__(WgradTile::NT, 2) train_wgrad_kernel(TrainArgs
 
 }  // namespace train
 
+// The forward on the inference tile kernel (rows layout: 256 rows of x by
+// 256 output features per tile, both operands loaded straight into LDS) when
+// N is a multiple of 256.
+static bool forward_on_tiles(const TrainArgs& t) { return t.mode == kTrainForward && t.N % 256 == 0; }
+
+static hipError_t launch_forward_tiles(const TrainArgs& t, hipStream_t s) {
+  GemmArgs g = {};
+  g.epi = kEpiDown;
+  g.rows.layout = 2;
+  g.act = t.x;
+  g.act_ld = t.K;
+  g.act_bytes = t.R * t.K * 2;
+  g.w = t.w;
+  g.w_expert_stride = (int64_t)t.N * t.K;
+  g.kdim = t.K;
+  g.nfeat = t.N;
+  g.E = t.E;
+  g.out = t.out;
+  g.out_ld = t.N;
+  return launch_tile_rows_bf16(g, t.offsets, t.R, s);
+}
+
 hipError_t launch_train(const TrainArgs& t, hipStream_t s) {
   using namespace train;
+  if (forward_on_tiles(t)) return launch_forward_tiles(t, s);
   if (t.mode == kTrainWgrad) {
     using W = WgradTile;
     hipLaunchKernelGGL(train_wgrad_kernel, dim3((t.N / W::BI) * ((t.K + W::BJ - 1) / W::BJ), t.E),

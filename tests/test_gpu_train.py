@@ -125,10 +125,31 @@ def test_train_ragged_edges(sizes):
     check_accumulate_bits(ti, dw, acc)
 
 
+@pytest.mark.parametrize("E,N,K,rows", [(16, 512, 1024, 5000), (9, 768, 256, 2600)])
+def test_train_zipf_every_element(E, N, K, rows):
+    """Zipf-sized groups (two of them empty) that start and end inside the
+    256-row tiles of the forward, several groups sharing a tile: every
+    element of y, dx and dW against the oracle."""
+    cfg = mi.TrainConfig(f"train_zipf_e{E}_n{N}_k{K}_r{rows}", 24, E=E, N=N, K=K, rows=rows, balance="zipf")
+    ti = mi.make_train_inputs(cfg, device="cuda")
+    sizes = np.diff(ti.offsets)
+    say(f"[train] {cfg.name}: group sizes {sizes.tolist()}")
+    y, dx, dw, acc = run(ti)
+    x, dy, w = host(ti.x), host(ti.dy), host(ti.w)
+    off = ti.offsets
+    check_close(y, oracle.grouped_forward(x, w, off), BF16_REL, BF16_ABS, "forward")
+    check_close(dx, oracle.grouped_dgrad(dy, w, off), BF16_REL, BF16_ABS, "dgrad")
+    ref = oracle.grouped_wgrad(dy, x, off)
+    err = np.abs(dw.cpu().numpy().astype(np.float64) - ref)
+    assert np.all(err <= wgrad_bound(dy, x, off))
+    check_accumulate_bits(ti, dw, acc)
+    del ti; free()
+
+
 def test_train_gu_full_size_sampled():
     """The gate/up shape at full size (E=32, N=4096, K=6144, 1024 rows per
-    group), in the launch configuration bench.py times: sampled dx rows and
-    dW elements against the oracle, every element's accumulate bits, and
+    group), in the launch configuration bench.py times: sampled y and dx rows
+    and dW elements against the oracle, every element's accumulate bits, and
     run-to-run equality of every output."""
     cfg = mi.train_config("train_gu")
     ti = mi.make_train_inputs(cfg, device="cuda")
@@ -136,15 +157,18 @@ def test_train_gu_full_size_sampled():
     R = int(ti.offsets[-1])
     outs = []
     for _ in range(2):
+        y = torch.empty((R, cfg.N), dtype=torch.bfloat16, device="cuda")
         dx = torch.empty((R, cfg.K), dtype=torch.bfloat16, device="cuda")
         dw = torch.empty((cfg.E, cfg.N, cfg.K), dtype=torch.float32, device="cuda")
+        moe.moe_grouped_forward(ti.x, ti.w, off, y)
         moe.moe_grouped_dgrad(ti.dy, ti.w, off, dx)
         moe.moe_grouped_wgrad(ti.dy, ti.x, off, dw)
         torch.cuda.synchronize()
-        outs.append((dx, dw))
+        outs.append((y, dx, dw))
     assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
-    assert torch.equal(outs[0][1].view(torch.int32), outs[1][1].view(torch.int32))
-    dx, dw = outs[0]
+    assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
+    assert torch.equal(outs[0][2].view(torch.int32), outs[1][2].view(torch.int32))
+    y, dx, dw = outs[0]
     del outs
     acc = ti.main_grad.clone()
     moe.moe_grouped_wgrad(ti.dy, ti.x, off, acc, accumulate=True)
@@ -156,6 +180,8 @@ def test_train_gu_full_size_sampled():
         a, b = int(ti.offsets[e]), int(ti.offsets[e + 1])
         rows = np.sort(rng.choice(np.arange(a, b), size=8, replace=False))
         we = host(ti.w[e])
+        ref = host(ti.x[torch.from_numpy(rows).cuda()]) @ we.T
+        check_close(y[torch.from_numpy(rows).cuda()], ref, BF16_REL, BF16_ABS, f"forward e={e}")
         ref = host(ti.dy[torch.from_numpy(rows).cuda()]) @ we
         check_close(dx[torch.from_numpy(rows).cuda()], ref, BF16_REL, BF16_ABS, f"dgrad e={e}")
         n = rng.integers(0, cfg.N, size=64)
@@ -167,4 +193,4 @@ def test_train_gu_full_size_sampled():
         got = dw[e].cpu().numpy()[n, k].astype(np.float64)
         say(f"[parity] wgrad e={e}: max err/bound {np.max(np.abs(got - ref) / bound):.3e}")
         assert np.all(np.abs(got - ref) <= bound)
-    del ti, dx, dw; free()
+    del ti, y, dx, dw; free()
