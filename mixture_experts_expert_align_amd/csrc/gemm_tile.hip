@@ -115,6 +115,33 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const TileCoord
   }
 }
 
+// Transposed weight slots (row = contraction index, 256 outputs of 2 bytes
+// a row): 16-byte chunk c of row r sits at chunk c ^ wt_swz(r), so the 4
+// rows one transposing read touches (r .. r+3 from a multiple of 4) put the
+// 16 lanes' 8-byte reads on distinct banks.
+__device__ __forceinline__ int wt_swz(int r) { return (r & 3) << 1; }
+__device__ __forceinline__ int wt_off(int r, int col) { return r * 256 + (((col >> 3) ^ wt_swz(r)) << 3) + (col & 7); }
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// MFMA row-operand fragment (32 outputs x 8 consecutive contraction values
+// per lane) of a transposed weight slot: outputs j0 .. j0+31, contraction
+// c0 + 8 (lane / 32) .. +7.  ds_read_b64_tr_b16 (gfx950): in each group of
+// 16 lanes, destination lane 4a+b receives element b of the 8 bytes read by
+// lanes a, a+4, a+8 and a+12; source lane L points at row c + L / 4, outputs
+// j + 4 (L % 4) .. +3, so destination lane D holds output j + D at rows
+// c .. c+3.  Two reads give 8 rows.
+__device__ __forceinline__ bf16x8 wt_frag(const uint16_t* slot, int j0, int c0, int lane) {
+  const int gq = lane >> 4, L = lane & 15;
+  const int j = j0 + 16 * (gq & 1) + 4 * (L & 3);
+  const int c = c0 + 8 * (gq >> 1) + (L >> 2);
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(slot + wt_off(c, j)));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(slot + wt_off(c + 4, j)));
+  const v4i16 v8[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8, v8);
+}
+
 // Per-lane byte offsets of the slice loads.  Block b of a slot (b = wave +
 // NW * i) holds rows RPB*b .. RPB*b + RPB-1 of its region; lane l lands on
 // row RPB*b + l/CH, physical chunk l%CH, which holds logical chunk
@@ -123,7 +150,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const TileCoord
 // topk) for W1, read in position order for W2, or taken from the expert's
 // slab for the batched format; a padding route (or a batched row past its
 // expert's count) gets an offset past the buffer, which loads zeros.
-template <int EPI, int BM, int BN, int BK, int NW>
+template <int EPI, int BM, int BN, int BK, int NW, bool WT>
 __device__ __forceinline__ void load_offsets(const GemmArgs& g, const TileCoord& tc, int wave, int lane,
                                              uint32_t (&ow)[BN / (512 / BK) / NW],
                                              uint32_t (&ox)[BM / (512 / BK) / NW]) {
@@ -134,6 +161,20 @@ __device__ __forceinline__ void load_offsets(const GemmArgs& g, const TileCoord&
   constexpr int LX = BM / RPB / NW;
   const RowMap& rm = g.rows;
   const int K = g.kdim;
+  if (WT) {
+    // weights stored with the output index contiguous: the slot holds BK
+    // contraction rows of BN outputs; block b = rows 2b, 2b+1 (BN = 256:
+    // 512 bytes a row), lane l -> row 2b + l / 32, physical chunk l % 32,
+    // holding logical chunk (l % 32) ^ wt_swz(row); the slice's first row
+    // comes in through the instruction offset
+    static_assert(!WT || BN * 2 == 512, "transposed weight rows of 512 bytes");
+#pragma unroll
+    for (int i = 0; i < LW; ++i) {
+      const int r = 2 * (wave + NW * i) + lane / 32;
+      const int c = (lane % 32) ^ wt_swz(r);
+      ow[i] = (uint32_t)(((int64_t)r * g.nfeat + tc.col0 + 8 * c) * 2);
+    }
+  } else
 #pragma unroll
   for (int i = 0; i < LW; ++i) {
     const int n = (wave + NW * i) * RPB + lane / CH;
@@ -213,7 +254,7 @@ struct SplitRing {
 // One tile: BN weight rows from tc.col0 times the route rows [mlo, nvalid)
 // of the BM from tc.row0, through the epilogue.  smem: SplitRing::Elems
 // elements; the caller meets a barrier before it reuses them.
-template <int EPI, int BM, int BN, int BK, int WN, int WM>
+template <int EPI, int BM, int BN, int BK, int WN, int WM, bool WT = false>
 __device__ __forceinline__ void split_tile(const GemmArgs& g, const TileCoord& tc, uint16_t* smem) {
   constexpr int NW = WN * WM;
   constexpr int CH = BK / 8;
@@ -240,7 +281,10 @@ __device__ __forceinline__ void split_tile(const GemmArgs& g, const TileCoord& t
   const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(wexp, g.w_expert_stride * 2);
   const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(g.act, g.act_bytes);
   uint32_t ow[LW], ox[LX];
-  load_offsets<EPI, BM, BN, BK, NW>(g, tc, wave, lane, ow, ox);
+  load_offsets<EPI, BM, BN, BK, NW, WT>(g, tc, wave, lane, ow, ox);
+  static_assert(!WT || EPI == kEpiDown, "transposed weights: plain outputs");
+  // per slice, the weight loads advance BK elements along a row, or BK rows
+  const int wstep = WT ? BK * g.nfeat * 2 : BK * 2;
   const int nk = g.kdim / BK;
   // A route block whose rows are all padding is not loaded: its LDS rows keep
   // stale values, which reach only those rows' own outputs (an MFMA output
@@ -254,7 +298,7 @@ __device__ __forceinline__ void split_tile(const GemmArgs& g, const TileCoord& t
   auto issue_w = [&](int kt) {
     uint16_t* slot = wbase + (kt % WS) * WSLOT;
 #pragma unroll
-    for (int i = 0; i < LW; ++i) lds_load16(wr, slot + (wave + NW * i) * RPB * BK, ow[i], kt * BK * 2);
+    for (int i = 0; i < LW; ++i) lds_load16(wr, slot + (wave + NW * i) * RPB * BK, ow[i], kt * wstep);
     issue_order();
   };
   auto issue_r = [&](int kt) {
@@ -281,7 +325,8 @@ __device__ __forceinline__ void split_tile(const GemmArgs& g, const TileCoord& t
     const int c = 2 * s + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < TW; ++i)
-      fw[fb][i] = as_bf16x8(*reinterpret_cast<const i32x4*>(&ws[lds_off<BK>(wrow_l[i], c)]));
+      fw[fb][i] = WT ? wt_frag(ws, wn * (BN / WN) + 32 * i, 16 * s, lane)
+                     : as_bf16x8(*reinterpret_cast<const i32x4*>(&ws[lds_off<BK>(wrow_l[i], c)]));
 #pragma unroll
     for (int j = 0; j < TX; ++j)
       fx[fb][j] = as_bf16x8(*reinterpret_cast<const i32x4*>(&rs[lds_off<BK>(xrow_l + 32 * j, c)]));
@@ -293,14 +338,18 @@ __device__ __forceinline__ void split_tile(const GemmArgs& g, const TileCoord& t
       for (int j = 0; j < TX; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[fb][i], fx[fb][j], acc[i][j], 0, 0, 0);
   };
-  // one fragment read, one MFMA, and so on; the MFMAs past the reads last
+  // one fragment read, one MFMA, and so on; the MFMAs (or reads) past the
+  // pairs last
   auto interleave = [&]() {
+    constexpr int NDS = (WT ? 2 : 1) * TW + TX;   // LDS reads per k step
+    constexpr int NP = NDS < TW * TX ? NDS : TW * TX;
 #pragma unroll
-    for (int q = 0; q < TW + TX; ++q) {
+    for (int q = 0; q < NP; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
     }
-    if (TW * TX > TW + TX) __builtin_amdgcn_sched_group_barrier(0x008, TW * TX - TW - TX, 0);
+    if (TW * TX > NP) __builtin_amdgcn_sched_group_barrier(0x008, TW * TX - NP, 0);
+    if (NDS > NP) __builtin_amdgcn_sched_group_barrier(0x100, NDS - NP, 0);
   };
 
   // prologue: weights 0, routes 0 and 1, weights 1 and 2; wait for slice 0
@@ -389,7 +438,7 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_split_bf16_kernel
 constexpr int kRowBlock = 4, kColBlock = 8;
 static_assert(kRowBlock * kColBlock == kXcdChunk, "a block fills one XCD chunk");
 
-template <int BM, int BN, int BK, int WN, int WM, int OCC>
+template <int BM, int BN, int BK, int WN, int WM, int OCC, bool WT>
 __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_rows_kernel(GemmArgs g, const int32_t* offsets,
                                                                           int E, int64_t R, int64_t nrt,
                                                                           int64_t nct) {
@@ -415,6 +464,18 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_rows_kernel(GemmA
   TileCoord tc;
   tc.col0 = (int)ct * BN;
   tc.row0 = r0;
+  {
+    // the common case, a tile inside one group: one pass, outside the loop
+    // (inside it the compiler keeps more values live and spills)
+    const int64_t a = off(lo), z = max(off(lo + 1), a);
+    if (a <= r0 && z >= min<int64_t>(r0 + BM, R)) {
+      tc.expert = lo;
+      tc.mlo = 0;
+      tc.nvalid = (int)(min<int64_t>(r0 + BM, R) - r0);
+      split_tile<kEpiDown, BM, BN, BK, WN, WM, WT>(g, tc, smem);
+      return;
+    }
+  }
   bool first = true;
   for (int e = lo; e < E; ++e) {
     const int64_t a = off(e), z = max(off(e + 1), a);
@@ -426,7 +487,7 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_rows_kernel(GemmA
     tc.expert = e;
     tc.mlo = (int)(s0 - r0);
     tc.nvalid = (int)(s1 - r0);
-    split_tile<kEpiDown, BM, BN, BK, WN, WM>(g, tc, smem);
+    split_tile<kEpiDown, BM, BN, BK, WN, WM, WT>(g, tc, smem);
   }
 }
 
@@ -459,7 +520,7 @@ hipError_t launch_layout(const GemmArgs& g, hipStream_t s) {
 }  // namespace tile
 
 // 256 rows x 256 features, the contiguous tile shape
-hipError_t launch_tile_rows_bf16(const GemmArgs& g, const int32_t* offsets, int64_t R, hipStream_t s) {
+hipError_t launch_tile_rows_bf16(const GemmArgs& g, const int32_t* offsets, int64_t R, bool wt, hipStream_t s) {
   using namespace tile;
   constexpr int BM = 256, BN = 256;
   if (g.rows.layout != 2 || g.epi != kEpiDown || g.nfeat % BN || g.kdim % 64) return hipErrorInvalidValue;
@@ -467,8 +528,12 @@ hipError_t launch_tile_rows_bf16(const GemmArgs& g, const int32_t* offsets, int6
   const int64_t nrt = (R + BM - 1) / BM, nct = g.nfeat / BN;
   const int64_t nchunk = (nrt + kRowBlock - 1) / kRowBlock * ((nct + kColBlock - 1) / kColBlock);
   const int64_t grid = (nchunk + NXCD - 1) / NXCD * NXCD * kXcdChunk;
-  hipLaunchKernelGGL((gemm_tile_rows_kernel<BM, BN, 64, 4, 4, 4>), dim3((unsigned)grid), dim3(1024), 0, s, g, offsets,
-                     g.E, R, nrt, nct);
+  if (wt)
+    hipLaunchKernelGGL((gemm_tile_rows_kernel<BM, BN, 64, 4, 4, 4, true>), dim3((unsigned)grid), dim3(1024), 0, s, g,
+                       offsets, g.E, R, nrt, nct);
+  else
+    hipLaunchKernelGGL((gemm_tile_rows_kernel<BM, BN, 64, 4, 4, 4, false>), dim3((unsigned)grid), dim3(1024), 0, s, g,
+                       offsets, g.E, R, nrt, nct);
   return hipGetLastError();
 }
 

@@ -113,8 +113,10 @@ constexpr int kTileRoutesMxfp8 = 64;
 
 hipError_t launch_gemm_tile_bf16(const GemmArgs& g, hipStream_t s);
 // rows layout (2): y rows = W[e] x rows for the groups offsets[e] ..
-// offsets[e+1] of R rows; 256 x 256 tiles (nfeat % 256 == 0, kdim % 64 == 0)
-hipError_t launch_tile_rows_bf16(const GemmArgs& g, const int32_t* offsets, int64_t R, hipStream_t s);
+// offsets[e+1] of R rows; 256 x 256 tiles (nfeat % 256 == 0, kdim % 64 == 0).
+// wt: W[e] is stored [kdim, nfeat] (output index contiguous) and is read
+// transposed: y rows = W[e]^T x rows.
+hipError_t launch_tile_rows_bf16(const GemmArgs& g, const int32_t* offsets, int64_t R, bool wt, hipStream_t s);
 hipError_t launch_gemm_stream_bf16(const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_stream_mxfp8(const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_tile_mxfp8(const GemmArgs& g, hipStream_t s);

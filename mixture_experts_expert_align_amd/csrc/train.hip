@@ -427,31 +427,37 @@ __global__ void __launch_bounds__(WgradTile::NT, 2) train_wgrad_kernel(TrainArgs
 
 }  // namespace train
 
-// The forward on the inference tile kernel (rows layout: 256 rows of x by
-// 256 output features per tile, both operands loaded straight into LDS) when
-// N is a multiple of 256.
-static bool forward_on_tiles(const TrainArgs& t) { return t.mode == kTrainForward && t.N % 256 == 0; }
+// Forward and dgrad on the inference tile kernel (rows layout: 256 rows of
+// x or dy by 256 output features per tile, both operands loaded straight
+// into LDS; for dgrad W[e] is read transposed from LDS) when the output
+// width (N for the forward, K for dgrad) is a multiple of 256.
+static bool rows_on_tiles(const TrainArgs& t) {
+  return (t.mode == kTrainForward && t.N % 256 == 0) || (t.mode == kTrainDgrad && t.K % 256 == 0);
+}
 
-static hipError_t launch_forward_tiles(const TrainArgs& t, hipStream_t s) {
+static hipError_t launch_rows_tiles(const TrainArgs& t, hipStream_t s) {
+  const bool fwd = t.mode == kTrainForward;
+  const int nc = fwd ? t.K : t.N;      // contraction
+  const int nout = fwd ? t.N : t.K;    // output features
   GemmArgs g = {};
   g.epi = kEpiDown;
   g.rows.layout = 2;
-  g.act = t.x;
-  g.act_ld = t.K;
-  g.act_bytes = t.R * t.K * 2;
+  g.act = fwd ? t.x : t.dy;
+  g.act_ld = nc;
+  g.act_bytes = t.R * nc * 2;
   g.w = t.w;
   g.w_expert_stride = (int64_t)t.N * t.K;
-  g.kdim = t.K;
-  g.nfeat = t.N;
+  g.kdim = nc;
+  g.nfeat = nout;
   g.E = t.E;
   g.out = t.out;
-  g.out_ld = t.N;
-  return launch_tile_rows_bf16(g, t.offsets, t.R, s);
+  g.out_ld = nout;
+  return launch_tile_rows_bf16(g, t.offsets, t.R, !fwd, s);
 }
 
 hipError_t launch_train(const TrainArgs& t, hipStream_t s) {
   using namespace train;
-  if (forward_on_tiles(t)) return launch_forward_tiles(t, s);
+  if (rows_on_tiles(t)) return launch_rows_tiles(t, s);
   if (t.mode == kTrainWgrad) {
     using W = WgradTile;
     hipLaunchKernelGGL(train_wgrad_kernel, dim3((t.N / W::BI) * ((t.K + W::BJ - 1) / W::BJ), t.E),
