@@ -115,33 +115,6 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const TileCoord
   }
 }
 
-// Transposed weight slots (row = contraction index, 256 outputs of 2 bytes
-// a row): 16-byte chunk c of row r sits at chunk c ^ wt_swz(r), so the 4
-// rows one transposing read touches (r .. r+3 from a multiple of 4) put the
-// 16 lanes' 8-byte reads on distinct banks.
-__device__ __forceinline__ int wt_swz(int r) { return (r & 3) << 1; }
-__device__ __forceinline__ int wt_off(int r, int col) { return r * 256 + (((col >> 3) ^ wt_swz(r)) << 3) + (col & 7); }
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-// MFMA row-operand fragment (32 outputs x 8 consecutive contraction values
-// per lane) of a transposed weight slot: outputs j0 .. j0+31, contraction
-// c0 + 8 (lane / 32) .. +7.  ds_read_b64_tr_b16 (gfx950): in each group of
-// 16 lanes, destination lane 4a+b receives element b of the 8 bytes read by
-// lanes a, a+4, a+8 and a+12; source lane L points at row c + L / 4, outputs
-// j + 4 (L % 4) .. +3, so destination lane D holds output j + D at rows
-// c .. c+3.  Two reads give 8 rows.
-__device__ __forceinline__ bf16x8 wt_frag(const uint16_t* slot, int j0, int c0, int lane) {
-  const int gq = lane >> 4, L = lane & 15;
-  const int j = j0 + 16 * (gq & 1) + 4 * (L & 3);
-  const int c = c0 + 8 * (gq >> 1) + (L >> 2);
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(slot + wt_off(c, j)));
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(slot + wt_off(c + 4, j)));
-  const v4i16 v8[2] = {lo, hi};
-  return __builtin_bit_cast(bf16x8, v8);
-}
-
 // Per-lane byte offsets of the slice loads.  Block b of a slot (b = wave +
 // NW * i) holds rows RPB*b .. RPB*b + RPB-1 of its region; lane l lands on
 // row RPB*b + l/CH, physical chunk l%CH, which holds logical chunk

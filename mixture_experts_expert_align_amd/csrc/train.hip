@@ -33,6 +33,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "tile_common.h"
 
 namespace moe {
 namespace train {
@@ -425,6 +426,208 @@ __global__ void __launch_bounds__(WgradTile::NT, 2) train_wgrad_kernel(TrainArgs
   }
 }
 
+
+// wgrad on the split ring (N and K multiples of 256): a workgroup owns the
+// 256 x 256 tile [n0, n0+256) x [k0, k0+256) of dW[e] and runs the
+// contraction over the group's rows in slices of 64.  Both operands hold the
+// contraction along their rows (x[r][k], dy[r][n], r in the group), so both
+// reach LDS in memory order — 64 rows of 256 outputs, 512 bytes a row,
+// chunks XOR-swizzled by row — and both are read transposed
+// (ds_read_b64_tr_b16): the MFMA rows are k (from x), the columns n (from
+// dy), so a lane's accumulators hold 4 consecutive k of one n.  Each
+// operand's buffer descriptor ends at the group's last row, so the rows of a
+// partial last slice read zeros through the range check.  x is requested two
+// slices ahead in 3 slots, dy one ahead in 2, as the inference tiles do with
+// weights and routes (160 KB, one workgroup per CU); every load count is
+// fixed.  The fp32 tile leaves through LDS in two halves of 128 rows of n,
+// each row's 1 KB segment read, added (accumulate) and written by 64
+// threads.  Tiles: per group, blocks of 4 n tiles x 8 k tiles, one block per
+// XCD chunk (the tiles an XCD runs together share 4 column blocks of dy and
+// 8 of x in its L2).
+constexpr int kWgB = 256;              // output tile, both ways
+constexpr int kWgBK = 64;              // contraction rows per slice
+constexpr int kWgSlot = kWgBK * kWgB;  // uint16 elements per slot
+constexpr int kWgNBlk = 4, kWgKBlk = 8;
+static_assert(kWgNBlk * kWgKBlk == tile::kXcdChunk, "a block fills one XCD chunk");
+
+__global__ void __launch_bounds__(1024, 4) train_wgrad_tile_kernel(TrainArgs t, int nnt, int nkt) {
+  constexpr int NW = 16, WM = 4;           // waves: 4 along k x 4 along n, 64 x 64 each
+  constexpr int LW = 2, LX = 2;            // 1 KB loads per wave per slice, each operand
+  constexpr int NSTEP = kWgBK / 16;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[5 * kWgSlot];
+  uint16_t* const wbase = smem;                 // 3 slots of x^T
+  uint16_t* const rbase = smem + 3 * kWgSlot;   // 2 slots of dy^T
+
+  const int64_t b = blockIdx.x;
+  const int64_t kx = b / tile::NXCD;
+  const int64_t chunk = (kx / tile::kXcdChunk) * tile::NXCD + b % tile::NXCD;
+  const int tt = (int)(kx % tile::kXcdChunk);
+  const int nnb = (nnt + kWgNBlk - 1) / kWgNBlk, nkb = (nkt + kWgKBlk - 1) / kWgKBlk;
+  const int64_t cpg = (int64_t)nnb * nkb;
+  const int64_t e = chunk / cpg;
+  if (e >= t.E) return;
+  const int lc = (int)(chunk % cpg);
+  const int ntile = (lc / nkb) * kWgNBlk + tt / kWgKBlk;
+  const int ktile = (lc % nkb) * kWgKBlk + tt % kWgKBlk;
+  if (ntile >= nnt || ktile >= nkt) return;
+  const int n0 = ntile * kWgB, k0 = ktile * kWgB;
+  int a, z;
+  group_rows(t, (int)e, a, z);
+  const int m = z - a;
+  const int nk = (m + kWgBK - 1) / kWgBK;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave / WM, wm = wave % WM;
+  const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(t.x + (int64_t)a * t.K, (int64_t)m * t.K * 2);
+  const __amdgpu_buffer_rsrc_t rr = buffer_rsrc(t.dy + (int64_t)a * t.N, (int64_t)m * t.N * 2);
+  // block i of this wave: slot rows 2 (wave + 16 i) and +1; lane l -> row
+  // 2 (wave + 16 i) + l / 32, physical chunk l % 32 (logical chunk
+  // (l % 32) ^ wt_swz(row))
+  uint32_t ow[LW], orr[LX];
+#pragma unroll
+  for (int i = 0; i < LW; ++i) {
+    const int r = 2 * (wave + NW * i) + lane / 32;
+    const int c = (lane % 32) ^ tile::wt_swz(r);
+    ow[i] = (uint32_t)(((int64_t)r * t.K + k0 + 8 * c) * 2);
+    orr[i] = (uint32_t)(((int64_t)r * t.N + n0 + 8 * c) * 2);
+  }
+  const int wstep = kWgBK * t.K * 2, rstep = kWgBK * t.N * 2;   // bytes per slice
+  auto issue_w = [&](int kt) {
+    uint16_t* slot = wbase + (kt % 3) * kWgSlot;
+#pragma unroll
+    for (int i = 0; i < LW; ++i) lds_load16(wr, slot + (wave + NW * i) * 512, ow[i], kt * wstep);
+    issue_order();
+  };
+  auto issue_r = [&](int kt) {
+    uint16_t* slot = rbase + (kt % 2) * kWgSlot;
+#pragma unroll
+    for (int i = 0; i < LX; ++i) lds_load16(rr, slot + (wave + NW * i) * 512, orr[i], kt * rstep);
+    issue_order();
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  bf16x8 fw[2][2], fx[2][2];
+  auto fload = [&](int fb, int kt, int st) {
+    const uint16_t* ws = wbase + (kt % 3) * kWgSlot;
+    const uint16_t* rs = rbase + (kt % 2) * kWgSlot;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) fw[fb][i] = tile::wt_frag(ws, wn * 64 + 32 * i, 16 * st, lane);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fx[fb][j] = tile::wt_frag(rs, wm * 64 + 32 * j, 16 * st, lane);
+  };
+  auto mma = [&](int fb) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[fb][i], fx[fb][j], acc[i][j], 0, 0, 0);
+  };
+  // 8 LDS reads and 4 MFMAs a step: read, MFMA in pairs, then the reads left
+  auto interleave = [&]() {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  };
+
+  if (nk > 0) {
+    // prologue: x^T 0, dy^T 0 and 1, x^T 1 and 2; wait for slice 0 (the
+    // count leaves only x^T loads outstanding, as in the inference tiles)
+    issue_w(0);
+    issue_r(0);
+    if (nk > 1) { issue_r(1); issue_w(1); }
+    if (nk > 2) issue_w(2);
+    if (nk > 2) wait_vm<2 * LW>();
+    else if (nk > 1) wait_vm<LW>();
+    else wait_vm<0>();
+    lds_barrier();
+    // slice kt; MODE 2: slices kt+2 and kt+3 exist, 1: only kt+2, 0: only
+    // kt+1, -1: kt is the last
+    auto slice = [&](int kt, auto mode) {
+      constexpr int MODE = decltype(mode)::value;
+#pragma unroll
+      for (int st = 0; st + 1 < NSTEP; ++st) {
+        fload((st + 1) & 1, kt, st + 1);
+        mma(st & 1);
+        interleave();
+      }
+      if (MODE >= 0) {
+        if (MODE >= 1) wait_vm<LW>();   // slice kt+1 is in; x^T of kt+2 may fly
+        else wait_vm<0>();
+        lds_barrier();                  // nobody reads slice kt's slots any more
+        if (MODE >= 1) issue_r(kt + 2);
+        if (MODE >= 2) issue_w(kt + 3);
+        fload(0, kt + 1, 0);
+        mma((NSTEP - 1) & 1);
+        interleave();
+      } else {
+        mma((NSTEP - 1) & 1);
+      }
+    };
+    fload(0, 0, 0);
+    int kt = 0;
+    for (; kt + 3 < nk; ++kt) slice(kt, std::integral_constant<int, 2>());
+    if (kt + 2 < nk) slice(kt++, std::integral_constant<int, 1>());
+    if (kt + 1 < nk) slice(kt++, std::integral_constant<int, 0>());
+    slice(kt, std::integral_constant<int, -1>());
+    wait_vm<0>();
+    lds_barrier();
+  }
+
+  // epilogue: acc[i][j][4q + h]: k = wn 64 + 32 i + 8 q + 4 (lane / 32) + h,
+  // n = wm 64 + 32 j + lane % 32.  Half hf stages the n rows [128 hf,
+  // 128 hf + 128) as fp32 rows of 256 k, 16-byte chunk c of row r at
+  // c ^ (r & 63).
+  float* stage = reinterpret_cast<float*>(smem);
+  float* out = static_cast<float*>(t.out) + (e * t.N + n0) * (int64_t)t.K + k0;
+  const int c = threadIdx.x % 64;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    if (wm / 2 == hf) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = (wm - 2 * hf) * 64 + 32 * j + (lane & 31);
+            const int kc = (wn * 64 + 32 * i + 8 * q + 4 * (lane >> 5)) / 4;
+            *reinterpret_cast<f32x4*>(stage + r * 256 + ((kc ^ (r & 63)) << 2)) =
+                (f32x4){acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          }
+    }
+    lds_barrier();
+    f32x4 prev[8];
+    if (t.accumulate) {
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const int r = threadIdx.x / 64 + 16 * p;
+        prev[p] = *reinterpret_cast<const f32x4*>(out + (int64_t)(128 * hf + r) * t.K + 4 * c);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int r = threadIdx.x / 64 + 16 * p;
+      f32x4 v = *reinterpret_cast<const f32x4*>(stage + r * 256 + ((c ^ (r & 63)) << 2));
+      if (t.accumulate) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) v[h] = prev[p][h] + v[h];
+      }
+      *reinterpret_cast<f32x4*>(out + (int64_t)(128 * hf + r) * t.K + 4 * c) = v;
+    }
+    lds_barrier();   // the half's reads are done before the next half is staged
+  }
+}
+
 }  // namespace train
 
 // Forward and dgrad on the inference tile kernel (rows layout: 256 rows of
@@ -458,6 +661,14 @@ static hipError_t launch_rows_tiles(const TrainArgs& t, hipStream_t s) {
 hipError_t launch_train(const TrainArgs& t, hipStream_t s) {
   using namespace train;
   if (rows_on_tiles(t)) return launch_rows_tiles(t, s);
+  if (t.mode == kTrainWgrad && t.N % kWgB == 0 && t.K % kWgB == 0) {
+    const int nnt = t.N / kWgB, nkt = t.K / kWgB;
+    const int64_t cpg = (int64_t)((nnt + kWgNBlk - 1) / kWgNBlk) * ((nkt + kWgKBlk - 1) / kWgKBlk);
+    const int64_t nchunk = (t.E * cpg + tile::NXCD - 1) / tile::NXCD * tile::NXCD;
+    hipLaunchKernelGGL(train_wgrad_tile_kernel, dim3((unsigned)(nchunk * tile::kXcdChunk)), dim3(1024), 0, s, t, nnt,
+                       nkt);
+    return hipGetLastError();
+  }
   if (t.mode == kTrainWgrad) {
     using W = WgradTile;
     hipLaunchKernelGGL(train_wgrad_kernel, dim3((t.N / W::BI) * ((t.K + W::BJ - 1) / W::BJ), t.E),
