@@ -156,7 +156,7 @@ DOMINANT_KERNEL = {"tiny": FUSED_KERNELS, "decode": ["gemm_stream_bf16_kernel<0,
                    "mxfp8_stream": ["quantize_gather_kernel", "gemm_stream_mxfp8_kernel<0,"],
                    "batched": ["gemm_tile_split_bf16_kernel<0,", "gemm_tile_split_bf16_kernel<1,"],
                    "decode_fused": FUSED_KERNELS, "tiny_fused": FUSED_KERNELS,
-                   "train_gu": ["train_wgrad_kernel"], "train_dn": ["train_wgrad_kernel"]}
+                   "train_gu": ["train_wgrad_tile_kernel"], "train_dn": ["train_wgrad_tile_kernel"]}
 KERNEL_FILES = {"tiny": FUSED_FILES, "decode": ["gemm_stream.hip", "stream_bf16.h"],
                 "prefill": ["gemm_tile.hip", "tile_common.h"],
                 "mxfp8": ["reduce_codec.hip", "gemm_mxfp8_tile.hip", "tile_common.h"],
