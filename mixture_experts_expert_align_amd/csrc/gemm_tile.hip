@@ -411,9 +411,31 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_split_bf16_kernel
 constexpr int kRowBlock = 4, kColBlock = 8;
 static_assert(kRowBlock * kColBlock == kXcdChunk, "a block fills one XCD chunk");
 
-template <int BM, int BN, int BK, int WN, int WM, int OCC, bool WT>
-__global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_rows_kernel(GemmArgs g, const int32_t* offsets,
-                                                                          int E, int64_t R, int64_t nrt,
+// The groups of rows a rows-layout launch multiplies: group e is rows
+// [offsets[e], offsets[e+1]) of the R rows of the activation matrix
+// (clamped to [0, R]; the groups follow each other).
+struct RowGroups {
+  const int32_t* offsets;
+  int32_t E;
+  int64_t R;
+  __device__ int64_t clampr(int64_t v) const { return min<int64_t>(max<int64_t>(v, 0), R); }
+  __device__ int64_t start(int e) const { return clampr(offsets[e]); }
+  __device__ int64_t end(int e) const { return max(clampr(offsets[e + 1]), start(e)); }
+  // rows of later groups begin at or after this
+  __device__ int64_t next_start(int e) const { return end(e); }
+  // the first group with rows past r0
+  __device__ int first(int64_t r0) const {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (end(mid) > r0) hi = mid; else lo = mid + 1;
+    }
+    return lo;
+  }
+};
+
+template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, bool WT>
+__global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_rows_kernel(GemmArgs g, RowGroups grp, int64_t nrt,
                                                                           int64_t nct) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[SplitRing<BM, BN, BK>::Elems];
   // block b runs on XCD b % 8 as that XCD's (b / 8)-th block: chunk
@@ -426,42 +448,52 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_rows_kernel(GemmA
   const int64_t rt = (chunk / ncb) * kRowBlock + t / kColBlock;
   const int64_t ct = (chunk % ncb) * kColBlock + t % kColBlock;
   if (rt >= nrt || ct >= nct) return;
-  const int64_t r0 = rt * BM;
-  auto off = [&](int e) { return min<int64_t>(max<int64_t>(offsets[e], 0), R); };
-  // first group with rows past r0
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (off(mid + 1) > r0) hi = mid; else lo = mid + 1;
-  }
+  const int64_t r0 = rt * BM, r1 = min<int64_t>(r0 + BM, grp.R);
+  int e = grp.first(r0);
   TileCoord tc;
   tc.col0 = (int)ct * BN;
   tc.row0 = r0;
-  {
-    // the common case, a tile inside one group: one pass, outside the loop
-    // (inside it the compiler keeps more values live and spills)
-    const int64_t a = off(lo), z = max(off(lo + 1), a);
-    if (a <= r0 && z >= min<int64_t>(r0 + BM, R)) {
-      tc.expert = lo;
-      tc.mlo = 0;
-      tc.nvalid = (int)(min<int64_t>(r0 + BM, R) - r0);
-      split_tile<kEpiDown, BM, BN, BK, WN, WM, WT>(g, tc, smem);
-      return;
-    }
+  if (grp.next_start(e) >= r1 || e + 1 >= grp.E) {
+    // the common case, one group at most in the tile: one pass, outside the
+    // loop (inside it the compiler keeps more values live and spills)
+    const int64_t s0 = max(grp.start(e), r0), s1 = min(grp.end(e), r1);
+    if (s1 <= s0) return;   // no row of any group
+    tc.expert = e;
+    tc.mlo = (int)(s0 - r0);
+    tc.nvalid = (int)(s1 - r0);
+    split_tile<EPI, BM, BN, BK, WN, WM, WT>(g, tc, smem);
+    return;
   }
   bool first = true;
-  for (int e = lo; e < E; ++e) {
-    const int64_t a = off(e), z = max(off(e + 1), a);
-    if (a >= r0 + BM) break;
-    const int64_t s0 = max(a, r0), s1 = min(z, r0 + BM);
+  for (; e < grp.E; ++e) {
+    const int64_t a = grp.start(e), z = grp.end(e);
+    if (a >= r1) break;
+    const int64_t s0 = max(a, r0), s1 = min(z, r1);
     if (s1 <= s0) continue;
     if (!first) lds_barrier();   // the previous pass's epilogue has read its LDS
     first = false;
     tc.expert = e;
     tc.mlo = (int)(s0 - r0);
     tc.nvalid = (int)(s1 - r0);
-    split_tile<kEpiDown, BM, BN, BK, WN, WM, WT>(g, tc, smem);
+    split_tile<EPI, BM, BN, BK, WN, WM, WT>(g, tc, smem);
   }
+}
+
+// 256 rows x 256 weight rows per tile (W1: 128 features of gate and up)
+constexpr int kRowsBM = 256, kRowsBN = 256;
+
+template <int EPI, bool WT>
+hipError_t launch_rows(const GemmArgs& g, const RowGroups& grp, hipStream_t s) {
+  constexpr int BM = kRowsBM, BN = kRowsBN;
+  const int fpt = EPI == kEpiGateUp ? BN / 2 : BN;   // output features per tile
+  if (g.rows.layout != 2 || g.nfeat % fpt || g.kdim % 64) return hipErrorInvalidValue;
+  if (grp.R <= 0) return hipSuccess;
+  const int64_t nrt = (grp.R + BM - 1) / BM, nct = g.nfeat / fpt;
+  const int64_t nchunk = (nrt + kRowBlock - 1) / kRowBlock * ((nct + kColBlock - 1) / kColBlock);
+  const int64_t grid = (nchunk + NXCD - 1) / NXCD * NXCD * kXcdChunk;
+  hipLaunchKernelGGL((gemm_tile_rows_kernel<EPI, BM, BN, 64, 4, 4, 4, WT>), dim3((unsigned)grid), dim3(1024), 0, s,
+                     g, grp, nrt, nct);
+  return hipGetLastError();
 }
 
 template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, int ORDER>
@@ -495,19 +527,9 @@ hipError_t launch_layout(const GemmArgs& g, hipStream_t s) {
 // 256 rows x 256 features, the contiguous tile shape
 hipError_t launch_tile_rows_bf16(const GemmArgs& g, const int32_t* offsets, int64_t R, bool wt, hipStream_t s) {
   using namespace tile;
-  constexpr int BM = 256, BN = 256;
-  if (g.rows.layout != 2 || g.epi != kEpiDown || g.nfeat % BN || g.kdim % 64) return hipErrorInvalidValue;
-  if (R <= 0) return hipSuccess;
-  const int64_t nrt = (R + BM - 1) / BM, nct = g.nfeat / BN;
-  const int64_t nchunk = (nrt + kRowBlock - 1) / kRowBlock * ((nct + kColBlock - 1) / kColBlock);
-  const int64_t grid = (nchunk + NXCD - 1) / NXCD * NXCD * kXcdChunk;
-  if (wt)
-    hipLaunchKernelGGL((gemm_tile_rows_kernel<BM, BN, 64, 4, 4, 4, true>), dim3((unsigned)grid), dim3(1024), 0, s, g,
-                       offsets, g.E, R, nrt, nct);
-  else
-    hipLaunchKernelGGL((gemm_tile_rows_kernel<BM, BN, 64, 4, 4, 4, false>), dim3((unsigned)grid), dim3(1024), 0, s, g,
-                       offsets, g.E, R, nrt, nct);
-  return hipGetLastError();
+  if (g.epi != kEpiDown) return hipErrorInvalidValue;
+  const RowGroups grp{offsets, g.E, R};
+  return wt ? launch_rows<kEpiDown, true>(g, grp, s) : launch_rows<kEpiDown, false>(g, grp, s);
 }
 
 hipError_t launch_gemm_tile_bf16(const GemmArgs& g, hipStream_t s) {
