@@ -324,8 +324,9 @@ int64_t moe_naive_batched_ws_bytes(const moe_plan* plan, int64_t n_out);
  * [E]; row_token: device int32 [E, max_tokens] (valid rows in [0, n_out));
  * row_weight: device float32 [E, max_tokens]; out: device bf16 [n_out, K];
  * ws: device, moe_naive_batched_ws_bytes(plan, n_out).  Invalid rows' map
- * entries are never read; valid rows mapping outside [0, n_out) are skipped
- * and counted in the first int32 of ws (written by every call). */
+ * entries are never read; a valid row mapping to -1 is skipped; valid rows
+ * mapping elsewhere outside [0, n_out) are skipped and counted in the first
+ * int32 of ws (written by every call). */
 int moe_topk_reduce_naive_batched(const moe_plan* plan, const void* y,
                                   const int32_t* expert_num_tokens, const int32_t* row_token,
                                   const float* row_weight, int64_t n_out, void* out, void* ws,

@@ -182,6 +182,16 @@ hipError_t launch_reduce_contiguous(const uint16_t* y, const int32_t* ids, const
                                     int32_t topk, int64_t K, int32_t E, int32_t* sync_zero,
                                     int64_t sync_lines, hipStream_t s);
 // out[t] = sum over CSR list of t (ascending) of w[row] * y[row]
+// out[t] = sum over the valid rows (e, r) of the batched format (r <
+// min(counts[e], mt)) with row_token == t, ascending (e, r), of w * y, one
+// workgroup per token scanning the map itself (K <= 8192, E <=
+// kReduceBatchedMaxE, whose counts it keeps in LDS: 64 KB of row list + the
+// counts fit two workgroups per CU); status[0] = valid rows mapping outside
+// {-1} U [0, n_out)
+constexpr int kReduceBatchedMaxE = 4080;
+hipError_t launch_reduce_batched(const uint16_t* y, const int32_t* counts, const int32_t* row_token,
+                                 const float* w, int32_t mt, int32_t E, uint16_t* out, int64_t n_out,
+                                 int64_t K, int32_t* status, hipStream_t s);
 hipError_t launch_reduce_csr(const uint16_t* y, const float* w, const int32_t* offsets,
                              const int32_t* rows, uint16_t* out, int64_t n_out, int64_t K,
                              hipStream_t s);

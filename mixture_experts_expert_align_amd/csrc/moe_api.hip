@@ -582,6 +582,14 @@ int moe_topk_reduce_naive_batched(const moe_plan* plan, const void* y,
       !aligned4(row_weight) || !aligned16(out) || !aligned16(ws))
     return MOE_EINVAL;
   const int64_t R = P.E * P.max_tokens;
+  hipStream_t s = (hipStream_t)stream;
+  if (P.K <= 8192 && P.E <= kReduceBatchedMaxE) {
+    // one launch: each token's workgroup finds its rows itself
+    const hipError_t e = launch_reduce_batched(static_cast<const uint16_t*>(y), expert_num_tokens, row_token,
+                                               row_weight, (int32_t)P.max_tokens, (int32_t)P.E,
+                                               static_cast<uint16_t*>(out), n_out, P.K, at<int32_t>(ws, 0), s);
+    return e == hipSuccess ? MOE_OK : MOE_EHIP;
+  }
   AlignLayout L = batched_reduce_layout(plan, n_out);
   AlignArgs a{};
   a.keys = row_token;
@@ -603,7 +611,6 @@ int moe_topk_reduce_naive_batched(const moe_plan* plan, const void* y,
   a.max_active = n_out < R ? n_out : R;
   a.sentinel = (int32_t)R;
   a.nblocks = (int32_t)align_nblocks(R);
-  hipStream_t s = (hipStream_t)stream;
   if (launch_align(a, s) != hipSuccess) return MOE_EHIP;
   hipError_t e = launch_reduce_csr(static_cast<const uint16_t*>(y), row_weight, a.offsets, a.sorted,
                                    static_cast<uint16_t*>(out), n_out, P.K, s);

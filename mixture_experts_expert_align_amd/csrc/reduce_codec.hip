@@ -233,6 +233,141 @@ inline unsigned nblocks(int64_t n) { return (unsigned)((n + NT - 1) / NT); }
 
 // Chunks per thread of the reduces: as many (up to kChunks) as keep about
 // 2048 workgroups (eight per CU) in the grid.
+
+// TopKWeightAndReduceNaiveBatched in one launch: workgroup t owns output
+// token t and all of its columns (K <= 8 * kRT: one 8-column chunk per
+// thread).  It walks the E * mt (expert, row) entries in ascending order,
+// kScanChunk at a time, each thread 16 consecutive entries in runs of 4: a
+// run of four valid rows of one expert (r < count[e]) is one 16-byte map load
+// (all of a thread's loads issued before any is used), a run past the count
+// reads nothing, and a run at a count or slab edge is read entry by entry, so
+// rows past the count are never read.  A workgroup-wide exclusive scan of the
+// per-thread match counts places the rows whose map entry is t in LDS in
+// ascending order; they are added into the fp32 accumulators, kBatch rows'
+// loads issued together, one multiply-add per row in order — the order and
+// the arithmetic of the list-based reduce, so the same bits.  Workgroup 0
+// also counts the valid rows whose map entry lies outside {-1} U [0, n_out)
+// and writes the count to status.
+constexpr int kRT = 1024;                  // threads of the one-launch reduce
+constexpr int kPerThread = 16;
+constexpr int kScanChunk = kPerThread * kRT;   // 64 KB of LDS list
+
+// exclusive prefix sum of v over the kRT threads; total gets the sum
+__device__ __forceinline__ int block_exclusive_scan(int v, int& total, int* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  int before = 0, sum = 0;
+#pragma unroll
+  for (int w = 0; w < kRT / 64; ++w) {
+    const int tw = sh[w];
+    if (w < wave) before += tw;
+    sum += tw;
+  }
+  total = sum;
+  __syncthreads();   // sh is free again
+  return before + x - v;
+}
+
+__global__ void __launch_bounds__(kRT) reduce_batched_kernel(const uint16_t* __restrict__ y,
+                                                             const int32_t* __restrict__ counts,
+                                                             const int32_t* __restrict__ row_token,
+                                                             const float* __restrict__ w, int mt, int E,
+                                                             uint16_t* __restrict__ out, int n_out, int K,
+                                                             int32_t* __restrict__ status, int vec_map) {
+  __shared__ int32_t list[kScanChunk];
+  __shared__ int32_t sh[kRT / 64];
+  __shared__ int32_t scnt[kReduceBatchedMaxE];   // valid rows per expert, min(counts[e], mt)
+  for (int e = threadIdx.x; e < E; e += kRT) scnt[e] = min(max(counts[e], 0), mt);
+  __syncthreads();
+  const int t = blockIdx.x;
+  const int K8 = K / 8;
+  const uint32_t R = (uint32_t)E * (uint32_t)mt;   // < 2^31
+  const int c = threadIdx.x;                       // this thread's 8-column chunk
+  float acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+  int invalid = 0;
+  constexpr int NR = kPerThread / 4;
+  for (uint32_t base = 0; base < R; base += kScanChunk) {
+    const uint32_t i0 = base + (uint32_t)threadIdx.x * kPerThread;
+    uint32_t e = i0 / (uint32_t)mt, r = i0 - e * (uint32_t)mt;
+    i32x4 v[NR];
+    uint32_t full = 0, edge = 0;
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      v[j] = (i32x4){-1, -1, -1, -1};
+      const uint32_t i = i0 + 4 * j;
+      if (i < R) {
+        const uint32_t cnt = (uint32_t)scnt[e];
+        if (vec_map && r + 4 <= cnt) {
+          v[j] = *reinterpret_cast<const i32x4*>(row_token + i);
+          full |= 1u << j;
+        } else if (!(r >= cnt && r + 4 <= (uint32_t)mt)) {
+          edge |= 1u << j;
+        }
+      }
+      r += 4;
+      while (r >= (uint32_t)mt) { r -= mt; ++e; }
+    }
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      if (!(edge >> j & 1)) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t iq = i0 + 4 * j + q;
+        const uint32_t eq = iq / (uint32_t)mt, rq = iq - eq * (uint32_t)mt;
+        if (iq < R && rq < (uint32_t)scnt[eq]) v[j][q] = row_token[iq];   // -1 stays: not a row
+      }
+    }
+    uint32_t mask = 0;
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      if (!((full | edge) >> j & 1)) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int tok = v[j][q];
+        if (tok == t) mask |= 1u << (4 * j + q);
+        if (t == 0 && tok != -1 && (tok < 0 || tok >= n_out)) ++invalid;
+      }
+    }
+    int total;
+    int pos = block_exclusive_scan(__builtin_popcount(mask), total, sh);
+    for (uint32_t m = mask; m; m &= m - 1) list[pos++] = (int32_t)(i0 + __builtin_ctz(m));
+    __syncthreads();
+    if (c < K8) {
+      for (int j0 = 0; j0 < total; j0 += kBatch) {
+        int64_t rr[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) rr[q] = j0 + q < total ? list[j0 + q] : -1;
+        float wt[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) wt[q] = rr[q] >= 0 ? w[rr[q]] : 0.f;
+        i32x4 yv[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q)
+          if (rr[q] >= 0) yv[q] = *reinterpret_cast<const i32x4*>(y + rr[q] * K + 8 * c);
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q)
+          if (rr[q] >= 0) fma8(acc, wt[q], yv[q]);
+      }
+    }
+    __syncthreads();   // the list is read before the next chunk writes it
+  }
+  if (c < K8) *reinterpret_cast<i32x4*>(out + (int64_t)t * K + 8 * c) = pack8(acc);
+  if (t == 0) {
+    int tot;
+    block_exclusive_scan(invalid, tot, sh);
+    if (threadIdx.x == 0) status[0] = tot;
+  }
+}
+
 inline int reduce_cpt(int64_t rows, int64_t K8) {
   int cpt = 1;
   while (cpt < kChunks && rows * ((K8 + NT * 2 * cpt - 1) / (NT * 2 * cpt)) >= 2048) cpt *= 2;
@@ -260,6 +395,19 @@ hipError_t launch_reduce_csr(const uint16_t* y, const float* w, const int32_t* o
   const int cpt = reduce_cpt(n_out, K / 8);
   const dim3 grid((unsigned)n_out, (unsigned)((K / 8 + NT * cpt - 1) / (NT * cpt)));
   hipLaunchKernelGGL(reduce_csr_kernel, grid, dim3(NT), 0, s, y, w, offsets, rows, out, n_out, K, cpt);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_batched(const uint16_t* y, const int32_t* counts, const int32_t* row_token,
+                                 const float* w, int32_t mt, int32_t E, uint16_t* out, int64_t n_out,
+                                 int64_t K, int32_t* status, hipStream_t s) {
+  if (n_out == 0) return hipSuccess;
+  if (K / 8 > kRT || E > kReduceBatchedMaxE || (int64_t)E * mt >= (1ll << 31) || n_out >= (1ll << 31))
+    return hipErrorInvalidValue;
+  // the map is read 16 bytes at a time where that is aligned
+  const int vec_map = (reinterpret_cast<uintptr_t>(row_token) & 15) == 0;
+  hipLaunchKernelGGL(reduce_batched_kernel, dim3((unsigned)n_out), dim3(kRT), 0, s, y, counts, row_token, w, mt, E,
+                     out, (int)n_out, (int)K, status, vec_map);
   return hipGetLastError();
 }
 

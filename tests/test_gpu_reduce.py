@@ -125,8 +125,13 @@ def test_reduce_naive_batched(which):
         assert np.all(out[torch.from_numpy(np.flatnonzero(~hit)).cuda()].view(torch.int16).cpu().numpy() == 0)
 
 
-def test_reduce_naive_batched_out_of_range_rows_skipped():
-    E, T, K, n_out = 4, 40, 128, 16
+@pytest.mark.parametrize("K", [128, 8448], ids=["one_launch", "wide_rows_list_path"])
+def test_reduce_naive_batched_out_of_range_rows_skipped(K):
+    """Valid rows whose token is outside [0, n_out) are skipped and counted
+    (id -1 is a skipped row, not counted).  K = 8448 takes the path that
+    builds the per-token row lists with the align kernels (rows wider than
+    8192 columns); K = 128 the one-launch reduce."""
+    E, T, n_out = 4, 40, 16
     counts = np.array([40, 3, 0, 17], np.int32)
     rng = np.random.default_rng(2)
     tok = rng.integers(0, n_out, (E, T)).astype(np.int32)
