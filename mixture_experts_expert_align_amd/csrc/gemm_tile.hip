@@ -138,13 +138,13 @@ __device__ __forceinline__ void load_offsets(const GemmArgs& g, const TileCoord&
     // weights stored with the output index contiguous: the slot holds BK
     // contraction rows of BN outputs; block b = rows 2b, 2b+1 (BN = 256:
     // 512 bytes a row), lane l -> row 2b + l / 32, physical chunk l % 32,
-    // holding logical chunk (l % 32) ^ wt_swz(row); the slice's first row
+    // holding logical chunk wt_logical(row, l % 32); the slice's first row
     // comes in through the instruction offset
     static_assert(!WT || BN * 2 == 512, "transposed weight rows of 512 bytes");
 #pragma unroll
     for (int i = 0; i < LW; ++i) {
       const int r = 2 * (wave + NW * i) + lane / 32;
-      const int c = (lane % 32) ^ wt_swz(r);
+      const int c = wt_logical(r, lane % 32);
       ow[i] = (uint32_t)(((int64_t)r * g.nfeat + tc.col0 + 8 * c) * 2);
     }
   } else

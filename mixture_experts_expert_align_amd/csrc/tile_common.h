@@ -24,11 +24,20 @@ __device__ __forceinline__ int lds_off(int row, int c) {
 }
 
 // Transposed operand slots (row = contraction index, 256 outputs of 2 bytes
-// a row): 16-byte chunk c of row r sits at chunk c ^ wt_swz(r), so the 4
-// rows one transposing read touches (r .. r+3 from a multiple of 4) put the
-// 16 lanes' 8-byte reads on distinct banks.
-__device__ __forceinline__ int wt_swz(int r) { return (r & 3) << 1; }
-__device__ __forceinline__ int wt_off(int r, int col) { return r * 256 + (((col >> 3) ^ wt_swz(r)) << 3) + (col & 7); }
+// a row): logical 16-byte chunk c of row r sits at physical chunk
+// wt_phys(r, c) = c ^ 2 (r & 3) ^ 8 bit1(c).  The first term puts the 4 rows
+// one transposing read touches (r .. r+3 from a multiple of 4) on distinct
+// chunks, so a group of 16 lanes covers 32 banks once; the second puts the
+// lane groups 0-15 and 16-31, whose outputs differ in bit 1 of the chunk, on
+// opposite halves of the 64 banks (with the first term alone all four groups
+// met in one half: counters showed more bank-conflict cycles than LDS-active
+// ones).  It is a bijection on the chunks of a row; wt_logical inverts it.
+__device__ __forceinline__ int wt_phys(int r, int c) { return c ^ ((r & 3) << 1) ^ (((c >> 1) & 1) << 3); }
+__device__ __forceinline__ int wt_logical(int r, int p) {
+  const int u = p ^ ((r & 3) << 1);
+  return u ^ (((u >> 1) & 1) << 3);
+}
+__device__ __forceinline__ int wt_off(int r, int col) { return r * 256 + (wt_phys(r, col >> 3) << 3) + (col & 7); }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;

@@ -483,12 +483,12 @@ __global__ void __launch_bounds__(1024, 4) train_wgrad_tile_kernel(TrainArgs t, 
   const __amdgpu_buffer_rsrc_t rr = buffer_rsrc(t.dy + (int64_t)a * t.N, (int64_t)m * t.N * 2);
   // block i of this wave: slot rows 2 (wave + 16 i) and +1; lane l -> row
   // 2 (wave + 16 i) + l / 32, physical chunk l % 32 (logical chunk
-  // (l % 32) ^ wt_swz(row))
+  // wt_logical(row, l % 32))
   uint32_t ow[LW], orr[LX];
 #pragma unroll
   for (int i = 0; i < LW; ++i) {
     const int r = 2 * (wave + NW * i) + lane / 32;
-    const int c = (lane % 32) ^ tile::wt_swz(r);
+    const int c = tile::wt_logical(r, lane % 32);
     ow[i] = (uint32_t)(((int64_t)r * t.K + k0 + 8 * c) * 2);
     orr[i] = (uint32_t)(((int64_t)r * t.N + n0 + 8 * c) * 2);
   }
