@@ -135,3 +135,44 @@ def test_two_streams():
     torch.cuda.synchronize()
     for (c, plan, _, _, out, ref) in runs:
         assert torch.equal(bits(out), ref), f"{c.cfg.name}: two-stream output differs"
+
+
+@pytest.mark.parametrize("E,N,K,rows", [(9, 768, 256, 2600), (8, 256, 384, 1000)],
+                         ids=["tiles", "older_kernels"])
+def test_graph_training(E, N, K, rows):
+    """The training grouped GEMMs (forward, dgrad, wgrad with the fp32
+    accumulate) captured in one graph and replayed: every replay equals the
+    eager calls bit for bit, the accumulate included (main_grad is restored
+    by a device copy inside the graph before each accumulate).  N, K
+    multiples of 256 take the split-ring tiles; K = 384 the older kernels."""
+    cfg = mi.TrainConfig(f"train_graph_e{E}", 25, E=E, N=N, K=K, rows=rows, balance="zipf")
+    ti = mi.make_train_inputs(cfg, device="cuda")
+    off = torch.from_numpy(ti.offsets).cuda()
+    R = int(ti.offsets[-1])
+
+    def buffers():
+        return (torch.empty((R, N), dtype=torch.bfloat16, device="cuda"),
+                torch.empty((R, K), dtype=torch.bfloat16, device="cuda"),
+                torch.empty((E, N, K), dtype=torch.float32, device="cuda"))
+
+    def call(y, dx, acc):
+        acc.copy_(ti.main_grad)
+        moe.moe_grouped_forward(ti.x, ti.w, off, y)
+        moe.moe_grouped_dgrad(ti.dy, ti.w, off, dx)
+        moe.moe_grouped_wgrad(ti.dy, ti.x, off, acc, accumulate=True)
+
+    rb = buffers()
+    call(*rb)
+    torch.cuda.synchronize()
+    ref = [rb[0].view(torch.int16).clone(), rb[1].view(torch.int16).clone(), rb[2].view(torch.int32).clone()]
+    gb = buffers()
+    g = capture(lambda: call(*gb))
+    for i in range(REPLAYS):
+        for t in gb:
+            t.fill_(float("nan"))
+        call(*rb)                      # eager work between the replays
+        g.replay()
+        torch.cuda.synchronize()
+        got = [gb[0].view(torch.int16), gb[1].view(torch.int16), gb[2].view(torch.int32)]
+        for name, a, b in zip(("y", "dx", "main_grad"), got, ref):
+            assert torch.equal(a, b), f"training {name}: replay {i} differs from the eager calls"
