@@ -306,8 +306,15 @@ def test_all_slots_skipped():
     assert np.all(out.view(torch.int16).cpu().numpy() == 0)
 
 
-def test_batched_scaled():
-    cfg = mi.config(4).scaled(E=8, max_tokens=100, K=256, I=128, M=64, slot_pool=400)
+# (K, I): both GEMMs on the weight-streaming kernel with a 2-step contraction
+# (no full 3-step round) / W1 4 steps and W2 3 / W1 5 steps with W2 on the
+# LDS-tiled kernel (K % 256 != 0) / both on the LDS-tiled kernel (I % 128 != 0)
+BATCHED_SHAPES = [(256, 128), (512, 384), (640, 256), (384, 192)]
+
+
+@pytest.mark.parametrize("K,I", BATCHED_SHAPES, ids=[f"k{k}_i{i}" for k, i in BATCHED_SHAPES])
+def test_batched_scaled(K, I):
+    cfg = mi.config(4).scaled(E=8, max_tokens=100, K=K, I=I, M=64, slot_pool=400)
     c = make_case(cfg)
     junk = torch.arange(cfg.max_tokens, device="cuda")[None, :] >= c.counts[:, None]
     c.inp.a[junk] = float("nan")                   # rows past the counts are never read
