@@ -268,12 +268,8 @@ __global__ void __launch_bounds__(64 * kMxWaves, 4) gemm_stream_mxfp8_kernel(Gem
       m = fmaxf(m, __shfl_xor(m, 32));
       const uint32_t sc = mx_scale_code(m);
       const float inv = mx_inv_scale(sc);
-      uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        w0 |= e4m3_encode(z[r] * inv) << (8 * r);
-        w1 |= e4m3_encode(z[4 + r] * inv) << (8 * r);
-      }
+      const uint32_t w0 = e4m3_pack4(z[0] * inv, z[1] * inv, z[2] * inv, z[3] * inv);
+      const uint32_t w1 = e4m3_pack4(z[4] * inv, z[5] * inv, z[6] * inv, z[7] * inv);
       const int t = tg * kMxTok + 16 * c + l16;
       if (t < cnt) {
         const int64_t pos = pos0 + t;

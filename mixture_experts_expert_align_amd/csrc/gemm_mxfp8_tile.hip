@@ -113,11 +113,8 @@ __device__ __forceinline__ void mx_epilogue(const GemmArgs& g, const TileCoord& 
       const float inv = mx_inv_scale(sc);
       uint32_t w[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        w[i] = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w[i] |= e4m3_encode(z[4 * i + j] * inv) << (8 * j);
-      }
+      for (int i = 0; i < 8; ++i)
+        w[i] = e4m3_pack4(z[4 * i] * inv, z[4 * i + 1] * inv, z[4 * i + 2] * inv, z[4 * i + 3] * inv);
       const int64_t pos = tc.row0 + m;
       const int f = tc.col0 / 2 + 32 * b;   // first feature of the block
       uint8_t* o = static_cast<uint8_t*>(g.out) + pos * g.out_ld + f;

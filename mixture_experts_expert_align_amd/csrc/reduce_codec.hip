@@ -153,10 +153,8 @@ __device__ __forceinline__ void quantize_block(const float* v, uint8_t* codes, u
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint32_t wd = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) wd |= e4m3_encode(v[16 * h + 4 * i + b] * inv) << (8 * b);
-      o[h][i] = (int)wd;
+      const float* q = v + 16 * h + 4 * i;
+      o[h][i] = (int)e4m3_pack4(q[0] * inv, q[1] * inv, q[2] * inv, q[3] * inv);
     }
   reinterpret_cast<i32x4*>(codes)[0] = o[0];
   reinterpret_cast<i32x4*>(codes)[1] = o[1];
@@ -195,30 +193,47 @@ __global__ void __launch_bounds__(NT) quantize_kernel(const void* __restrict__ x
   quantize_block(v, codes + r * cols + b * 32, scales + r * nb + b);
 }
 
+// One wave per sorted position p < num_post (a grid-stride loop over the
+// positions, so the grid is bounded whatever the plan's capacity): the
+// wave reads its route's token row once (sorted id / topk, a scalar load)
+// and each lane quantises blocks lane, lane + 64, ... of the row.
 __global__ void __launch_bounds__(NT) quantize_gather_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ sorted_ids,
-    const int32_t* __restrict__ num_post, int topk, int sentinel, int64_t capacity, int64_t K,
+    const int32_t* __restrict__ num_post, int topk, int sentinel, int64_t K,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-  const int64_t nb = K / 32;
-  const int64_t idx = (int64_t)blockIdx.x * NT + threadIdx.x;
-  if (idx >= capacity * nb) return;
-  const int64_t p = idx / nb;
-  if (p >= num_post[0]) return;
-  const int sid = sorted_ids[p];
-  if (sid == sentinel) return;   // padding rows are never read by the W1 kernel
-  const int64_t b = idx - p * nb;
-  const uint16_t* src = x + (int64_t)(sid / topk) * K + b * 32;
-  float v[32];
+  const int nb = (int)(K / 32);
+  const int lane = threadIdx.x & 63;
+  const int nwaves = (int)gridDim.x * (NT / 64);
+  const int npos = num_post[0];
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  for (int p = (int)blockIdx.x * (NT / 64) + wave; p < npos; p += nwaves) {
+    const int sid = __builtin_amdgcn_readfirstlane(sorted_ids[p]);
+    if (sid == sentinel) continue;   // padding rows are never read by the W1 kernel
+    const uint16_t* row = x + (int64_t)(sid / topk) * K;
+    // up to four blocks per lane at a time, all their loads issued first
+    for (int b0 = lane; b0 < nb; b0 += 4 * 64) {
+      i32x4 q[4][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const i32x4 q = reinterpret_cast<const i32x4*>(src)[i];
+      for (int u = 0; u < 4; ++u)
+        if (b0 + 64 * u < nb)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[8 * i + 2 * j] = bf16_to_f32((uint32_t)q[j] & 0xffffu);
-      v[8 * i + 2 * j + 1] = bf16_to_f32((uint32_t)q[j] >> 16);
+          for (int i = 0; i < 4; ++i) q[u][i] = reinterpret_cast<const i32x4*>(row + (b0 + 64 * u) * 32)[i];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int b = b0 + 64 * u;
+        if (b >= nb) break;
+        float v[32];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v[8 * i + 2 * j] = bf16_to_f32((uint32_t)q[u][i][j] & 0xffffu);
+            v[8 * i + 2 * j + 1] = bf16_to_f32((uint32_t)q[u][i][j] >> 16);
+          }
+        quantize_block(v, codes + (int64_t)p * K + b * 32, scales + (int64_t)p * nb + b);
+      }
     }
   }
-  quantize_block(v, codes + p * K + b * 32, scales + p * nb + b);
 }
 
 // p[i * stride] = 0 for i < n: clears counters where a caller cannot rely on
@@ -428,8 +443,12 @@ hipError_t launch_quantize_gather_mxfp8(const uint16_t* x, const int32_t* sorted
                                         const int32_t* num_post, int32_t topk, int32_t sentinel,
                                         int64_t capacity, int64_t K, uint8_t* codes,
                                         uint8_t* scales, hipStream_t s) {
-  hipLaunchKernelGGL(quantize_gather_kernel, dim3(nblocks(capacity * (K / 32))), dim3(NT), 0, s, x,
-                     sorted_ids, num_post, topk, sentinel, capacity, K, codes, scales);
+  // a wave per position, up to eight workgroups per CU
+  if (capacity <= 0) return hipSuccess;
+  const int64_t need = (capacity + NT / 64 - 1) / (NT / 64);
+  const int64_t wgs = need < 2048 ? need : 2048;
+  hipLaunchKernelGGL(quantize_gather_kernel, dim3((unsigned)wgs), dim3(NT), 0, s, x, sorted_ids, num_post, topk,
+                     sentinel, K, codes, scales);
   return hipGetLastError();
 }
 

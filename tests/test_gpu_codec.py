@@ -90,3 +90,25 @@ def test_codec_expert_weights_full_size():
     rc, rs = oracle.mxfp8_quantize(w.cpu().numpy())
     assert np.array_equal(scales.cpu().numpy(), rs)
     assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def test_codec_every_bf16_magnitude():
+    """Every bf16 value of magnitude <= 448 (both signs, subnormals, +-0),
+    31 to a block next to a 448: the block scale is 2^0, so the E4M3 rounding
+    sees each value unscaled.  Through the float32 and the bf16 entry."""
+    bits = np.arange(0, 0x43E1, dtype=np.uint32)
+    vals = np.concatenate([bits, bits | 0x8000]).astype(np.uint32) << 16
+    vals = vals.view(np.float32)
+    nblk = -(-vals.size // 31)
+    blocks = np.zeros((nblk, 32), np.float32)
+    blocks[:, 0] = 448.0
+    blocks[:, 1:].flat[:vals.size] = vals
+    pad = (-nblk) % 8
+    x = np.concatenate([blocks, np.zeros((pad, 32), np.float32)]).reshape(-1, 256)
+    rc, rs = oracle.mxfp8_quantize(x)
+    assert np.all(rs[: nblk // 8] == 127)
+    codes, scales = gpu_quantize(x)
+    assert np.array_equal(scales, rs) and np.array_equal(codes, rc)
+    codes, scales = gpu_quantize_bf16(torch.from_numpy(x).to(torch.bfloat16))
+    say(f"[codec] every bf16 magnitude <= 448: {vals.size} values, mismatching codes {(codes != rc).sum()}")
+    assert np.array_equal(scales, rs) and np.array_equal(codes, rc)
