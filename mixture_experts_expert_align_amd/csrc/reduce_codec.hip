@@ -12,6 +12,8 @@
 // Codec (page "Cake MegaMoE EP16 backend for BF16 activations and MXFP8
 // weights", section 2): one thread per 32-element block: block max, scale
 // code, then E4M3 round-to-nearest-even of each element over the scale.
+#include <algorithm>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -96,6 +98,97 @@ __global__ void __launch_bounds__(NT) reduce_contiguous_kernel(const uint16_t* _
     const int64_t c = cbeg + (int64_t)NT * u;
     if (u < cpt && c < K8) *reinterpret_cast<i32x4*>(out + t * K + 8 * c) = pack8(acc[u]);
   }
+}
+
+// With an expert map (one rank's share of the experts: most slots belong to
+// experts held elsewhere) the per-token chain of dependent loads (ids, then
+// the map, then the rows) dominates, so a workgroup takes kMapTok tokens at
+// once.  Wave tt resolves token tt: lane j loads id and weight of slot j
+// together, maps the id, and the local slots are compacted in ascending slot
+// order into LDS (a ballot).  Then thread c owns 8-column chunk c of all
+// kMapTok tokens: the first kMapBatch terms of every token are loaded
+// together and added, the rest (tokens with more local slots) kMapBatch at a
+// time.  Same terms, order and arithmetic as reduce_contiguous_kernel, so the
+// same bits.  Workgroup size: the chunks of a row rounded up to waves, at
+// least kMapTok waves.
+constexpr int kMapTok = 4;
+constexpr int kMapBatch = 2;
+constexpr int kMapMaxTopk = 64;
+
+__global__ void __launch_bounds__(1024) reduce_map_kernel(const uint16_t* __restrict__ y,
+                                                          const int32_t* __restrict__ ids,
+                                                          const float* __restrict__ w,
+                                                          const int32_t* __restrict__ emap, int G,
+                                                          uint16_t* __restrict__ out, int64_t M, int topk,
+                                                          int64_t K, int E, int32_t* __restrict__ sync_zero,
+                                                          int64_t sync_lines) {
+  __shared__ int s_row[kMapTok * kMapMaxTopk];
+  __shared__ float s_w[kMapTok * kMapMaxTopk];
+  __shared__ int s_n[kMapTok];
+  if (sync_zero && blockIdx.x == 0)
+    for (int64_t i = threadIdx.x; i < sync_lines; i += blockDim.x) sync_zero[32 * i] = 0;
+  const int64_t t0 = (int64_t)blockIdx.x * kMapTok;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (wave < kMapTok) {
+    const int64_t t = t0 + wave;
+    bool valid = false;
+    float wt = 0.f;
+    if (t < M && lane < topk) {
+      const int64_t sl = t * topk + lane;
+      int id = ids[sl];
+      wt = w[sl];
+      if (emap) id = (id >= 0 && id < G) ? emap[id] : -1;   // global -> local
+      valid = id >= 0 && id < E;
+    }
+    const uint64_t mask = __ballot(valid);
+    if (valid) {
+      const int r = __popcll(mask & ((1ull << lane) - 1ull));
+      s_row[wave * kMapMaxTopk + r] = (int)(t * topk + lane);
+      s_w[wave * kMapMaxTopk + r] = wt;
+    }
+    if (lane == 0) s_n[wave] = __popcll(mask);
+  }
+  __syncthreads();
+  const int64_t c = threadIdx.x;
+  if (c >= K / 8) return;
+  float acc[kMapTok][8];
+  int n[kMapTok];
+#pragma unroll
+  for (int tt = 0; tt < kMapTok; ++tt) {
+    n[tt] = s_n[tt];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[tt][q] = 0.f;
+  }
+  auto add = [&](int tt, int q0) {
+    i32x4 v[kMapBatch];
+#pragma unroll
+    for (int q = 0; q < kMapBatch; ++q)
+      if (q0 + q < n[tt])
+        v[q] = *reinterpret_cast<const i32x4*>(y + (int64_t)s_row[tt * kMapMaxTopk + q0 + q] * K + 8 * c);
+#pragma unroll
+    for (int q = 0; q < kMapBatch; ++q)
+      if (q0 + q < n[tt]) fma8(acc[tt], s_w[tt * kMapMaxTopk + q0 + q], v[q]);
+  };
+  {
+    // the first kMapBatch terms of every token, all loads issued first
+    i32x4 v[kMapTok][kMapBatch];
+#pragma unroll
+    for (int tt = 0; tt < kMapTok; ++tt)
+#pragma unroll
+      for (int q = 0; q < kMapBatch; ++q)
+        if (q < n[tt]) v[tt][q] = *reinterpret_cast<const i32x4*>(y + (int64_t)s_row[tt * kMapMaxTopk + q] * K + 8 * c);
+#pragma unroll
+    for (int tt = 0; tt < kMapTok; ++tt)
+#pragma unroll
+      for (int q = 0; q < kMapBatch; ++q)
+        if (q < n[tt]) fma8(acc[tt], s_w[tt * kMapMaxTopk + q], v[tt][q]);
+  }
+#pragma unroll
+  for (int tt = 0; tt < kMapTok; ++tt)
+    for (int q0 = kMapBatch; q0 < n[tt]; q0 += kMapBatch) add(tt, q0);
+#pragma unroll
+  for (int tt = 0; tt < kMapTok; ++tt)
+    if (t0 + tt < M) *reinterpret_cast<i32x4*>(out + (t0 + tt) * K + 8 * c) = pack8(acc[tt]);
 }
 
 // The same layout for the batched format's CSR list of each output token.
@@ -396,6 +489,12 @@ hipError_t launch_reduce_contiguous(const uint16_t* y, const int32_t* ids, const
                                     int32_t topk, int64_t K, int32_t E, int32_t* sync_zero,
                                     int64_t sync_lines, hipStream_t s) {
   if (M == 0) return hipSuccess;
+  if (expert_map && K / 8 <= 1024 && topk <= kMapMaxTopk) {
+    const int64_t nth = std::max<int64_t>(64 * kMapTok, (K / 8 + 63) / 64 * 64);
+    hipLaunchKernelGGL(reduce_map_kernel, dim3((unsigned)((M + kMapTok - 1) / kMapTok)), dim3((unsigned)nth), 0, s,
+                       y, ids, w, expert_map, G, out, M, topk, K, E, sync_zero, sync_lines);
+    return hipGetLastError();
+  }
   const int cpt = reduce_cpt(M, K / 8);
   const dim3 grid((unsigned)M, (unsigned)((K / 8 + NT * cpt - 1) / (NT * cpt)));
   hipLaunchKernelGGL(reduce_contiguous_kernel, grid, dim3(NT), 0, s, y, ids, w, expert_map, G, out, M,
