@@ -88,6 +88,10 @@ CASES = [
     ("wide_multi", 3001, 6, 300, 0.3, 0.0),
     ("dup_ids", 200, 3, 3, 0.0, 0.0),
     ("max_buckets_multi", 1500, 8, 8192, 0.1, 0.01),   # 8192 buckets, 12 chunks
+    ("r65536_b1024", 8192, 8, 1024, 0.05, 0.01),       # 64 chunks x 1024 buckets
+    ("r32784_half_skipped", 2049, 16, 40, 0.5, 0.01),  # half the slots skipped
+    ("r65544", 8193, 8, 64, 0.0, 0.0),
+    ("b1025", 1200, 8, 1025, 0.0, 0.0),
     ("capped_chunks", 140000, 8, 64, 0.02, 0.0),       # R = 1.12M: 1024 chunks, empty tail chunks
 ]
 
