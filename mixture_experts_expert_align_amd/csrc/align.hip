@@ -14,7 +14,8 @@
 // (decode batches are launch-latency bound); larger ones as three launches:
 // per-chunk histograms (stored bucket-major), a scan of each bucket over
 // the chunks plus the bucket layout, and the scatter, whose workgroups also
-// write the padding sentinels and the tile owners.
+// write the padding sentinels and the tile owners — two launches when the
+// histogram matrix is small enough for every scatter workgroup to scan it.
 #include "align_device.h"
 
 namespace moe {
@@ -108,7 +109,60 @@ __global__ void __launch_bounds__(256) align_scatter_kernel(AlignArgs a) {
   scatter_range(a, begin, end, s_cur);
   const int nwaves = blockDim.x / kWave;
   pad_and_owners(a, (int64_t)blockIdx.x * nwaves + threadIdx.x / kWave, (int64_t)gridDim.x * nwaves,
-                 (int64_t)blockIdx.x * blockDim.x + threadIdx.x, (int64_t)gridDim.x * blockDim.x);
+                 (int64_t)blockIdx.x * blockDim.x + threadIdx.x, (int64_t)gridDim.x * blockDim.x, a.offsets,
+                 a.counts);
+}
+
+// Launches 2 and 3 in one, when the histogram matrix is small (at most
+// kAlignFuseMaxBuckets buckets and kAlignFuseMaxEntries entries, kFusePer a
+// thread, all loaded together): every scatter workgroup sums the matrix
+// itself — per bucket the total and the counts of the chunks before its own,
+// integer LDS atomics, exact in any order — and lays the buckets out in its
+// LDS; the first workgroup also publishes the layout and the invalid count.
+// Padding and tile owners come from the LDS layout, so no workgroup reads
+// what another one writes.
+constexpr int kAlignFuseMaxBuckets = 1024;
+constexpr int kFusePer = 16;
+constexpr int64_t kAlignFuseMaxEntries = 256 * kFusePer;
+__global__ void __launch_bounds__(256) align_scan_scatter_kernel(AlignArgs a) {
+  __shared__ int s_cnt[kAlignFuseMaxBuckets + 1];
+  __shared__ int s_off[kAlignFuseMaxBuckets + 1];
+  __shared__ int s_cur[kAlignFuseMaxBuckets + 1];
+  __shared__ int s_tmp[17];
+  const int me = blockIdx.x;
+  for (int e = threadIdx.x; e <= a.nb; e += blockDim.x) {
+    s_cnt[e] = 0;
+    s_cur[e] = 0;
+  }
+  const int n = (a.nb + 1) * a.nblocks;
+  int v[kFusePer];
+#pragma unroll
+  for (int q = 0; q < kFusePer; ++q) {
+    const int i = threadIdx.x + 256 * q;
+    v[q] = i < n ? a.block_hist[i] : 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kFusePer; ++q) {
+    if (v[q]) {
+      const int i = threadIdx.x + 256 * q;
+      const int e = i / a.nblocks, b = i - e * a.nblocks;   // row e: bucket (nb: invalid ids), column b: chunk
+      atomicAdd(&s_cnt[e], v[q]);
+      if (b < me) atomicAdd(&s_cur[e], v[q]);
+    }
+  }
+  __syncthreads();
+  const bool first = me == 0;
+  if (first && threadIdx.x == 0) a.status[0] = s_cnt[a.nb];
+  bucket_layout(a, s_cnt, s_off, s_tmp, first);   // ends with a barrier
+  for (int e = threadIdx.x; e < a.nb; e += blockDim.x) s_cur[e] += s_off[e];
+  __syncthreads();
+  const int64_t begin = (int64_t)me * a.chunk;
+  const int64_t end = min(a.R, begin + a.chunk);
+  scatter_range(a, begin, end, s_cur);
+  const int nwaves = blockDim.x / kWave;
+  pad_and_owners(a, (int64_t)me * nwaves + threadIdx.x / kWave, (int64_t)gridDim.x * nwaves,
+                 (int64_t)me * blockDim.x + threadIdx.x, (int64_t)gridDim.x * blockDim.x, s_off, s_cnt);
 }
 
 }  // namespace
@@ -126,6 +180,10 @@ hipError_t launch_align(const AlignArgs& args, hipStream_t s) {
   hipLaunchKernelGGL(align_hist_kernel, dim3(a.nblocks), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.nb <= kAlignFuseMaxBuckets && (int64_t)(a.nb + 1) * a.nblocks <= kAlignFuseMaxEntries) {
+    hipLaunchKernelGGL(align_scan_scatter_kernel, dim3(a.nblocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(1024), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -78,9 +78,10 @@ __device__ __forceinline__ int find_bucket(const int* s_off, int nb, int pos) {
   return lo;
 }
 
-// From per-bucket counts in s_cnt: offsets, counts and the active list.
-// Run by one workgroup.  s_off needs nb+1 ints.
-__device__ void bucket_layout(const AlignArgs& a, int* s_cnt, int* s_off, int* s_tmp) {
+// From per-bucket counts in s_cnt: offsets (in s_off, nb+1 ints) and, when
+// publish is set, offsets, counts, the active list and the padded total in
+// memory.  Run by one workgroup.
+__device__ void bucket_layout(const AlignArgs& a, int* s_cnt, int* s_off, int* s_tmp, bool publish = true) {
   const int nb = a.nb;
   const int nt = blockDim.x;
   const int per = (nb + nt - 1) / nt;
@@ -98,34 +99,40 @@ __device__ void bucket_layout(const AlignArgs& a, int* s_cnt, int* s_off, int* s
   for (int e = e0; e < e1; ++e) {
     const int c = s_cnt[e];
     s_off[e] = pbase;
-    a.offsets[e] = pbase;
-    a.counts[e] = c;
+    if (publish) {
+      a.offsets[e] = pbase;
+      a.counts[e] = c;
+      if (c > 0) a.active[abase++] = e;
+    }
     pbase += (c + a.B - 1) / a.B * a.B;
-    if (c > 0) a.active[abase++] = e;
   }
   if (threadIdx.x == 0) {
     s_off[nb] = total;
-    a.offsets[nb] = total;
-    a.num_post[0] = total;
-    a.active[a.max_active] = n_active;
+    if (publish) {
+      a.offsets[nb] = total;
+      a.num_post[0] = total;
+      a.active[a.max_active] = n_active;
+    }
   }
-  for (int64_t i = n_active + threadIdx.x; i < a.max_active; i += nt) a.active[i] = -1;
+  if (publish)
+    for (int64_t i = n_active + threadIdx.x; i < a.max_active; i += nt) a.active[i] = -1;
   __syncthreads();
 }
 
-// Padding sentinels and tile owners, from offsets and counts in global
-// memory: bucket e's padding [offsets[e] + counts[e], offsets[e+1]) and
-// tiles [offsets[e] / B, offsets[e+1] / B); past the total, sentinels and
-// owner -1.  Work item w of nw: buckets w, w + nw, ... one wave each, and a
-// grid-stride share of the tail.
-__device__ void pad_and_owners(const AlignArgs& a, int64_t w, int64_t nw, int64_t gtid, int64_t gsize) {
+// Padding sentinels and tile owners, from offsets (nb+1) and counts, in
+// global memory or LDS: bucket e's padding [offsets[e] + counts[e],
+// offsets[e+1]) and tiles [offsets[e] / B, offsets[e+1] / B); past the total,
+// sentinels and owner -1.  Work item w of nw: buckets w, w + nw, ... one
+// wave each, and a grid-stride share of the tail.
+__device__ void pad_and_owners(const AlignArgs& a, int64_t w, int64_t nw, int64_t gtid, int64_t gsize,
+                               const int* offsets, const int* counts) {
   const int lane = __lane_id();
   for (int64_t e = w; e < a.nb; e += nw) {
-    const int off = a.offsets[e], c = a.counts[e], end = a.offsets[e + 1];
+    const int off = offsets[e], c = counts[e], end = offsets[e + 1];
     for (int64_t p = off + c + lane; p < end; p += kWave) a.sorted[p] = a.sentinel;
     for (int64_t t = off / a.B + lane; t < end / a.B; t += kWave) a.block_bucket[t] = (int32_t)e;
   }
-  const int64_t total = a.offsets[a.nb];
+  const int64_t total = offsets[a.nb];
   for (int64_t p = total + gtid; p < a.capacity; p += gsize) a.sorted[p] = a.sentinel;
   for (int64_t t = total / a.B + gtid; t < a.max_tiles; t += gsize) a.block_bucket[t] = -1;
 }
@@ -174,7 +181,7 @@ __device__ void align_workgroup(const AlignArgs& a, int* s_cnt, int* s_off, int*
   __syncthreads();
   if (threadIdx.x == 0) a.status[0] = *s_invalid;
   bucket_layout(a, s_cnt, s_off, s_tmp);   // ends with a barrier: its global writes are visible
-  pad_and_owners(a, threadIdx.x / kWave, blockDim.x / kWave, threadIdx.x, blockDim.x);
+  pad_and_owners(a, threadIdx.x / kWave, blockDim.x / kWave, threadIdx.x, blockDim.x, a.offsets, a.counts);
   for (int e = threadIdx.x; e < a.nb; e += blockDim.x) s_cnt[e] = s_off[e];
   __syncthreads();
   scatter_range(a, 0, a.R, s_cnt);
