@@ -138,15 +138,17 @@ __device__ void pad_and_owners(const AlignArgs& a, int64_t w, int64_t nw, int64_
 }
 
 // Place routes [begin, end) in index order; s_cur[e] is the next free
-// position of bucket e and is advanced.  Waves take turns.
-__device__ void scatter_range(const AlignArgs& a, int64_t begin, int64_t end, int* s_cur) {
+// position of bucket e and is advanced.  Waves take turns.  first (optional):
+// this thread's key of the first block, read before.
+__device__ void scatter_range(const AlignArgs& a, int64_t begin, int64_t end, int* s_cur,
+                              const KeyRead* first = nullptr) {
   const int nt = blockDim.x;
   const int wave = threadIdx.x / kWave;
   const int nwaves = nt / kWave;
   for (int64_t base = begin; base < end; base += nt) {
     const int64_t i = base + threadIdx.x;
     KeyRead kr{-1, false, false};
-    if (i < end) kr = read_key(a, i);
+    if (i < end) kr = (first && base == begin) ? *first : read_key(a, i);
     int rank, gsize;
     bool last;
     wave_match_rank(kr.key, kr.valid, a.nbits, rank, gsize, last);
@@ -172,19 +174,23 @@ __device__ void align_workgroup(const AlignArgs& a, int* s_cnt, int* s_off, int*
   if (threadIdx.x == 0) *s_invalid = 0;
   __syncthreads();
   int inv = 0;
+  KeyRead k0{-1, false, false};   // this thread's key of the first block, kept for the scatter
   for (int64_t i = threadIdx.x; i < a.R; i += blockDim.x) {
     const KeyRead kr = read_key(a, i);
+    if (i == threadIdx.x) k0 = kr;
     if (kr.valid) atomicAdd(&s_cnt[kr.key], 1);
     inv += kr.invalid;
   }
   if (inv) atomicAdd(s_invalid, inv);
   __syncthreads();
   if (threadIdx.x == 0) a.status[0] = *s_invalid;
-  bucket_layout(a, s_cnt, s_off, s_tmp);   // ends with a barrier: its global writes are visible
-  pad_and_owners(a, threadIdx.x / kWave, blockDim.x / kWave, threadIdx.x, blockDim.x, a.offsets, a.counts);
+  bucket_layout(a, s_cnt, s_off, s_tmp);   // ends with a barrier
+  // padding and tile owners from the layout in LDS (s_cnt still holds the counts)
+  pad_and_owners(a, threadIdx.x / kWave, blockDim.x / kWave, threadIdx.x, blockDim.x, s_off, s_cnt);
+  __syncthreads();
   for (int e = threadIdx.x; e < a.nb; e += blockDim.x) s_cnt[e] = s_off[e];
   __syncthreads();
-  scatter_range(a, 0, a.R, s_cnt);
+  scatter_range(a, 0, a.R, s_cnt, &k0);
 }
 
 }  // namespace
