@@ -76,6 +76,47 @@ def test_reduce_contiguous_expert_map():
     assert np.all(np.abs(g - ref) <= bf16_bound(ref, absum))
 
 
+# (M, topk, K, E, G): a sparse share; an MXFP8-like share; a dense map (most
+# slots local, more per token than one load batch) with M not a multiple of
+# the tokens a workgroup takes; K / 8 > 1024 and topk > 64 (the other kernel)
+MAP_SHAPES = [(300, 4, 256, 6, 20), (1001, 8, 6144, 32, 512), (77, 16, 512, 40, 48),
+              (130, 8, 8448, 8, 16), (50, 70, 256, 70, 100)]
+
+
+@pytest.mark.parametrize("M,topk,K,E,G", MAP_SHAPES, ids=[f"m{m}_k{k}_t{t}_e{e}_g{g}" for m, t, k, e, g in MAP_SHAPES])
+def test_reduce_expert_map_matches_host_masked(M, topk, K, E, G):
+    """The reduce with global ids and an expert map gives the same bits as
+    the reduce with the ids masked on the host, and is within the bf16 bound
+    of the oracle; rows of slots held elsewhere (or invalid) hold NaN."""
+    rng = np.random.default_rng(M + K)
+    gid = rng.integers(0, G, (M, topk)).astype(np.int32)
+    gid[rng.random((M, topk)) < 0.05] = -1
+    gid[rng.random((M, topk)) < 0.02] = G + 5                      # out of range: skipped
+    emap = np.full(G, -1, np.int32)
+    emap[rng.choice(G, E, replace=False)] = rng.permutation(E)
+    local = oracle.map_expert_ids(gid, emap)
+    host = np.where((local >= 0) & (local < E), local, -1).astype(np.int32)
+    w = rng.random((M, topk)).astype(np.float32)
+    y = mi.ih4_normal(M * topk * K, 1.0, 97, 9, 3, device="cuda").view(M * topk, K)
+    y[torch.from_numpy(host.reshape(-1) < 0).cuda()] = float("nan")     # never read
+    plan = moe.moe_plan_init(moe.make_problem(M, K, 512, E, topk=topk, global_experts=G))
+    plan_h = moe.moe_plan_init(moe.make_problem(M, K, 512, E, topk=topk))
+    w_d = torch.from_numpy(w).cuda()
+    out = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    out_h = torch.empty_like(out)
+    moe.moe_topk_reduce_contiguous(plan, y, torch.from_numpy(gid).cuda(), w_d, out,
+                                   expert_map=torch.from_numpy(emap).cuda())
+    moe.moe_topk_reduce_contiguous(plan_h, y, torch.from_numpy(host).cuda(), w_d, out_h)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out_h.view(torch.int16))
+    yh = np.nan_to_num(oracle.bf16_to_f64(mi.bf16_bits(y)))
+    ref = oracle.topk_reduce_contiguous(yh, host, w, E)
+    absum = oracle.topk_reduce_contiguous(np.abs(yh), host, np.abs(w), E)
+    g = out.float().cpu().numpy().astype(np.float64)
+    say(f"[reduce] map M={M} topk={topk} K={K}: local slots per token {np.mean((host >= 0).sum(1)):.2f}")
+    assert np.all(np.abs(g - ref) <= bf16_bound(ref, absum))
+
+
 def run_naive_batched(E, T, K, n_out, counts, tok, w, seed):
     y = mi.ih4_normal(E * T * K, 1.0, seed, 9, 1, device="cuda").view(E, T, K)
     invalid = torch.arange(T, device="cuda")[None, :] >= torch.from_numpy(counts).cuda()[:, None]
