@@ -91,6 +91,8 @@ CASES = [
     ("r65536_b1024", 8192, 8, 1024, 0.05, 0.01),       # 64 chunks x 1024 buckets
     ("r32784_half_skipped", 2049, 16, 40, 0.5, 0.01),  # half the slots skipped
     ("r65544", 8193, 8, 64, 0.0, 0.0),
+    ("hist_4096_entries", 8192, 8, 63, 0.02, 0.01),   # 64 chunks x 64 rows: two launches
+    ("hist_4160_entries", 8192, 8, 64, 0.02, 0.01),   # 64 chunks x 65 rows: three launches
     ("b1025", 1200, 8, 1025, 0.0, 0.0),
     ("capped_chunks", 140000, 8, 64, 0.02, 0.0),       # R = 1.12M: 1024 chunks, empty tail chunks
 ]
