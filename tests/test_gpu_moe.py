@@ -298,6 +298,21 @@ def test_expert_map_mxfp8_share(M):
     del c; free()
 
 
+def test_expert_map_mxfp8_nothing_local():
+    """An MXFP8 share whose map holds none of the global experts: nothing is
+    gathered or multiplied, every output is +0.0, no id counts as invalid."""
+    cfg = mi.config(3).scaled(M=300, K=512, I=256)
+    c = make_case(cfg)
+    emap = np.full(cfg.global_experts, -1, np.int32)
+    gid = torch.from_numpy(c.inp.global_ids).cuda()
+    gw = torch.from_numpy(c.inp.global_weights).cuda()
+    out, plan, ws13, _ = run_contiguous(c, ids=gid, wts=gw, expert_map=emap, poison=True)
+    assert np.all(out.view(torch.int16).cpu().numpy() == 0)
+    assert int(moe.ws_view(ws13, plan.off_num_post_padded, 1).cpu()[0]) == 0
+    assert int(moe.ws_view(ws13, plan.off_status, 1).cpu()[0]) == 0
+    del c; free()
+
+
 def test_all_slots_skipped():
     cfg = mi.config(0)
     c = make_case(cfg)
@@ -306,9 +321,9 @@ def test_all_slots_skipped():
     assert np.all(out.view(torch.int16).cpu().numpy() == 0)
 
 
-# (K, I): both GEMMs on the weight-streaming kernel with a 2-step contraction
-# (no full 3-step round) / W1 4 steps and W2 3 / W1 5 steps with W2 on the
-# LDS-tiled kernel (K % 256 != 0) / both on the LDS-tiled kernel (I % 128 != 0)
+# (K, I): W1 / W2 contractions of 4 / 2, 8 / 6, 10 / 4 and 6 / 3 slices of 64
+# (the split ring's branches for two and three slices included), 2 to 6
+# feature strips of W1 and 2 to 5 column tiles of W2
 BATCHED_SHAPES = [(256, 128), (512, 384), (640, 256), (384, 192)]
 
 
