@@ -49,21 +49,38 @@ constexpr int kBM = kTileRoutesMxfp8;   // routes per tile (the plan's block siz
 constexpr int kSlots = 3;
 
 // NW waves, 32 weight rows each: BN = 32 NW weight rows per tile.  One step
-// slot (bytes): weight codes, route codes, weight scale words, route scale
-// words; each region a whole number of KB.
-template <int NW>
+// slot (bytes): weight codes, route codes and, unless GS, the step's scale
+// words of the weight rows and of the routes; each region a whole number of
+// KB.
+// GS (grouped scales, when a row's scale bytes are a multiple of 16): the
+// scale words of kGroup steps travel together, one 16-byte load per lane
+// (16 consecutive scale bytes of one row) into a ring of their own, instead
+// of one 4-byte load per lane and step.  A scale load touches one cache line
+// per lane whatever its width, so the 4-byte form costs the address and data
+// path as much per load as a 1 KB code block; in a read loop with this
+// kernel's mix of loads it held the weight stream at 5.4 TB/s against 5.9
+// with the grouped form.
+constexpr int kGroup = 4;     // steps per scale group (16 bytes of a row)
+constexpr int kSSlots = 2;    // scale group slots
+template <int NW, bool GS>
 struct MxTile {
   static constexpr int BN = 32 * NW;
   static constexpr int WCode = 0;
   static constexpr int XCode = WCode + BN * 128;
   static constexpr int WScale = XCode + kBM * 128;
   static constexpr int XScale = WScale + (BN * 4 + 1023) / 1024 * 1024;
-  static constexpr int Slot = XScale + 1024;
-  // loads per wave per step: weight code blocks, route code blocks, one
-  // 256-byte block of scale words
+  static constexpr int Slot = GS ? WScale : XScale + 1024;
+  // GS: one scale group slot (weight rows' 16 bytes, then the routes'), and
+  // where the ring of them starts
+  static constexpr int SSlot = (BN + kBM) * 16;
+  static constexpr int SRing = kSlots * Slot;
+  static constexpr int Lds = SRing + (GS ? kSSlots * SSlot : 0);
+  // loads per wave per step: weight code blocks, route code blocks and,
+  // unless GS, one 256-byte block of scale words (GS: one 1 KB block of
+  // scale words on the first step of each group, scale waves only)
   static constexpr int LW = BN / 8 / NW;
   static constexpr int LX = kBM / 8 / NW;
-  static constexpr int Loads = LW + LX + 1;
+  static constexpr int Loads = LW + LX + (GS ? 0 : 1);
   static_assert(LW * 8 * NW == BN && LX * 8 * NW == kBM, "code blocks per wave");
   static_assert(BN / 64 + 1 <= NW, "every scale block has a wave");
 };
@@ -141,9 +158,9 @@ __device__ __forceinline__ void mx_epilogue(const GemmArgs& g, const TileCoord& 
   }
 }
 
-template <int EPI, int NW>
+template <int EPI, int NW, bool GS>
 __device__ __forceinline__ void mxfp8_tile(const GemmArgs& g, const TileCoord& tc, uint8_t* smem) {
-  using T = MxTile<NW>;
+  using T = MxTile<NW, GS>;
   constexpr int kNW = NW;
   constexpr int kBN = T::BN;
   constexpr int kWCode = T::WCode, kXCode = T::XCode, kWScale = T::WScale, kXScale = T::XScale, kSlot = T::Slot;
@@ -175,7 +192,9 @@ __device__ __forceinline__ void mxfp8_tile(const GemmArgs& g, const TileCoord& t
   // physical chunk i % 8), LX blocks of route codes, and one 256-byte block
   // of scale words (waves 0 .. BN/64-1: weight rows 64w .. 64w+63; wave
   // BN/64: the 64 routes; later waves repeat weight blocks from 0, the same
-  // bytes to the same place).
+  // bytes to the same place).  GS: the scale blocks are 1 KB (16 bytes of
+  // each row: kGroup steps), loaded on the first step of each group into
+  // group slot (step / kGroup) % kSSlots, by waves 0 .. BN/64 only.
   constexpr int LW = T::LW, LX = T::LX;
   constexpr int kWsBlocks = kBN / 64;
   uint32_t ow[LW], ox[LX], osc;
@@ -198,17 +217,30 @@ __device__ __forceinline__ void mxfp8_tile(const GemmArgs& g, const TileCoord& t
   } else {
     osc = (uint32_t)(wrow_of(64 * sblk + lane) * KS);
   }
+  // GS: whether this wave loads scale groups (waves past BN/64 do not)
+  const bool sc_wave = !GS || wave <= kWsBlocks;
   auto issue = [&](int st) {
     uint8_t* slot = smem + (st % kSlots) * kSlot;
 #pragma unroll
     for (int j = 0; j < LW; ++j) lds_load16(wr, slot + kWCode + (wave + kNW * j) * 1024, ow[j], st * 128);
 #pragma unroll
     for (int j = 0; j < LX; ++j) lds_load16(ar, slot + kXCode + (wave + kNW * j) * 1024, ox[j], st * 128);
-    if (xscale_wave) lds_load4(asr, slot + kXScale, osc, st * 4);
-    else lds_load4(wsr, slot + kWScale + sblk * 256, osc, st * 4);
+    if (!GS) {
+      if (xscale_wave) lds_load4(asr, slot + kXScale, osc, st * 4);
+      else lds_load4(wsr, slot + kWScale + sblk * 256, osc, st * 4);
+    } else if (sc_wave && st % kGroup == 0) {
+      uint8_t* ss = smem + T::SRing + (st / kGroup % kSSlots) * T::SSlot;
+      if (xscale_wave) lds_load16(asr, ss + kBN * 16, osc, st * 4);
+      else lds_load16(wsr, ss + sblk * 1024, osc, st * 4);
+    }
     issue_order();
   };
-  constexpr int kLoads = T::Loads;   // per wave per step
+  constexpr int kLoads = T::Loads;   // per wave per step, scale groups aside
+  // wait until step st has landed, step st+1 (the only younger one) in flight
+  auto wait_before = [&](int st1) {
+    if (GS && sc_wave && st1 % kGroup == 0) wait_vm<kLoads + 1>();
+    else wait_vm<kLoads>();
+  };
 
   f32x4 acc[2][4];
 #pragma unroll
@@ -219,6 +251,14 @@ __device__ __forceinline__ void mxfp8_tile(const GemmArgs& g, const TileCoord& t
   // low byte; the builtin takes the scale from byte 0 with opsel 0)
   i32x8 fa[2][2], fb[2][4];
   int sa[2][2], sb[2][4];
+  // scale word of LDS row r (weight rows, then BN + route rows) at step st
+  auto scale_word = [&](const uint8_t* slot, int r, int st) {
+    if (GS) {
+      const uint8_t* ss = smem + T::SRing + (st / kGroup % kSSlots) * T::SSlot;
+      return *reinterpret_cast<const uint32_t*>(ss + 16 * r + 4 * (st % kGroup));
+    }
+    return *reinterpret_cast<const uint32_t*>(slot + (r < kBN ? kWScale + 4 * r : kXScale + 4 * (r - kBN)));
+  };
   auto fload = [&](int buf, int st) {
     const uint8_t* slot = smem + (st % kSlots) * kSlot;
 #pragma unroll
@@ -227,7 +267,7 @@ __device__ __forceinline__ void mxfp8_tile(const GemmArgs& g, const TileCoord& t
       const i32x4 lo = *reinterpret_cast<const i32x4*>(slot + kWCode + chunk_off(r, q));
       const i32x4 hi = *reinterpret_cast<const i32x4*>(slot + kWCode + chunk_off(r, 4 + q));
       fa[buf][t] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      sa[buf][t] = (int)(*reinterpret_cast<const uint32_t*>(slot + kWScale + 4 * r) >> (8 * q));
+      sa[buf][t] = (int)(scale_word(slot, r, st) >> (8 * q));
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -235,7 +275,7 @@ __device__ __forceinline__ void mxfp8_tile(const GemmArgs& g, const TileCoord& t
       const i32x4 lo = *reinterpret_cast<const i32x4*>(slot + kXCode + chunk_off(r, q));
       const i32x4 hi = *reinterpret_cast<const i32x4*>(slot + kXCode + chunk_off(r, 4 + q));
       fb[buf][c] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      sb[buf][c] = (int)(*reinterpret_cast<const uint32_t*>(slot + kXScale + 4 * r) >> (8 * q));
+      sb[buf][c] = (int)(scale_word(slot, kBN + r, st) >> (8 * q));
     }
   };
   auto mma = [&](int buf) {
@@ -247,7 +287,8 @@ __device__ __forceinline__ void mxfp8_tile(const GemmArgs& g, const TileCoord& t
                                                                     sa[buf][t], 0, sb[buf][c]);
   };
 
-  // prologue: steps 0, 1, 2 requested; wait for step 0
+  // prologue: steps 0, 1, 2 requested; wait for step 0 (steps 1 and 2 open
+  // no scale group)
   issue(0);
   if (nk > 1) issue(1);
   if (nk > 2) issue(2);
@@ -264,7 +305,7 @@ __device__ __forceinline__ void mxfp8_tile(const GemmArgs& g, const TileCoord& t
     if (kt + 1 < nk) {
       // step kt+1 has landed once only step kt+2's loads may still fly;
       // after the barrier nobody reads step kt's slot any more
-      if (kt + 2 < nk) wait_vm<kLoads>();
+      if (kt + 2 < nk) wait_before(kt + 2);
       else wait_vm<0>();
       lds_barrier();
       if (kt + 3 < nk) issue(kt + 3);
@@ -286,32 +327,43 @@ __device__ __forceinline__ void mxfp8_tile(const GemmArgs& g, const TileCoord& t
 // allows (an expert-parallel share may hold only a small part of the
 // routes), so the walk stops at the tiles the align step actually laid out
 // instead of dispatching a workgroup for every possible one.
-template <int EPI, int NW, int WPC>
+template <int EPI, int NW, int WPC, bool GS>
 __global__ void __launch_bounds__(64 * NW, NW * WPC / 4) gemm_tile_mxfp8_kernel(GemmArgs g, int ncol, int64_t nlog) {
-  using T = MxTile<NW>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSlots * T::Slot];
+  using T = MxTile<NW, GS>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::Lds];
   const int64_t total = (int64_t)g.rows.num_post[0] / kBM * ncol;
   const int64_t vend = tile::padded_blocks(total < nlog ? total : nlog);
   for (int64_t v = blockIdx.x; v < vend; v += gridDim.x) {
     TileCoord tc;
     if (!tile::tile_coord<kBM, T::BN, tile::kWeightMajor>(g, ncol, nlog, tc, v)) continue;
-    mxfp8_tile<EPI, NW>(g, tc, smem);
+    mxfp8_tile<EPI, NW, GS>(g, tc, smem);
     lds_barrier();   // the epilogue's LDS reads are done before the next tile's loads land
   }
 }
 
 // NW waves per workgroup, WPC workgroups per CU (the grid: WPC per CU, a
 // multiple of the 8 XCDs)
-template <int EPI, int NW, int WPC>
-hipError_t launch_tile_mxfp8_nw(const GemmArgs& g, hipStream_t s) {
-  using T = MxTile<NW>;
-  static_assert(WPC * kSlots * T::Slot <= 160 * 1024, "workgroups per CU fit the LDS");
+template <int EPI, int NW, int WPC, bool GS>
+hipError_t launch_tile_mxfp8_gs(const GemmArgs& g, hipStream_t s) {
+  using T = MxTile<NW, GS>;
+  static_assert(WPC * T::Lds <= 160 * 1024, "workgroups per CU fit the LDS");
   if (g.rows.layout != 0) return hipErrorInvalidValue;
   const int ncol = EPI == kEpiGateUp ? g.nfeat / (T::BN / 2) : g.nfeat / T::BN;
   const int64_t nlog = g.max_tiles * ncol;
   const int64_t grid = std::min<int64_t>(tile::padded_blocks(nlog), 256 * WPC);
-  hipLaunchKernelGGL((gemm_tile_mxfp8_kernel<EPI, NW, WPC>), dim3((unsigned)grid), dim3(64 * NW), 0, s, g, ncol, nlog);
+  hipLaunchKernelGGL((gemm_tile_mxfp8_kernel<EPI, NW, WPC, GS>), dim3((unsigned)grid), dim3(64 * NW), 0, s, g, ncol,
+                     nlog);
   return hipGetLastError();
+}
+
+// Grouped scales need 16 consecutive scale bytes of a row to be one aligned
+// 16-byte load: weight and activation rows whose scale bytes are a multiple
+// of 16 (contraction a multiple of 512) and 16-byte aligned scale arrays.
+template <int EPI, int NW, int WPC>
+hipError_t launch_tile_mxfp8_nw(const GemmArgs& g, hipStream_t s) {
+  const bool gs = g.kdim % 512 == 0 && g.act_ld % 512 == 0 &&
+                  ((reinterpret_cast<uintptr_t>(g.w_scale) | reinterpret_cast<uintptr_t>(g.act_scale)) & 15) == 0;
+  return gs ? launch_tile_mxfp8_gs<EPI, NW, WPC, true>(g, s) : launch_tile_mxfp8_gs<EPI, NW, WPC, false>(g, s);
 }
 
 // 4 waves and 128 weight rows per tile, two workgroups per CU (78 KB of LDS

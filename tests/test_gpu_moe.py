@@ -55,6 +55,9 @@ SCALED = [
     # single step (K = 128), W2 over I = 384 (3 steps)
     ("mxfp8_k384", mi.config(3).scaled(M=700, K=384, I=256), moe.VARIANT_AUTO),
     ("mxfp8_k128_i384", mi.config(3).scaled(M=300, K=128, I=384), moe.VARIANT_AUTO),
+    # both contractions multiples of 512: W1 (8 steps) and W2 (4 steps) load
+    # their scale words in groups of 4 steps
+    ("mxfp8_k1024_i512", mi.config(3).scaled(M=700, K=1024, I=512), moe.VARIANT_AUTO),
     # streaming kernels, W1 weights 8 steps ahead: one trip of two chunks
     # (8 steps), and a full trip before the last (16 steps) with two
     # 64-token passes per expert
@@ -166,8 +169,9 @@ def test_mxfp8_intermediates():
 
 
 @pytest.mark.parametrize("cfg", [mi.config(3).scaled(M=4160, K=512, I=256),
-                                 mi.config(3).scaled(M=12000, K=256, I=128)],
-                         ids=["m4160", "m12000_375_routes_per_expert"])
+                                 mi.config(3).scaled(M=12000, K=256, I=128),
+                                 mi.config(3).scaled(M=2000, K=2048, I=512)],
+                         ids=["m4160", "m12000_375_routes_per_expert", "k2048_i512_grouped_scales"])
 def test_mxfp8_tile_equals_stream(cfg):
     """The MXFP8 tile kernels (both operands staged in LDS, weights read once
     per expert however many 64-route tiles it has) and the streaming kernels
