@@ -74,7 +74,10 @@ struct MxTile {
   // where the ring of them starts
   static constexpr int SSlot = (BN + kBM) * 16;
   static constexpr int SRing = kSlots * Slot;
-  static constexpr int Lds = SRing + (GS ? kSSlots * SSlot : 0);
+  // W2: the tile's 64 destination rows (sorted ids), after the scale ring;
+  // Lds: the W2 kernel's LDS, Rows: the W1 kernel's
+  static constexpr int Rows = SRing + (GS ? kSSlots * SSlot : 0);
+  static constexpr int Lds = Rows + kBM * 4;
   // loads per wave per step: weight code blocks, route code blocks and,
   // unless GS, one 256-byte block of scale words (GS: one 1 KB block of
   // scale words on the first step of each group, scale waves only)
@@ -91,12 +94,12 @@ __device__ __forceinline__ int chunk_off(int row, int c) { return row * 128 + ((
 
 // The tile's end.  acc[t][c][r]: weight row 32 wave + 16 t + 4 q + r, route
 // 16 c + l16.  The operand slots are free (the caller has waited for every
-// load and met a barrier), so W1 stages z there.
+// load and met a barrier), so both epilogues stage the tile there.  orow
+// (W2): the tile's route rows' destination rows, in LDS.
 template <int EPI, int NW, int SMEM>
 __device__ __forceinline__ void mx_epilogue(const GemmArgs& g, const TileCoord& tc, const f32x4 (&acc)[2][4],
-                                            uint8_t* smem) {
+                                            uint8_t* smem, const int32_t* orow) {
   constexpr int kBN = 32 * NW;
-  const RowMap& rm = g.rows;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15;
@@ -140,21 +143,32 @@ __device__ __forceinline__ void mx_epilogue(const GemmArgs& g, const TileCoord& 
       g.out_scale[pos * (g.out_ld / 32) + f / 32] = (uint8_t)sc;
     }
   } else {
-    uint16_t* out = static_cast<uint16_t*>(g.out);
+    // bf16 rows of the tile's kBN outputs per route, laid out in LDS row by
+    // row (16-byte chunk c of row m at c ^ (m % NCH), so the 8-byte writes
+    // from the accumulators and the row reads spread over the banks), then
+    // written out as whole row segments: each store instruction covers 4
+    // rows of 256 bytes instead of 16 rows of 32
+    constexpr int NCH = kBN / 8;   // 16-byte chunks per row
+    static_assert(kBM * kBN * 2 <= SMEM && (NCH & (NCH - 1)) == 0 && NCH <= 64, "W2 staging");
+    uint16_t* st = reinterpret_cast<uint16_t*>(smem);
+    auto chunk_at = [](int m, int c) { return (m * NCH + (c ^ (m & (NCH - 1)))) * 8; };
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int m = 16 * c + l16;
-      if (m >= tc.nvalid) continue;
-      const int64_t orow = rm.sorted_ids[tc.row0 + m];   // the route's (token, slot) row
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
+        const int m = 16 * c + l16;
+        const int f = 32 * wave + 16 * t + 4 * q;
         uint32_t h[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(acc[t][c][r]);
-        *reinterpret_cast<uint2*>(out + orow * g.out_ld + tc.col0 + 32 * wave + 16 * t + 4 * q) =
-            make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        *reinterpret_cast<uint2*>(st + chunk_at(m, f / 8) + (f & 7)) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
       }
-    }
+    lds_barrier();
+    uint16_t* out = static_cast<uint16_t*>(g.out);
+    const int c = threadIdx.x % NCH;
+    for (int m = threadIdx.x / NCH; m < tc.nvalid; m += 64 * NW / NCH)
+      *reinterpret_cast<i32x4*>(out + (int64_t)orow[m] * g.out_ld + tc.col0 + 8 * c) =
+          *reinterpret_cast<const i32x4*>(st + chunk_at(m, c));
   }
 }
 
@@ -219,8 +233,14 @@ __device__ __forceinline__ void mxfp8_tile(const GemmArgs& g, const TileCoord& t
   }
   // GS: whether this wave loads scale groups (waves past BN/64 do not)
   const bool sc_wave = !GS || wave <= kWsBlocks;
+  // W2: the last wave brings the tile's 64 sorted ids (the routes'
+  // destination rows) into LDS with step 0, so the epilogue does not wait
+  // for them; a route past the tile's valid rows is never written
+  int32_t* const orow = reinterpret_cast<int32_t*>(smem + T::Rows);
+  const __amdgpu_buffer_rsrc_t sidr = buffer_rsrc(g.rows.sorted_ids + tc.row0, kBM * 4);
   auto issue = [&](int st) {
     uint8_t* slot = smem + (st % kSlots) * kSlot;
+    if (EPI == kEpiDown && st == 0 && wave == kNW - 1) lds_load4(sidr, orow, (uint32_t)(4 * lane), 0);
 #pragma unroll
     for (int j = 0; j < LW; ++j) lds_load16(wr, slot + kWCode + (wave + kNW * j) * 1024, ow[j], st * 128);
 #pragma unroll
@@ -319,7 +339,7 @@ __device__ __forceinline__ void mxfp8_tile(const GemmArgs& g, const TileCoord& t
   wait_vm<0>();
   lds_barrier();
 
-  mx_epilogue<EPI, NW, kSlots * kSlot>(g, tc, acc, smem);
+  mx_epilogue<EPI, NW, kSlots * kSlot>(g, tc, acc, smem, orow);
 }
 
 // WPC workgroups per CU (each ring takes 3 slots of LDS) walk the tiles in
@@ -330,7 +350,8 @@ __device__ __forceinline__ void mxfp8_tile(const GemmArgs& g, const TileCoord& t
 template <int EPI, int NW, int WPC, bool GS>
 __global__ void __launch_bounds__(64 * NW, NW * WPC / 4) gemm_tile_mxfp8_kernel(GemmArgs g, int ncol, int64_t nlog) {
   using T = MxTile<NW, GS>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::Lds];
+  // W1 has no destination rows to keep
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[EPI == kEpiDown ? T::Lds : T::Rows];
   const int64_t total = (int64_t)g.rows.num_post[0] / kBM * ncol;
   const int64_t vend = tile::padded_blocks(total < nlog ? total : nlog);
   for (int64_t v = blockIdx.x; v < vend; v += gridDim.x) {
