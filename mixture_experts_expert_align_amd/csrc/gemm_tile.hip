@@ -54,7 +54,9 @@ namespace tile {
 // spread over the banks; then each row's segment of the output goes out in
 // 16-byte stores, whole segments per group of lanes, instead of 8-byte
 // pieces of 32 rows per store instruction.
-template <int EPI, int BM, int BN, int WN, int WM, int NT, int TW, int TX>
+// ROUTES: the launch may take the contiguous format, whose W2 rows go to the
+// routes' (token, slot) rows (false for the rows layout of training).
+template <int EPI, int BM, int BN, int WN, int WM, int NT, int TW, int TX, bool ROUTES>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const TileCoord& tc,
                                               const f32x16 (&acc)[TW][TX], int wn, int wm, int lane,
                                               uint16_t* stage) {
@@ -64,6 +66,17 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const TileCoord
   const RowMap& rm = g.rows;
   // element offset of chunk c of row m
   auto chunk_at = [](int m, int c) { return (m * NCH + (c ^ (m & (NCH - 1)))) * 8; };
+  // contiguous W2: the destination rows of the rows this thread writes out,
+  // requested before the staging so their latency hides behind it
+  constexpr int RPP = NT / NCH;   // rows per pass of the workgroup
+  constexpr int NP = BM / RPP;    // passes
+  static_assert(BM % RPP == 0, "whole passes");
+  const bool lookup = ROUTES && EPI != kEpiGateUp && rm.layout == 0;
+  int sid[NP];
+  if (lookup) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) sid[p] = rm.sorted_ids[tc.row0 + threadIdx.x / NCH + RPP * p];
+  }
 #pragma unroll
   for (int j = 0; j < TX; ++j) {
     const int m = wm * (BM / WM) + 32 * j + (lane & 31);
@@ -100,18 +113,19 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const TileCoord
   uint16_t* out = static_cast<uint16_t*>(g.out);
   const int col = EPI == kEpiGateUp ? tc.col0 / 2 : tc.col0;
   const int c = threadIdx.x % NCH;
-  for (int m = threadIdx.x / NCH; m < BM; m += NT / NCH) {
-    if (rm.layout != 0 && (m < tc.mlo || m >= tc.nvalid)) continue;   // batched / rows: only the tile's own rows
-    int64_t orow;
-    if (EPI == kEpiGateUp || rm.layout != 0) {
-      orow = tc.row0 + m;
-    } else {
-      const int sid = rm.sorted_ids[tc.row0 + m];       // W2: the route's (token, slot) row
-      if (sid == rm.sentinel) continue;                 // padding rows are dropped
-      orow = sid;
-    }
+  auto put = [&](int m, int64_t orow) {
     *reinterpret_cast<i32x4*>(out + orow * g.out_ld + col + 8 * c) =
         *reinterpret_cast<const i32x4*>(stage + chunk_at(m, c));
+  };
+  if (lookup) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p)   // W2: each route to its (token, slot) row, padding rows dropped
+      if (sid[p] != rm.sentinel) put(threadIdx.x / NCH + RPP * p, sid[p]);
+  } else {
+    for (int m = threadIdx.x / NCH; m < BM; m += RPP) {
+      if (rm.layout != 0 && (m < tc.mlo || m >= tc.nvalid)) continue;   // batched / rows: only the tile's own rows
+      put(m, tc.row0 + m);
+    }
   }
 }
 
@@ -227,7 +241,7 @@ struct SplitRing {
 // One tile: BN weight rows from tc.col0 times the route rows [mlo, nvalid)
 // of the BM from tc.row0, through the epilogue.  smem: SplitRing::Elems
 // elements; the caller meets a barrier before it reuses them.
-template <int EPI, int BM, int BN, int BK, int WN, int WM, bool WT = false>
+template <int EPI, int BM, int BN, int BK, int WN, int WM, bool WT = false, bool ROUTES = true>
 __device__ __forceinline__ void split_tile(const GemmArgs& g, const TileCoord& tc, uint16_t* smem) {
   constexpr int NW = WN * WM;
   constexpr int CH = BK / 8;
@@ -383,7 +397,7 @@ __device__ __forceinline__ void split_tile(const GemmArgs& g, const TileCoord& t
   wait_vm<0>();
   lds_barrier();
   static_assert(BM * (EPI == kEpiGateUp ? BN / 2 : BN) <= Ring::Elems, "epilogue tile fits the LDS");
-  tile_epilogue<EPI, BM, BN, WN, WM, 64 * WN * WM>(g, tc, acc, wn, wm, lane, smem);
+  tile_epilogue<EPI, BM, BN, WN, WM, 64 * WN * WM, TW, TX, ROUTES>(g, tc, acc, wn, wm, lane, smem);
 }
 
 template <int EPI, int BM, int BN, int BK, int WN, int WM, int OCC, int ORDER>
@@ -392,7 +406,7 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_split_bf16_kernel
   __shared__ __attribute__((aligned(1024))) uint16_t smem[SplitRing<BM, BN, BK>::Elems];
   TileCoord tc;
   if (!tile_coord<BM, BN, ORDER>(g, ncol, nlog, tc)) return;
-  split_tile<EPI, BM, BN, BK, WN, WM>(g, tc, smem);
+  split_tile<EPI, BM, BN, BK, WN, WM, false, ORDER == kWeightMajor>(g, tc, smem);
 }
 
 // Training forward (page "Cake deterministic MoE grouped GEMM",
@@ -461,7 +475,7 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_rows_kernel(GemmA
     tc.expert = e;
     tc.mlo = (int)(s0 - r0);
     tc.nvalid = (int)(s1 - r0);
-    split_tile<EPI, BM, BN, BK, WN, WM, WT>(g, tc, smem);
+    split_tile<EPI, BM, BN, BK, WN, WM, WT, false>(g, tc, smem);
     return;
   }
   bool first = true;
@@ -475,7 +489,7 @@ __global__ void __launch_bounds__(64 * WN * WM, OCC) gemm_tile_rows_kernel(GemmA
     tc.expert = e;
     tc.mlo = (int)(s0 - r0);
     tc.nvalid = (int)(s1 - r0);
-    split_tile<EPI, BM, BN, BK, WN, WM, WT>(g, tc, smem);
+    split_tile<EPI, BM, BN, BK, WN, WM, WT, false>(g, tc, smem);
   }
 }
 
