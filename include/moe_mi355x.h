@@ -27,7 +27,12 @@
  *  - Return value: MOE_OK (0) or an error code.  On an error nothing has been
  *    enqueued, except MOE_EHIP (a launch failed; earlier kernels of the same
  *    call may have been enqueued).  No C++ exception crosses this boundary.
- *  - Device buffers must be 16-byte aligned.
+ *  - Device buffers of activations, weights, outputs and workspaces must be
+ *    16-byte aligned; the 4-byte element arrays (topk ids and weights,
+ *    expert_num_tokens, the batched row map, group offsets, the expert map)
+ *    and the MXFP8 scale arrays need 4-byte alignment.  (Scale arrays that
+ *    are 16-byte aligned, with K and I multiples of 512, let the MXFP8 tile
+ *    kernels load four contraction steps of scale words at once.)
  *  - Calls are reentrant; a plan is immutable after moe_plan_init.
  */
 #ifndef MOE_MI355X_H

@@ -10,6 +10,7 @@ times and check sampled tokens one by one.  Tolerances: bf16 weights
 <= 6e-2 * max|ref|, max|ref| over the checked outputs.  Also: bitwise run-to-run
 equality, +0.0 for tokens with no valid slot, nullity of weight-0 / id -1
 slots, token-shuffle equivariance."""
+import dataclasses
 import gc
 
 import numpy as np
@@ -183,6 +184,29 @@ def test_mxfp8_tile_equals_stream(cfg):
     assert ptile.variant == moe.VARIANT_TILE and pstream.variant == moe.VARIANT_STREAM
     assert torch.equal(tile.view(torch.int16), stream.view(torch.int16)), "MXFP8 tile and stream outputs differ"
     check_close(tile, oracle_contiguous(c, np.arange(cfg.M)), MX_REL, 0.0, f"{cfg.name} tile")
+
+
+def test_mxfp8_scale_groups_equal_per_step_scales():
+    """With K and I multiples of 512 the MXFP8 tile kernels load the scale
+    words of four steps at once; weight scale arrays that are only 4-byte
+    aligned make them load each step's words on their own.  The MFMAs and
+    their order are the same, so the outputs agree bit for bit."""
+    cfg = mi.config(3).scaled(M=700, K=1024, I=512)
+    c = make_case(cfg)
+    grouped, pg, *_ = run_contiguous(c, moe.VARIANT_TILE, poison=True)
+
+    def shifted(t):   # the same bytes 4 bytes past a 16-byte boundary
+        buf = torch.empty(t.numel() + 4, dtype=t.dtype, device=t.device)
+        v = buf[4:].view(t.shape)
+        v.copy_(t)
+        assert v.data_ptr() % 16 == 4
+        return v
+
+    c2 = dataclasses.replace(c, w1_scale=shifted(c.w1_scale), w2_scale=shifted(c.w2_scale))
+    per_step, ps, *_ = run_contiguous(c2, moe.VARIANT_TILE, poison=True)
+    assert pg.variant == ps.variant == moe.VARIANT_TILE
+    assert torch.equal(grouped.view(torch.int16), per_step.view(torch.int16))
+    check_close(grouped, oracle_contiguous(c, np.arange(cfg.M)), MX_REL, 0.0, f"{cfg.name} grouped scales")
 
 
 def test_tiny_intermediate_z():
