@@ -26,6 +26,7 @@ CONTIGUOUS = [
     ("prefill_tile", mi.config(2).scaled(M=700, K=512, I=384, E=24), moe.VARIANT_AUTO),
     ("mxfp8_tile", mi.config(3).scaled(M=512, K=512, I=256), moe.VARIANT_AUTO),
     ("mxfp8_stream", mi.config(3).scaled(M=512, K=512, I=256), moe.VARIANT_STREAM),
+    ("mxfp8_tile_grouped_scales", mi.config(3).scaled(M=700, K=1024, I=512), moe.VARIANT_AUTO),
 ]
 
 

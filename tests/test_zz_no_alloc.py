@@ -10,7 +10,7 @@ import torch
 
 import moe_inputs as mi
 import mixture_experts_expert_align_amd as moe
-from moe_cases import BF16_ABS, BF16_REL, check_close, make_case, oracle_contiguous, problem, say
+from moe_cases import BF16_ABS, BF16_REL, MX_REL, check_close, make_case, oracle_contiguous, problem, say
 
 pytestmark = pytest.mark.gpu
 
@@ -39,6 +39,9 @@ def static_vs_allocating(c, variant=moe.VARIANT_AUTO):
      (1, dict(M=13, K=512, I=1024), moe.VARIANT_STREAM)),
     # single launch twice: a larger then a smaller batch of the same layer
     ((0, dict(M=200), moe.VARIANT_FUSED), (0, None, moe.VARIANT_FUSED)),
+    # MXFP8 tiles: scale words in groups of four steps (K, I multiples of
+    # 512), then a smaller layer whose W2 loads them step by step
+    ((3, dict(M=700, K=1024, I=512), moe.VARIANT_AUTO), (3, dict(M=300, K=512, I=256), moe.VARIANT_AUTO)),
 ])
 def test_static_matches_allocating_two_calls(first, second):
     outs = []
@@ -48,7 +51,8 @@ def test_static_matches_allocating_two_calls(first, second):
         outs.append((c, static_vs_allocating(c, variant)))
     # the second call against the oracle as well
     c, out = outs[-1]
-    check_close(out, oracle_contiguous(c, np.arange(c.cfg.M)), BF16_REL, BF16_ABS, f"static {c.cfg.name}")
+    rel, ab = (MX_REL, 0.0) if c.cfg.w_dtype == "mxfp8" else (BF16_REL, BF16_ABS)
+    check_close(out, oracle_contiguous(c, np.arange(c.cfg.M)), rel, ab, f"static {c.cfg.name}")
 
 
 def test_static_refuses_plans_that_do_not_fit():
