@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 /* Status codes. */
 enum {
@@ -66,7 +66,19 @@ enum {
    * ceil(log2(blockmax/448)) + 127 clamped to [0,254], 0 for an all-zero block
    * (page "Cake MegaMoE EP16 backend for BF16 activations and MXFP8 weights",
    * section 2, the new scale rule). */
-  MOE_W_MXFP8 = 1
+  MOE_W_MXFP8 = 1,
+  /* MOE_W_MXFP8 with the scale arrays grouped: in each expert's matrix of
+   * rows x cols/32 scale bytes, byte j of row r sits at
+   * (j / 16) * rows * 16 + r * 16 + j % 16.  For every 4 contraction steps of
+   * 128, the 16 scale bytes of each row lie side by side.
+   * moe_pack_mxfp8_scales writes this layout from the row-major one, once,
+   * as the weights are loaded (the same page, section 2, packs the scale
+   * arrays for its GEMM at that point).  The tile kernels then load the
+   * scale words of 4 steps of 64 rows as one contiguous KiB, instead of one
+   * 16-byte piece from each of 64 rows.  Needs K and I multiples of 512,
+   * the contiguous format, the tile variant and 16-byte-aligned scale
+   * arrays. */
+  MOE_W_MXFP8_GROUPED = 2
 };
 
 /* Row order of W1 [E, 2I, K]. */
@@ -174,10 +186,12 @@ typedef struct moe_plan {
                               order: bf16 [sorted_capacity, I], or E4M3
                               [sorted_capacity, I] for MXFP8 (batched: rows
                               e*max_tokens + r)                                */
-  int64_t off_z_scale;     /* MXFP8: UE8M0 [rows of z, I/32]                   */
+  int64_t off_z_scale;     /* MXFP8: UE8M0 [rows of z, I/32]; MOE_W_MXFP8_GROUPED:
+                              grouped as the weights' ([I/512][rows][16])      */
   int64_t off_xq;          /* MXFP8: E4M3 activations gathered in sorted order
                               [sorted_capacity, K]                              */
-  int64_t off_xq_scale;    /* MXFP8: UE8M0 [sorted_capacity, K/32]             */
+  int64_t off_xq_scale;    /* MXFP8: UE8M0 [sorted_capacity, K/32];
+                              MOE_W_MXFP8_GROUPED: [K/512][sorted_capacity][16]*/
   int64_t off_sync;        /* MOE_VARIANT_FUSED: the work queue, int32 words:
                               counters at 32*i for i < 2 + max_active (ticket,
                               align published, W1 strips done per slot), then
@@ -346,6 +360,18 @@ int moe_topk_reduce_naive_batched(const moe_plan* plan, const void* y,
  * how MXFP8 weights are produced for moe_apply_*. */
 int moe_quantize_mxfp8(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* codes,
                        uint8_t* scales, void* stream);
+
+/* Scale arrays for MOE_W_MXFP8_GROUPED (page "Cake MegaMoE EP16 backend for
+ * BF16 activations and MXFP8 weights", section 2: the scales are packed for
+ * the GEMM once, when the weights are loaded).  src (device) holds mats
+ * matrices of rows x cols/32 UE8M0 bytes, row-major, as moe_quantize_mxfp8
+ * writes them (W1: mats = E, rows = 2I, cols = K; W2: E, K, I); dst (device,
+ * the same size, 16-byte aligned, not overlapping src) receives each matrix
+ * grouped as MOE_W_MXFP8_GROUPED describes.  cols % 512 must be 0.  Enqueues
+ * one kernel on the stream; allocates nothing and does not synchronise.
+ * MOE_EINVAL for a null or misaligned pointer or a bad size. */
+int moe_pack_mxfp8_scales(const uint8_t* src, uint8_t* dst, int64_t mats, int64_t rows, int64_t cols,
+                          void* stream);
 
 /* ---------------------------------------------------------------------------
  * Training grouped GEMMs (page "Cake deterministic MoE grouped GEMM":

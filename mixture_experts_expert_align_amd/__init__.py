@@ -15,7 +15,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "ABI_VERSION", "LAYOUT_CONTIGUOUS", "LAYOUT_BATCHED", "W_BF16", "W_MXFP8", "W1_HALVES",
+    "ABI_VERSION", "LAYOUT_CONTIGUOUS", "LAYOUT_BATCHED", "W_BF16", "W_MXFP8", "W_MXFP8_GROUPED", "W1_HALVES",
     "W1_INTERLEAVE16", "VARIANT_AUTO", "VARIANT_TILE", "VARIANT_STREAM", "VARIANT_FUSED", "REDUCE_NOOP",
     "REDUCE_CONTIGUOUS", "REDUCE_NAIVE_BATCHED", "MoeError", "MoeProblem", "MoePlan", "MoeWeights",
     "load_library", "library_path", "moe_abi_version", "moe_status_string", "moe_plan_init",
@@ -23,16 +23,16 @@ __all__ = [
     "moe_plan_reason", "moe_align_permute", "moe_apply_contiguous", "moe_apply_batched",
     "moe_gate_up_act", "moe_down_unpermute",
     "moe_topk_reduce_contiguous", "moe_naive_batched_ws_bytes", "moe_topk_reduce_naive_batched",
-    "moe_quantize_mxfp8", "make_problem", "allocate_workspaces", "ws_view", "status_words",
+    "moe_quantize_mxfp8", "moe_pack_mxfp8_scales", "make_problem", "allocate_workspaces", "ws_view", "status_words",
     "check_status",
     "MoeGroupedProblem", "moe_grouped_forward", "moe_grouped_dgrad", "moe_grouped_wgrad",
 ]
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 STATIC_SCRATCH_BYTES = 64 << 20     # MOE_STATIC_SCRATCH_BYTES
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, 1, 2, 3
 LAYOUT_CONTIGUOUS, LAYOUT_BATCHED = 0, 1
-W_BF16, W_MXFP8 = 0, 1
+W_BF16, W_MXFP8, W_MXFP8_GROUPED = 0, 1, 2
 W1_HALVES, W1_INTERLEAVE16 = 0, 1
 VARIANT_AUTO, VARIANT_TILE, VARIANT_STREAM, VARIANT_FUSED = -1, 0, 1, 2
 REDUCE_NOOP, REDUCE_CONTIGUOUS, REDUCE_NAIVE_BATCHED = 0, 1, 2
@@ -108,6 +108,7 @@ def load_library() -> ctypes.CDLL:
         "moe_naive_batched_ws_bytes": (_i64, [_vp, _i64]),
         "moe_topk_reduce_naive_batched": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp]),
         "moe_quantize_mxfp8": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _vp]),
+        "moe_pack_mxfp8_scales": (_i32, [_vp, _vp, _i64, _i64, _i64, _vp]),
         "moe_grouped_forward": (_i32, [_vp] * 6),
         "moe_grouped_dgrad": (_i32, [_vp] * 6),
         "moe_grouped_wgrad": (_i32, [_vp] * 5 + [_i32, _vp]),
@@ -256,7 +257,7 @@ def moe_align_permute(plan: MoePlan, topk_ids: torch.Tensor, ws13: torch.Tensor,
 
 def _weights(plan: MoePlan, w1, w2, w1_scale=None, w2_scale=None, expert_map=None) -> MoeWeights:
     p = plan.prob
-    mx = p.w_dtype == W_MXFP8
+    mx = p.w_dtype in (W_MXFP8, W_MXFP8_GROUPED)
     wt = torch.uint8 if mx else torch.bfloat16
     n1, n2 = p.E * 2 * p.I * p.K, p.E * p.K * p.I
     if mx and (w1_scale is None or w2_scale is None):
@@ -358,6 +359,21 @@ def moe_quantize_mxfp8(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tenso
                                            _arg(scales, "scales", torch.uint8, x.numel() // 32),
                                            _stream(stream))
     _check("moe_quantize_mxfp8", st)
+
+
+def moe_pack_mxfp8_scales(scales: torch.Tensor, packed: torch.Tensor, stream=None):
+    """Row-major MXFP8 scale arrays ``[..., rows, cols/32]`` (as
+    moe_quantize_mxfp8 writes them) into ``packed`` (same size) in the layout
+    of W_MXFP8_GROUPED: each matrix of the last two dimensions in groups of
+    16 bytes a row."""
+    if scales.dim() < 2:
+        raise ValueError("scales: expected [..., rows, cols/32]")
+    rows, ncols = scales.shape[-2], scales.shape[-1] * 32
+    mats = scales.numel() // max(rows * scales.shape[-1], 1)
+    st = load_library().moe_pack_mxfp8_scales(_arg(scales, "scales", torch.uint8, scales.numel()),
+                                              _arg(packed, "packed", torch.uint8, scales.numel()),
+                                              mats, rows, ncols, _stream(stream))
+    _check("moe_pack_mxfp8_scales", st)
 
 
 # ------------------------------------------------------------- training ----

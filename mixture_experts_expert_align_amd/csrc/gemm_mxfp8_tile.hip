@@ -96,7 +96,7 @@ __device__ __forceinline__ int chunk_off(int row, int c) { return row * 128 + ((
 // 16 c + l16.  The operand slots are free (the caller has waited for every
 // load and met a barrier), so both epilogues stage the tile there.  orow
 // (W2): the tile's route rows' destination rows, in LDS.
-template <int EPI, int NW, int SMEM>
+template <int EPI, int NW, int SMEM, bool PK>
 __device__ __forceinline__ void mx_epilogue(const GemmArgs& g, const TileCoord& tc, const f32x4 (&acc)[2][4],
                                             uint8_t* smem, const int32_t* orow) {
   constexpr int kBN = 32 * NW;
@@ -140,7 +140,10 @@ __device__ __forceinline__ void mx_epilogue(const GemmArgs& g, const TileCoord& 
       uint8_t* o = static_cast<uint8_t*>(g.out) + pos * g.out_ld + f;
       *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2], w[3]);
       *reinterpret_cast<uint4*>(o + 16) = make_uint4(w[4], w[5], w[6], w[7]);
-      g.out_scale[pos * (g.out_ld / 32) + f / 32] = (uint8_t)sc;
+      // PK: z's scales grouped like the weights' (16 bytes a row per group)
+      const int j = f / 32;
+      g.out_scale[PK ? (int64_t)(j / 16) * g.scale_group + pos * 16 + j % 16 : pos * (g.out_ld / 32) + j] =
+          (uint8_t)sc;
     }
   } else {
     // bf16 rows of the tile's kBN outputs per route, laid out in LDS row by
@@ -172,8 +175,12 @@ __device__ __forceinline__ void mx_epilogue(const GemmArgs& g, const TileCoord& 
   }
 }
 
-template <int EPI, int NW, bool GS>
+// PK (with GS): the scale arrays are grouped (moe_pack_mxfp8_scales for the
+// weights, the same layout for the activations), so a group's 16 bytes of
+// 64 consecutive rows are one contiguous KiB.
+template <int EPI, int NW, bool GS, bool PK>
 __device__ __forceinline__ void mxfp8_tile(const GemmArgs& g, const TileCoord& tc, uint8_t* smem) {
+  static_assert(!PK || GS, "grouped arrays are loaded a group at a time");
   using T = MxTile<NW, GS>;
   constexpr int kNW = NW;
   constexpr int kBN = T::BN;
@@ -227,10 +234,14 @@ __device__ __forceinline__ void mxfp8_tile(const GemmArgs& g, const TileCoord& t
   const int sblk = wave < kWsBlocks ? wave : (wave - kWsBlocks - 1) % kWsBlocks;
   if (xscale_wave) {
     const int64_t pos = pos_of(lane);
-    osc = pos >= 0 ? (uint32_t)(pos * (g.act_ld / 32)) : 0x80000000u;
+    osc = pos >= 0 ? (uint32_t)(pos * (PK ? 16 : g.act_ld / 32)) : 0x80000000u;
   } else {
-    osc = (uint32_t)(wrow_of(64 * sblk + lane) * KS);
+    osc = (uint32_t)(wrow_of(64 * sblk + lane) * (PK ? 16 : KS));
   }
+  // PK: bytes between groups, the weights' (rows of the expert's matrix x
+  // 16) and the activations'
+  const int wgroup = PK ? (int)(g.w_expert_stride / K) * 16 : 0;
+  const int xgroup = PK ? (int)g.scale_group : 0;
   // GS: whether this wave loads scale groups (waves past BN/64 do not)
   const bool sc_wave = !GS || wave <= kWsBlocks;
   // W2: the last wave brings the tile's 64 sorted ids (the routes'
@@ -250,8 +261,8 @@ __device__ __forceinline__ void mxfp8_tile(const GemmArgs& g, const TileCoord& t
       else lds_load4(wsr, slot + kWScale + sblk * 256, osc, st * 4);
     } else if (sc_wave && st % kGroup == 0) {
       uint8_t* ss = smem + T::SRing + (st / kGroup % kSSlots) * T::SSlot;
-      if (xscale_wave) lds_load16(asr, ss + kBN * 16, osc, st * 4);
-      else lds_load16(wsr, ss + sblk * 1024, osc, st * 4);
+      if (xscale_wave) lds_load16(asr, ss + kBN * 16, osc, PK ? st / kGroup * xgroup : st * 4);
+      else lds_load16(wsr, ss + sblk * 1024, osc, PK ? st / kGroup * wgroup : st * 4);
     }
     issue_order();
   };
@@ -339,7 +350,7 @@ __device__ __forceinline__ void mxfp8_tile(const GemmArgs& g, const TileCoord& t
   wait_vm<0>();
   lds_barrier();
 
-  mx_epilogue<EPI, NW, kSlots * kSlot>(g, tc, acc, smem, orow);
+  mx_epilogue<EPI, NW, kSlots * kSlot, PK>(g, tc, acc, smem, orow);
 }
 
 // WPC workgroups per CU (each ring takes 3 slots of LDS) walk the tiles in
@@ -347,7 +358,7 @@ __device__ __forceinline__ void mxfp8_tile(const GemmArgs& g, const TileCoord& t
 // allows (an expert-parallel share may hold only a small part of the
 // routes), so the walk stops at the tiles the align step actually laid out
 // instead of dispatching a workgroup for every possible one.
-template <int EPI, int NW, int WPC, bool GS>
+template <int EPI, int NW, int WPC, bool GS, bool PK>
 __global__ void __launch_bounds__(64 * NW, NW * WPC / 4) gemm_tile_mxfp8_kernel(GemmArgs g, int ncol, int64_t nlog) {
   using T = MxTile<NW, GS>;
   // W1 has no destination rows to keep
@@ -357,14 +368,14 @@ __global__ void __launch_bounds__(64 * NW, NW * WPC / 4) gemm_tile_mxfp8_kernel(
   for (int64_t v = blockIdx.x; v < vend; v += gridDim.x) {
     TileCoord tc;
     if (!tile::tile_coord<kBM, T::BN, tile::kWeightMajor>(g, ncol, nlog, tc, v)) continue;
-    mxfp8_tile<EPI, NW, GS>(g, tc, smem);
+    mxfp8_tile<EPI, NW, GS, PK>(g, tc, smem);
     lds_barrier();   // the epilogue's LDS reads are done before the next tile's loads land
   }
 }
 
 // NW waves per workgroup, WPC workgroups per CU (the grid: WPC per CU, a
 // multiple of the 8 XCDs)
-template <int EPI, int NW, int WPC, bool GS>
+template <int EPI, int NW, int WPC, bool GS, bool PK>
 hipError_t launch_tile_mxfp8_gs(const GemmArgs& g, hipStream_t s) {
   using T = MxTile<NW, GS>;
   static_assert(WPC * T::Lds <= 160 * 1024, "workgroups per CU fit the LDS");
@@ -372,19 +383,23 @@ hipError_t launch_tile_mxfp8_gs(const GemmArgs& g, hipStream_t s) {
   const int ncol = EPI == kEpiGateUp ? g.nfeat / (T::BN / 2) : g.nfeat / T::BN;
   const int64_t nlog = g.max_tiles * ncol;
   const int64_t grid = std::min<int64_t>(tile::padded_blocks(nlog), 256 * WPC);
-  hipLaunchKernelGGL((gemm_tile_mxfp8_kernel<EPI, NW, WPC, GS>), dim3((unsigned)grid), dim3(64 * NW), 0, s, g, ncol,
-                     nlog);
+  hipLaunchKernelGGL((gemm_tile_mxfp8_kernel<EPI, NW, WPC, GS, PK>), dim3((unsigned)grid), dim3(64 * NW), 0, s, g,
+                     ncol, nlog);
   return hipGetLastError();
 }
 
 // Grouped scales need 16 consecutive scale bytes of a row to be one aligned
 // 16-byte load: weight and activation rows whose scale bytes are a multiple
 // of 16 (contraction a multiple of 512) and 16-byte aligned scale arrays.
+// Grouped arrays (g.scale_group > 0) meet all of that by construction (the
+// plan and the entry points check it).
 template <int EPI, int NW, int WPC>
 hipError_t launch_tile_mxfp8_nw(const GemmArgs& g, hipStream_t s) {
+  if (g.scale_group) return launch_tile_mxfp8_gs<EPI, NW, WPC, true, true>(g, s);
   const bool gs = g.kdim % 512 == 0 && g.act_ld % 512 == 0 &&
                   ((reinterpret_cast<uintptr_t>(g.w_scale) | reinterpret_cast<uintptr_t>(g.act_scale)) & 15) == 0;
-  return gs ? launch_tile_mxfp8_gs<EPI, NW, WPC, true>(g, s) : launch_tile_mxfp8_gs<EPI, NW, WPC, false>(g, s);
+  return gs ? launch_tile_mxfp8_gs<EPI, NW, WPC, true, false>(g, s)
+            : launch_tile_mxfp8_gs<EPI, NW, WPC, false, false>(g, s);
 }
 
 // 4 waves and 128 weight rows per tile, two workgroups per CU (78 KB of LDS

@@ -100,6 +100,11 @@ struct GemmArgs {
   void* out;                   // W1: z; W2: y rows
   uint8_t* out_scale;          // W1 MXFP8: z scales
   int64_t out_ld;
+  // MXFP8 with grouped scales (moe_pack_mxfp8_scales): bytes between the
+  // 16-byte groups of the activation scales and of W1's output scales (their
+  // rows x 16); the weight scales are grouped per expert.  0: every scale
+  // array row-major.
+  int64_t scale_group;
 };
 
 // Routes per plan tile of the tiled kernels: the contiguous format's align
@@ -203,10 +208,17 @@ hipError_t launch_zero_words(int32_t* p, int64_t n, int64_t stride, hipStream_t 
 hipError_t launch_quantize_mxfp8(const void* x, int x_dtype, int64_t rows, int64_t cols,
                                  uint8_t* codes, uint8_t* scales, hipStream_t s);
 // MXFP8 rows of x gathered in sorted order: row p <- x[sorted_ids[p] / topk]
-// (sentinel rows are zero-filled), for p < capacity.
+// for the positions p < num_post[0] that hold a route (padding positions are
+// skipped: the W1 kernels never read them).  Scales row-major [capacity,
+// K/32], or with scale_group > 0 grouped: byte j of row p at
+// (j / 16) * scale_group + p * 16 + j % 16.
 hipError_t launch_quantize_gather_mxfp8(const uint16_t* x, const int32_t* sorted_ids,
                                         const int32_t* num_post, int32_t topk, int32_t sentinel,
                                         int64_t capacity, int64_t K, uint8_t* codes,
-                                        uint8_t* scales, hipStream_t s);
+                                        uint8_t* scales, int64_t scale_group, hipStream_t s);
+// mats matrices of rows x cols/32 scale bytes, row-major -> grouped per
+// matrix (byte j of row r at (j / 16) * rows * 16 + r * 16 + j % 16)
+hipError_t launch_pack_mxfp8_scales(const uint8_t* src, uint8_t* dst, int64_t mats, int64_t rows, int64_t cols,
+                                    hipStream_t s);
 
 }  // namespace moe

@@ -18,6 +18,8 @@ constexpr int64_t kAlign = 256;
 inline int64_t up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 inline bool aligned16(const void* p) { return p && ((uintptr_t)p & 15u) == 0; }
 inline bool aligned4(const void* p) { return p && ((uintptr_t)p & 3u) == 0; }
+// MXFP8 weights, with row-major or grouped scale arrays
+inline bool is_mxfp8(const moe_problem& P) { return P.w_dtype == MOE_W_MXFP8 || P.w_dtype == MOE_W_MXFP8_GROUPED; }
 
 int fail(moe_plan* plan, int code, const char* msg) {
   if (plan) snprintf(plan->reason, sizeof(plan->reason), "%s", msg);
@@ -138,7 +140,7 @@ int moe_plan_init(moe_plan* plan, const moe_problem* prob) {
     return fail(plan, MOE_EINVAL, "M, K, I and E must be positive");
   if (P.layout != MOE_LAYOUT_CONTIGUOUS && P.layout != MOE_LAYOUT_BATCHED)
     return fail(plan, MOE_EINVAL, "unknown layout");
-  if (P.w_dtype != MOE_W_BF16 && P.w_dtype != MOE_W_MXFP8)
+  if (P.w_dtype != MOE_W_BF16 && !is_mxfp8(P))
     return fail(plan, MOE_EINVAL, "unknown weight dtype");
   if (P.w1_order != MOE_W1_HALVES && P.w1_order != MOE_W1_INTERLEAVE16)
     return fail(plan, MOE_EINVAL, "unknown W1 row order");
@@ -164,7 +166,7 @@ int moe_plan_init(moe_plan* plan, const moe_problem* prob) {
     return fail(plan, MOE_EINVAL, "the 16-row interleave needs I % 16 == 0");
 
   int variant = P.variant;
-  if (P.w_dtype == MOE_W_MXFP8) {
+  if (is_mxfp8(P)) {
     if (!contiguous)
       return fail(plan, MOE_EUNSUPPORTED, "MXFP8 weights are built for the contiguous format only");
     if (variant == MOE_VARIANT_FUSED)
@@ -176,6 +178,12 @@ int moe_plan_init(moe_plan* plan, const moe_problem* prob) {
     // the tiles (128 weight rows: 64 W1 features, 128 W2 rows, covered by
     // the checks above) unless the streaming kernels are asked for
     if (variant == MOE_VARIANT_AUTO) variant = MOE_VARIANT_TILE;
+    if (P.w_dtype == MOE_W_MXFP8_GROUPED) {
+      if (variant != MOE_VARIANT_TILE)
+        return fail(plan, MOE_EUNSUPPORTED, "grouped MXFP8 scales are read by the tile kernels only");
+      if (P.K % 512 || P.I % 512)
+        return fail(plan, MOE_EUNSUPPORTED, "grouped MXFP8 scales need K % 512 == 0 and I % 512 == 0");
+    }
     if (variant == MOE_VARIANT_TILE) {
       snprintf(plan->reason, sizeof(plan->reason),
                "tile (MXFP8): 128 weight rows x 64 routes per workgroup, both operands staged in LDS");
@@ -235,7 +243,7 @@ int moe_plan_init(moe_plan* plan, const moe_problem* prob) {
   plan->variant = variant;
   plan->block_m = variant != MOE_VARIANT_TILE   ? 16
                   : !contiguous                  ? kTileRowsBatched
-                  : P.w_dtype == MOE_W_MXFP8     ? kTileRoutesMxfp8
+                  : is_mxfp8(P)                  ? kTileRoutesMxfp8
                                                  : kTileRoutesContiguous;
   plan->reduce_kind = contiguous ? MOE_REDUCE_NOOP : MOE_REDUCE_NAIVE_BATCHED;
   plan->routes = R;
@@ -253,12 +261,12 @@ int moe_plan_init(moe_plan* plan, const moe_problem* prob) {
   }
   if (plan->max_tiles > 65535 || plan->max_active > 65535)
     return fail(plan, MOE_EUNSUPPORTED, "grid too large");
-  if (contiguous && (variant != MOE_VARIANT_TILE || P.w_dtype == MOE_W_MXFP8)) {
+  if (contiguous && (variant != MOE_VARIANT_TILE || is_mxfp8(P))) {
     // the streaming and MXFP8 kernels read z (and for MXFP8 the gathered
     // activation codes) through one buffer resource with 32-bit offsets,
     // whose range check stops at 2^31 - 1 bytes: rows past it would read 0
-    const int64_t zbytes = plan->sorted_capacity * P.I * (P.w_dtype == MOE_W_MXFP8 ? 1 : 2);
-    const int64_t xqbytes = P.w_dtype == MOE_W_MXFP8 ? plan->sorted_capacity * P.K : 0;
+    const int64_t zbytes = plan->sorted_capacity * P.I * (is_mxfp8(P) ? 1 : 2);
+    const int64_t xqbytes = is_mxfp8(P) ? plan->sorted_capacity * P.K : 0;
     if (zbytes >= (1ll << 31) - 1 || xqbytes >= (1ll << 31) - 1)
       return fail(plan, MOE_EUNSUPPORTED,
                   "streaming/MXFP8 kernels address z and the gathered activations with 32-bit offsets");
@@ -277,7 +285,7 @@ int moe_plan_init(moe_plan* plan, const moe_problem* prob) {
   int64_t o = L.end;
   const int64_t zrows = contiguous ? plan->sorted_capacity : P.E * P.max_tokens;
   plan->off_z = o;
-  if (P.w_dtype == MOE_W_MXFP8) {
+  if (is_mxfp8(P)) {
     o = up(o + zrows * P.I, kAlign);
     plan->off_z_scale = o;
     o = up(o + zrows * (P.I / 32), kAlign);
@@ -343,6 +351,7 @@ static bool contiguous_args_ok(const moe_plan* plan, const moe_weights* w) {
   if (P.layout != MOE_LAYOUT_CONTIGUOUS) return false;
   if (!aligned16(w->w1) || !aligned16(w->w2)) return false;
   if (P.w_dtype == MOE_W_MXFP8 && (!aligned4(w->w1_scale) || !aligned4(w->w2_scale))) return false;
+  if (P.w_dtype == MOE_W_MXFP8_GROUPED && (!aligned16(w->w1_scale) || !aligned16(w->w2_scale))) return false;
   return true;
 }
 
@@ -377,16 +386,24 @@ static GemmArgs w2_args(const moe_plan* plan, const moe_weights* w, void* ws13, 
   return g;
 }
 
+// Grouped MXFP8 scales: bytes between the 16-byte groups of the gathered
+// activations' and z's scale arrays (sorted_capacity rows each); 0 for
+// row-major scales.
+static int64_t scale_group(const moe_plan* plan) {
+  return plan->prob.w_dtype == MOE_W_MXFP8_GROUPED ? plan->sorted_capacity * 16 : 0;
+}
+
 static int gate_up_act(const moe_plan* plan, const void* a, const moe_weights* w, void* ws13,
                        hipStream_t s) {
   const moe_problem& P = plan->prob;
   GemmArgs g = w1_args(plan, w, ws13);
-  if (P.w_dtype == MOE_W_MXFP8) {
+  if (is_mxfp8(P)) {
     uint8_t* xq = at<uint8_t>(ws13, plan->off_xq);
     uint8_t* xqs = at<uint8_t>(ws13, plan->off_xq_scale);
+    g.scale_group = scale_group(plan);
     if (launch_quantize_gather_mxfp8(static_cast<const uint16_t*>(a), g.rows.sorted_ids,
                                      g.rows.num_post, (int32_t)P.topk, g.rows.sentinel,
-                                     plan->sorted_capacity, P.K, xq, xqs, s) != hipSuccess)
+                                     plan->sorted_capacity, P.K, xq, xqs, g.scale_group, s) != hipSuccess)
       return MOE_EHIP;
     g.act = xq;
     g.act_scale = xqs;
@@ -409,8 +426,9 @@ static int down_unpermute(const moe_plan* plan, const moe_weights* w, void* ws13
   const moe_problem& P = plan->prob;
   GemmArgs g = w2_args(plan, w, ws13, ws2);
   hipError_t e;
-  if (P.w_dtype == MOE_W_MXFP8) {
+  if (is_mxfp8(P)) {
     g.act_scale = at<uint8_t>(ws13, plan->off_z_scale);
+    g.scale_group = scale_group(plan);
     g.act_bytes = plan->sorted_capacity * P.I;
     e = plan->variant == MOE_VARIANT_TILE ? launch_gemm_tile_mxfp8(g, s) : launch_gemm_stream_mxfp8(g, s);
   } else {
@@ -622,6 +640,18 @@ int moe_quantize_mxfp8(const void* x, int x_dtype, int64_t rows, int64_t cols, u
   if (rows <= 0 || cols <= 0 || cols % 32 || (x_dtype != 0 && x_dtype != 1)) return MOE_EINVAL;
   if (!aligned16(x) || !aligned16(codes) || !scales) return MOE_EINVAL;
   hipError_t e = launch_quantize_mxfp8(x, x_dtype, rows, cols, codes, scales, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+int moe_pack_mxfp8_scales(const uint8_t* src, uint8_t* dst, int64_t mats, int64_t rows, int64_t cols,
+                          void* stream) {
+  if (mats <= 0 || rows <= 0 || cols <= 0 || cols % 512) return MOE_EINVAL;
+  if (!aligned16(src) || !aligned16(dst)) return MOE_EINVAL;
+  const int64_t bytes = mats * rows * (cols / 32);
+  if (bytes / mats / rows != cols / 32) return MOE_EINVAL;   // overflow
+  // the buffers must not overlap
+  if ((uintptr_t)src < (uintptr_t)dst + bytes && (uintptr_t)dst < (uintptr_t)src + bytes) return MOE_EINVAL;
+  hipError_t e = launch_pack_mxfp8_scales(src, dst, mats, rows, cols, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 

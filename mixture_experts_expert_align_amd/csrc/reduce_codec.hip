@@ -293,7 +293,7 @@ __global__ void __launch_bounds__(NT) quantize_kernel(const void* __restrict__ x
 __global__ void __launch_bounds__(NT) quantize_gather_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ num_post, int topk, int sentinel, int64_t K,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t scale_group) {
   const int nb = (int)(K / 32);
   const int lane = threadIdx.x & 63;
   const int nwaves = (int)gridDim.x * (NT / 64);
@@ -323,9 +323,26 @@ __global__ void __launch_bounds__(NT) quantize_gather_kernel(
             v[8 * i + 2 * j] = bf16_to_f32((uint32_t)q[u][i][j] & 0xffffu);
             v[8 * i + 2 * j + 1] = bf16_to_f32((uint32_t)q[u][i][j] >> 16);
           }
-        quantize_block(v, codes + (int64_t)p * K + b * 32, scales + (int64_t)p * nb + b);
+        uint8_t* sc = scale_group ? scales + (int64_t)(b / 16) * scale_group + (int64_t)p * 16 + b % 16
+                                  : scales + (int64_t)p * nb + b;
+        quantize_block(v, codes + (int64_t)p * K + b * 32, sc);
       }
     }
+  }
+}
+
+// Scale arrays row-major -> grouped: thread i moves 16-byte piece i of the
+// source, piece g of row r of matrix m (rows of ng pieces), to
+// m * rows * ng * 16 + g * rows * 16 + r * 16 in dst.  Sources rows are
+// read in order, so each wave reads 1 KB of them contiguously.
+__global__ void __launch_bounds__(NT) pack_scales_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                          int64_t rows, int64_t ng, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) {
+    const int64_t g = i % ng;
+    const int64_t mr = i / ng;   // m * rows + r
+    const int64_t m = mr / rows, r = mr - m * rows;
+    const i32x4 v = reinterpret_cast<const i32x4*>(src)[i];
+    reinterpret_cast<i32x4*>(dst)[(m * ng + g) * rows + r] = v;
   }
 }
 
@@ -541,13 +558,22 @@ hipError_t launch_quantize_mxfp8(const void* x, int x_dtype, int64_t rows, int64
 hipError_t launch_quantize_gather_mxfp8(const uint16_t* x, const int32_t* sorted_ids,
                                         const int32_t* num_post, int32_t topk, int32_t sentinel,
                                         int64_t capacity, int64_t K, uint8_t* codes,
-                                        uint8_t* scales, hipStream_t s) {
+                                        uint8_t* scales, int64_t scale_group, hipStream_t s) {
   // a wave per position, up to eight workgroups per CU
   if (capacity <= 0) return hipSuccess;
   const int64_t need = (capacity + NT / 64 - 1) / (NT / 64);
   const int64_t wgs = need < 2048 ? need : 2048;
   hipLaunchKernelGGL(quantize_gather_kernel, dim3((unsigned)wgs), dim3(NT), 0, s, x, sorted_ids, num_post, topk,
-                     sentinel, K, codes, scales);
+                     sentinel, K, codes, scales, scale_group);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_mxfp8_scales(const uint8_t* src, uint8_t* dst, int64_t mats, int64_t rows, int64_t cols,
+                                    hipStream_t s) {
+  const int64_t n = mats * rows * (cols / 512);   // 16-byte pieces
+  if (n == 0) return hipSuccess;
+  const int64_t wgs = std::min<int64_t>((n + NT - 1) / NT, 8192);
+  hipLaunchKernelGGL(pack_scales_kernel, dim3((unsigned)wgs), dim3(NT), 0, s, src, dst, rows, cols / 512, n);
   return hipGetLastError();
 }
 

@@ -8,6 +8,7 @@ ever fed to the oracle.
 """
 from __future__ import annotations
 
+import dataclasses
 import math
 import sys
 from dataclasses import dataclass, field
@@ -45,10 +46,14 @@ class DeviceCase:
     cache: dict = field(default_factory=dict)
 
 
-def problem(cfg: mi.MoEConfig, variant=moe.VARIANT_AUTO, global_experts=0):
+def problem(cfg: mi.MoEConfig, variant=moe.VARIANT_AUTO, global_experts=0, w_dtype=None):
+    """The problem of a workload; ``w_dtype`` overrides the weight type (e.g.
+    W_MXFP8_GROUPED for grouped scale arrays)."""
+    if w_dtype is None:
+        w_dtype = moe.W_BF16 if cfg.w_dtype == "bf16" else moe.W_MXFP8
     return moe.make_problem(cfg.M, cfg.K, cfg.I, cfg.E, topk=cfg.topk, max_tokens=cfg.max_tokens,
                             layout=moe.LAYOUT_CONTIGUOUS if cfg.layout == "contiguous" else moe.LAYOUT_BATCHED,
-                            w_dtype=moe.W_BF16 if cfg.w_dtype == "bf16" else moe.W_MXFP8,
+                            w_dtype=w_dtype,
                             w1_order=moe.W1_HALVES if cfg.w1_order == "halves" else moe.W1_INTERLEAVE16,
                             variant=variant, global_experts=global_experts)
 
@@ -60,6 +65,16 @@ def quantize_on_device(w: torch.Tensor):
     scales = torch.empty((*w.shape[:-1], w.shape[-1] // 32), dtype=torch.uint8, device=w.device)
     moe.moe_quantize_mxfp8(w.contiguous(), codes, scales)
     return codes, scales
+
+
+def grouped_scales(c: DeviceCase) -> DeviceCase:
+    """The case with its MXFP8 scale arrays grouped by moe_pack_mxfp8_scales
+    (for W_MXFP8_GROUPED)."""
+    p1, p2 = torch.empty_like(c.w1_scale), torch.empty_like(c.w2_scale)
+    moe.moe_pack_mxfp8_scales(c.w1_scale, p1)
+    moe.moe_pack_mxfp8_scales(c.w2_scale, p2)
+    torch.cuda.synchronize()
+    return dataclasses.replace(c, w1_scale=p1, w2_scale=p2)
 
 
 def make_case(cfg: mi.MoEConfig, device="cuda") -> DeviceCase:
@@ -94,12 +109,13 @@ def poison_workspaces(plan, ws13: torch.Tensor, ws2: torch.Tensor):
 
 
 def run_contiguous(c: DeviceCase, variant=moe.VARIANT_AUTO, ids=None, wts=None, x=None,
-                   expert_map: Optional[np.ndarray] = None, poison: bool = False):
+                   expert_map: Optional[np.ndarray] = None, poison: bool = False, w_dtype=None):
     """One moe_apply_contiguous call; with ``expert_map`` (host int32 [G]) the
     ids are global and the plan's global_experts is G.  ``poison``: the
-    intermediate buffers start as NaN patterns (see poison_workspaces)."""
+    intermediate buffers start as NaN patterns (see poison_workspaces).
+    ``w_dtype``: as in problem()."""
     G = 0 if expert_map is None else len(expert_map)
-    plan = moe.moe_plan_init(problem(c.cfg, variant, global_experts=G))
+    plan = moe.moe_plan_init(problem(c.cfg, variant, global_experts=G, w_dtype=w_dtype))
     ws13, ws2 = moe.allocate_workspaces(plan)
     if poison:
         poison_workspaces(plan, ws13, ws2)

@@ -98,6 +98,11 @@ def test_plans_of_the_five_workloads(idx):
     (dict(variant=moe.VARIANT_FUSED, M=4097), moe.MOE_EUNSUPPORTED),      # M*topk > 8192
     (dict(variant=moe.VARIANT_FUSED, E=2049), moe.MOE_EUNSUPPORTED),
     (dict(variant=moe.VARIANT_FUSED, K=200), moe.MOE_EUNSUPPORTED),
+    # grouped MXFP8 scales: K and I multiples of 512, tile kernels, contiguous
+    (dict(K=512, I=384, w_dtype=moe.W_MXFP8_GROUPED), moe.MOE_EUNSUPPORTED),
+    (dict(K=384, I=512, w_dtype=moe.W_MXFP8_GROUPED), moe.MOE_EUNSUPPORTED),
+    (dict(K=512, I=512, w_dtype=moe.W_MXFP8_GROUPED, variant=moe.VARIANT_STREAM), moe.MOE_EUNSUPPORTED),
+    (dict(K=512, I=512, w_dtype=moe.W_MXFP8_GROUPED, layout=1, max_tokens=64), moe.MOE_EUNSUPPORTED),
 ])
 def test_plan_validation(kw, code):
     base = dict(M=64, K=256, I=512, E=8, topk=2)
@@ -114,6 +119,16 @@ def test_global_experts_topk_range():
     assert p.prob.global_experts == 512
     with pytest.raises(moe.MoeError):
         moe.moe_plan_init(moe.make_problem(64, 256, 512, 2, topk=8))
+
+
+def test_mxfp8_grouped_plan():
+    """Grouped MXFP8 scale arrays plan like row-major ones (the tiles, the
+    same workspace layout and sizes: only the scale bytes' order differs)."""
+    a = moe.moe_plan_init(moe.make_problem(512, 6144, 2048, 32, topk=8, w_dtype=moe.W_MXFP8))
+    b = moe.moe_plan_init(moe.make_problem(512, 6144, 2048, 32, topk=8, w_dtype=moe.W_MXFP8_GROUPED))
+    assert b.variant == moe.VARIANT_TILE and b.block_m == 64
+    for f in ("ws13_bytes", "ws2_bytes", "sorted_capacity", "off_z", "off_z_scale", "off_xq", "off_xq_scale"):
+        assert getattr(a, f) == getattr(b, f), f
 
 
 def test_mxfp8_tile_shapes():

@@ -20,7 +20,7 @@ import torch
 import moe_inputs as mi
 import mixture_experts_expert_align_amd as moe
 import oracle
-from moe_cases import (BF16_ABS, BF16_REL, MX_REL, check_close, heavy_tail_rows, make_case,
+from moe_cases import (BF16_ABS, BF16_REL, MX_REL, check_close, grouped_scales, heavy_tail_rows, make_case,
                        oracle_contiguous, oracle_weights, run_batched, run_contiguous, sample_tokens, say,
                        tokens_covering_experts, _host_f64)
 
@@ -207,6 +207,73 @@ def test_mxfp8_scale_groups_equal_per_step_scales():
     assert pg.variant == ps.variant == moe.VARIANT_TILE
     assert torch.equal(grouped.view(torch.int16), per_step.view(torch.int16))
     check_close(grouped, oracle_contiguous(c, np.arange(cfg.M)), MX_REL, 0.0, f"{cfg.name} grouped scales")
+
+
+def grouped_to_rows(a: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """Row-major [rows, cols/32] scale bytes from one grouped matrix, by the
+    layout the header states: byte j of row r at (j/16)*rows*16 + r*16 + j%16."""
+    r, j = np.meshgrid(np.arange(rows), np.arange(cols // 32), indexing="ij")
+    return a.reshape(-1)[(j // 16) * rows * 16 + r * 16 + j % 16]
+
+
+def test_pack_mxfp8_scales_layout():
+    """moe_pack_mxfp8_scales moves every scale byte to where the grouped layout
+    puts it, matrix by matrix; sizes it cannot group are refused."""
+    rng = np.random.default_rng(11)
+    for mats, rows, cols in ((3, 200, 1024), (1, 64, 512), (2, 130, 2048)):
+        src = rng.integers(0, 256, (mats, rows, cols // 32), dtype=np.uint8)
+        s = torch.from_numpy(src).cuda()
+        d = torch.empty_like(s)
+        moe.moe_pack_mxfp8_scales(s, d)
+        got = d.cpu().numpy()
+        for m in range(mats):
+            assert np.array_equal(grouped_to_rows(got[m], rows, cols), src[m]), (mats, rows, cols, m)
+    s = torch.zeros((2, 64, 12), dtype=torch.uint8, device="cuda")     # cols = 384
+    with pytest.raises(moe.MoeError):
+        moe.moe_pack_mxfp8_scales(s, torch.empty_like(s))
+
+
+# (M, K, I): W1 and W2 with 2/1, 1/1 and 1/2 groups of four steps; M = 4160
+# gives experts more than one 64-route tile
+GROUPED_SHAPES = [(700, 1024, 512), (4160, 512, 512), (300, 512, 1024)]
+
+
+@pytest.mark.parametrize("M,K,I", GROUPED_SHAPES, ids=[f"m{m}_k{k}_i{i}" for m, k, i in GROUPED_SHAPES])
+def test_mxfp8_grouped_scales_equal_row_major(M, K, I):
+    """Grouped scale arrays (W_MXFP8_GROUPED, weights packed by
+    moe_pack_mxfp8_scales) give the row-major call's output bit for bit, and
+    the gathered activations' and z's scale bytes are the same bytes in the
+    grouped layout."""
+    cfg = mi.config(3).scaled(M=M, K=K, I=I)
+    c = make_case(cfg)
+    row, pr, wsr, _ = run_contiguous(c, moe.VARIANT_TILE, poison=True)
+    grp, pg, wsg, _ = run_contiguous(grouped_scales(c), moe.VARIANT_TILE, poison=True, w_dtype=moe.W_MXFP8_GROUPED)
+    assert torch.equal(row.view(torch.int16), grp.view(torch.int16)), f"{cfg.name}: grouped scales differ"
+    cap = pr.sorted_capacity
+    assert pg.sorted_capacity == cap
+    sid = moe.ws_view(wsr, pr.off_sorted_ids, cap).cpu().numpy()
+    npost = int(moe.ws_view(wsr, pr.off_num_post_padded, 1).cpu()[0])
+    real = np.nonzero(sid[:npost] != pr.routes)[0]              # positions that hold a route
+    for off_r, off_g, n in ((pr.off_xq_scale, pg.off_xq_scale, K), (pr.off_z_scale, pg.off_z_scale, I)):
+        a = moe.ws_view(wsr, off_r, cap * n // 32, torch.uint8).view(cap, n // 32).cpu().numpy()
+        b = grouped_to_rows(moe.ws_view(wsg, off_g, cap * n // 32, torch.uint8).cpu().numpy(), cap, n)
+        assert np.array_equal(a[real], b[real]), f"{cfg.name}: scale bytes of the {n}-wide rows differ"
+    if M == 700:
+        check_close(grp, oracle_contiguous(c, np.arange(cfg.M)), MX_REL, 0.0, f"{cfg.name} grouped")
+
+
+def test_mxfp8_grouped_scales_expert_map():
+    """The expert-parallel share fed as bench.py feeds it (global ids, the
+    rank's map) with grouped scale arrays: the row-major call's bits."""
+    cfg = mi.config(3).scaled(M=900, K=512, I=512)
+    c = make_case(cfg)
+    emap = mi.ep_expert_map(cfg.global_experts, cfg.E, rank=0)
+    gid = torch.from_numpy(c.inp.global_ids).cuda()
+    gw = torch.from_numpy(c.inp.global_weights).cuda()
+    row, *_ = run_contiguous(c, ids=gid, wts=gw, expert_map=emap, poison=True)
+    grp, *_ = run_contiguous(grouped_scales(c), ids=gid, wts=gw, expert_map=emap, poison=True,
+                             w_dtype=moe.W_MXFP8_GROUPED)
+    assert torch.equal(row.view(torch.int16), grp.view(torch.int16))
 
 
 def test_tiny_intermediate_z():
