@@ -13,7 +13,7 @@ import torch
 
 import moe_inputs as mi
 import mixture_experts_expert_align_amd as moe
-from moe_cases import make_case, problem, say
+from moe_cases import grouped_scales, make_case, problem, say
 
 pytestmark = pytest.mark.gpu
 
@@ -26,7 +26,8 @@ CONTIGUOUS = [
     ("prefill_tile", mi.config(2).scaled(M=700, K=512, I=384, E=24), moe.VARIANT_AUTO),
     ("mxfp8_tile", mi.config(3).scaled(M=512, K=512, I=256), moe.VARIANT_AUTO),
     ("mxfp8_stream", mi.config(3).scaled(M=512, K=512, I=256), moe.VARIANT_STREAM),
-    ("mxfp8_tile_grouped_scales", mi.config(3).scaled(M=700, K=1024, I=512), moe.VARIANT_AUTO),
+    ("mxfp8_tile_scale_groups", mi.config(3).scaled(M=700, K=1024, I=512), moe.VARIANT_AUTO),
+    ("mxfp8_tile_grouped_arrays", mi.config(3).scaled(M=700, K=1024, I=512), "grouped scale arrays"),
 ]
 
 
@@ -52,7 +53,11 @@ def bits(t: torch.Tensor) -> torch.Tensor:
 @pytest.mark.parametrize("name,cfg,variant", CONTIGUOUS, ids=[c[0] for c in CONTIGUOUS])
 def test_graph_contiguous(name, cfg, variant):
     c = make_case(cfg)
-    plan = moe.moe_plan_init(problem(cfg, variant))
+    if variant == "grouped scale arrays":   # the tiles, W_MXFP8_GROUPED
+        c = grouped_scales(c)
+        plan = moe.moe_plan_init(problem(cfg, moe.VARIANT_TILE, w_dtype=moe.W_MXFP8_GROUPED))
+    else:
+        plan = moe.moe_plan_init(problem(cfg, variant))
     say(f"[graph] {name}: variant {plan.variant} ({plan.reason.decode()})")
 
     def call(out, ws13, ws2):
