@@ -7,10 +7,13 @@
 // A workgroup of NW waves computes 32 NW weight rows x 64 routes of one
 // expert (NW = 4: 128 rows, two workgroups per CU).  Each 128-wide
 // contraction step (one v_mfma_scale_f32_16x16x128_f8f6f4) of both
-// operands — weight codes 32 NW x 128 B, route codes 64 x 128 B and their
-// scale words — reaches LDS by buffer loads that write LDS directly, into a
-// ring of 3 step slots: step kt+3 is requested once step kt's slot is free,
-// so every load has two steps of work to land in.  Workgroups are ordered
+// operands — weight codes 32 NW x 128 B and route codes 64 x 128 B — reaches
+// LDS by buffer loads that write LDS directly, into a ring of 3 step slots:
+// step kt+3 is requested once step kt's slot is free, so every load has two
+// steps of work to land in.  The scale words come with each step, or, where
+// the contraction allows, 4 steps at a time into a ring of their own (from
+// row-major scale arrays, or as contiguous blocks from grouped ones: see
+// MxTile).  Workgroups are ordered
 // weight-major inside an expert and handed to the XCDs in chunks (the bf16
 // tile kernel's order), so an expert with more than 64 routes reads each
 // weight tile from HBM once and its other route tiles find it in L2.
@@ -31,8 +34,8 @@
 //            16w .. 16w+15; z = silu(gate) * up is staged in LDS and each
 //            thread then quantises one (route, 32-feature block) to E4M3 codes
 //            and a UE8M0 scale (the same rule as the weights).
-//   kDown:   wave w writes its 32 output features of each route as bf16 to
-//            the route's (token, slot) row of y.
+//   kDown:   the tile's bf16 outputs are staged in LDS and leave as whole
+//            256-byte row segments of each route's (token, slot) row of y.
 #include <algorithm>
 #include <type_traits>
 
