@@ -228,6 +228,14 @@ def test_pack_mxfp8_scales_layout():
         got = d.cpu().numpy()
         for m in range(mats):
             assert np.array_equal(grouped_to_rows(got[m], rows, cols), src[m]), (mats, rows, cols, m)
+    # more 16-byte pieces (64 x 4096 x 16) than one pass of the kernel's grid
+    # (8192 workgroups x 256 threads) covers: matrices in both passes
+    mats, rows, cols = 64, 4096, 8192
+    s = torch.randint(0, 256, (mats, rows, cols // 32), dtype=torch.uint8, device="cuda")
+    d = torch.empty_like(s)
+    moe.moe_pack_mxfp8_scales(s, d)
+    for m in (0, 31, 32, 63):
+        assert np.array_equal(grouped_to_rows(d[m].cpu().numpy(), rows, cols), s[m].cpu().numpy()), m
     s = torch.zeros((2, 64, 12), dtype=torch.uint8, device="cuda")     # cols = 384
     with pytest.raises(moe.MoeError):
         moe.moe_pack_mxfp8_scales(s, torch.empty_like(s))
