@@ -363,11 +363,11 @@ int moe_quantize_mxfp8(const void* x, int x_dtype, int64_t rows, int64_t cols, u
 
 /* Scale arrays for MOE_W_MXFP8_GROUPED (page "Cake MegaMoE EP16 backend for
  * BF16 activations and MXFP8 weights", section 2: the scales are packed for
- * the GEMM once, when the weights are loaded).  src (device) holds mats
- * matrices of rows x cols/32 UE8M0 bytes, row-major, as moe_quantize_mxfp8
- * writes them (W1: mats = E, rows = 2I, cols = K; W2: E, K, I); dst (device,
- * the same size, 16-byte aligned, not overlapping src) receives each matrix
- * grouped as MOE_W_MXFP8_GROUPED describes.  cols % 512 must be 0.  Enqueues
+ * the GEMM once, when the weights are loaded).  src (device, 16-byte
+ * aligned) holds mats matrices of rows x cols/32 UE8M0 bytes, row-major, as
+ * moe_quantize_mxfp8 writes them (W1: mats = E, rows = 2I, cols = K; W2: E,
+ * K, I); dst (device, the same size, 16-byte aligned, not overlapping src)
+ * receives each matrix grouped as MOE_W_MXFP8_GROUPED describes.  cols % 512 must be 0.  Enqueues
  * one kernel on the stream; allocates nothing and does not synchronise.
  * MOE_EINVAL for a null or misaligned pointer or a bad size. */
 int moe_pack_mxfp8_scales(const uint8_t* src, uint8_t* dst, int64_t mats, int64_t rows, int64_t cols,
