@@ -59,6 +59,8 @@ SCALED = [
     # both contractions multiples of 512: W1 (8 steps) and W2 (4 steps) load
     # their scale words in groups of 4 steps
     ("mxfp8_k1024_i512", mi.config(3).scaled(M=700, K=1024, I=512), moe.VARIANT_AUTO),
+    # W1 one step at a time (K = 384: 3 steps), W2 four steps at a time
+    ("mxfp8_k384_i512", mi.config(3).scaled(M=700, K=384, I=512), moe.VARIANT_AUTO),
     # streaming kernels, W1 weights 8 steps ahead: one trip of two chunks
     # (8 steps), and a full trip before the last (16 steps) with two
     # 64-token passes per expert
@@ -392,6 +394,10 @@ def test_expert_map_mxfp8_share(M):
     if M == 4096:
         masked, *_ = run_contiguous(c)                       # the host-masked call, same bits
         assert torch.equal(out.view(torch.int16), masked.view(torch.int16))
+        # the share as bench.py times it: grouped scale arrays, same bits
+        grp, *_ = run_contiguous(grouped_scales(c), ids=gid, wts=gw, expert_map=emap, w_dtype=moe.W_MXFP8_GROUPED)
+        assert torch.equal(out.view(torch.int16), grp.view(torch.int16))
+        del grp
         tokens = sample_tokens(M, 12, seed=5)
     else:
         tokens = np.arange(M)
