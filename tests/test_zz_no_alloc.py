@@ -10,13 +10,14 @@ import torch
 
 import moe_inputs as mi
 import mixture_experts_expert_align_amd as moe
-from moe_cases import BF16_ABS, BF16_REL, MX_REL, check_close, make_case, oracle_contiguous, problem, say
+from moe_cases import (BF16_ABS, BF16_REL, MX_REL, check_close, grouped_scales, make_case, oracle_contiguous,
+                       problem, say)
 
 pytestmark = pytest.mark.gpu
 
 
-def static_vs_allocating(c, variant=moe.VARIANT_AUTO):
-    plan = moe.moe_plan_init(problem(c.cfg, variant))
+def static_vs_allocating(c, variant=moe.VARIANT_AUTO, w_dtype=None):
+    plan = moe.moe_plan_init(problem(c.cfg, variant, w_dtype=w_dtype))
     need = -(-plan.ws13_bytes // 256) * 256 + plan.ws2_bytes
     say(f"[no_alloc] {c.cfg.name} variant {plan.variant}: workspaces {need} of {moe.STATIC_SCRATCH_BYTES} bytes")
     assert need <= moe.STATIC_SCRATCH_BYTES
@@ -42,13 +43,20 @@ def static_vs_allocating(c, variant=moe.VARIANT_AUTO):
     # MXFP8 tiles: scale words in groups of four steps (K, I multiples of
     # 512), then a smaller layer whose W2 loads them step by step
     ((3, dict(M=700, K=1024, I=512), moe.VARIANT_AUTO), (3, dict(M=300, K=512, I=256), moe.VARIANT_AUTO)),
+    # MXFP8 tiles on grouped scale arrays, twice: the second call's scale
+    # groups are shorter (fewer sorted rows) than the first call left them
+    ((3, dict(M=700, K=1024, I=512), "grouped"), (3, dict(M=300, K=512, I=512), "grouped")),
 ])
 def test_static_matches_allocating_two_calls(first, second):
     outs = []
     for idx, kw, variant in (first, second):
         cfg = mi.config(idx) if kw is None else mi.config(idx).scaled(**kw)
         c = make_case(cfg)
-        outs.append((c, static_vs_allocating(c, variant)))
+        if variant == "grouped":                           # W_MXFP8_GROUPED, the tile kernels
+            c = grouped_scales(c)
+            outs.append((c, static_vs_allocating(c, moe.VARIANT_TILE, moe.W_MXFP8_GROUPED)))
+        else:
+            outs.append((c, static_vs_allocating(c, variant)))
     # the second call against the oracle as well
     c, out = outs[-1]
     rel, ab = (MX_REL, 0.0) if c.cfg.w_dtype == "mxfp8" else (BF16_REL, BF16_ABS)
