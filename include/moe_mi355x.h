@@ -217,8 +217,10 @@ int moe_abi_version(void);
 const char* moe_status_string(int status);
 
 /* sizeof(moe_problem), sizeof(moe_plan) and sizeof(moe_weights) as compiled
- * into the library, for bindings that lay the structs out themselves.
- * Each pointer may be NULL. */
+ * into the library, for bindings that lay the structs out themselves (the
+ * same concern as moe_abi_version: page "Cake deterministic MoE grouped
+ * GEMM", review follow-up, a binding whose view of the arguments no longer
+ * matches the library).  Each pointer may be NULL. */
 void moe_struct_sizes(int64_t* problem, int64_t* plan, int64_t* weights);
 
 /* Validate `prob` (host) and fill `plan` (host): the workspace sizes of page
@@ -332,7 +334,10 @@ int moe_topk_reduce_contiguous(const moe_plan* plan, const void* y, const int32_
                                const float* topk_weights, const int32_t* expert_map, void* out,
                                void* stream);
 
-/* Bytes of workspace moe_topk_reduce_naive_batched needs for n_out tokens. */
+/* Bytes of workspace moe_topk_reduce_naive_batched needs for n_out tokens
+ * (page "Fused MoE Modular Kernel", workspace_shapes(): the kernel reports
+ * its workspace sizes and the caller allocates them).  -1 for a NULL plan,
+ * a plan of the contiguous layout, or n_out outside [1, 8192]. */
 int64_t moe_naive_batched_ws_bytes(const moe_plan* plan, int64_t n_out);
 
 /* TopKWeightAndReduceNaiveBatched (page "Fused MoE Modular Kernel", section
@@ -401,15 +406,18 @@ typedef struct moe_grouped_problem {
   int64_t E;   /* groups (experts)                                          */
 } moe_grouped_problem;
 
-/* y[r] = W[e] x[r] for the rows r of group e: y device bf16 [R, N]. */
+/* Forward (page "Cake deterministic MoE grouped GEMM", introduction):
+ * y[r] = W[e] x[r] for the rows r of group e: y device bf16 [R, N]. */
 int moe_grouped_forward(const moe_grouped_problem* p, const void* x, const void* w,
                         const int32_t* group_offsets, void* y, void* stream);
 
-/* dgrad: dx[r] = W[e]^T dy[r]: dx device bf16 [R, K]. */
+/* dgrad (page "Cake deterministic MoE grouped GEMM", introduction):
+ * dx[r] = W[e]^T dy[r]: dx device bf16 [R, K]. */
 int moe_grouped_dgrad(const moe_grouped_problem* p, const void* dy, const void* w,
                       const int32_t* group_offsets, void* dx, void* stream);
 
-/* wgrad: dW[e] = sum over the rows r of group e of dy[r] x[r]^T, fp32.
+/* wgrad (page "Cake deterministic MoE grouped GEMM", sections 1 and 2):
+ * dW[e] = sum over the rows r of group e of dy[r] x[r]^T, fp32.
  * dw: device float32 [E, N, K]; accumulate = 0 writes dW (+0.0 for an empty
  * group), accumulate = 1 adds it: dw[e] = dw[e] + dW[e] in one fp32 add per
  * element, bit for bit what the overwrite followed by dw.add_(dW) gives (an
