@@ -21,7 +21,8 @@ _orig = {n: getattr(oracle, n) for n in ("split_gate_up", "silu", "expert_ffn", 
                                          "topk_reduce_contiguous", "moe_contiguous",
                                          "map_expert_ids", "grouped_forward", "grouped_dgrad",
                                          "naive_batched_reduce", "moe_batched_rows",
-                                         "grouped_wgrad", "grouped_wgrad_accumulate")}
+                                         "grouped_wgrad", "grouped_wgrad_accumulate",
+                                         "mx_scale_code", "mxfp8_quantize", "mxfp8_dequantize")}
 
 
 def m_swap_gate_up(w1, order):
@@ -82,6 +83,26 @@ def m_encode_ties_away(v):
     mid = (tab[c & 0x7F] + tab[up]) / 2
     bump = (a == mid) & (up != (c & 0x7F))
     return np.where(bump, (c & 0x80) | up.astype(np.uint8), c).astype(np.uint8)
+
+
+def m_scale_code_zero_block_biased(bm):
+    bm = np.asarray(bm, np.float64)
+    return np.where(bm > 0, _orig["mx_scale_code"](bm), 127).astype(np.uint8)   # zero block: 2^0
+
+
+def m_quantize_half_block_max(x):
+    # the block maximum taken over the first 16 values of each block only
+    x = np.asarray(x, np.float64)
+    n = x.shape[-1]
+    b = x.reshape(-1, n // 32, 32)
+    sc = oracle.mx_scale_code(np.abs(b[..., :16]).max(axis=-1))
+    s = np.ldexp(1.0, sc.astype(np.int32) - 127)
+    codes = oracle.e4m3fn_encode(np.clip(b / s[..., None], -448.0, 448.0)).reshape(x.shape)
+    return codes, sc.reshape(*x.shape[:-1], n // 32)
+
+
+def m_dequantize_bias_128(codes, scales):
+    return _orig["mxfp8_dequantize"](codes, np.asarray(scales, np.int64) - 1)
 
 
 def m_reduce_reads_skipped(y, ids, w, E):
@@ -192,6 +213,8 @@ MUTATIONS = [
     ("naive_batched_reduce", m_batched_reduce_transposed_map),
     ("naive_batched_reduce", m_batched_reduce_unweighted),
     ("moe_batched_rows", m_batched_rows_one_past), ("moe_batched_rows", m_batched_rows_wrong_expert),
+    ("mx_scale_code", m_scale_code_zero_block_biased), ("mxfp8_quantize", m_quantize_half_block_max),
+    ("mxfp8_dequantize", m_dequantize_bias_128),
 ]
 
 
